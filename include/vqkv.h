@@ -1,0 +1,220 @@
+/*
+ * vqkv.h -- C ABI of libvqkv: decode self-attention that reads a
+ * vector-quantized KV cache directly, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is VecInfer's ("VecInfer: Efficient LLM Inference with Low-Bit KV
+ * Cache via Outlier-Suppressed Vector Quantization"; summary card on
+ * research.elamur.ai, sections "Summary" and "Key points"; arXiv 2510.06175
+ * abstract and its "technical framework" paragraph):
+ *   1. keys are smoothed per channel (divided by s) and rotated by a Hadamard
+ *      transform; the query gets the matching inverse (times s, same rotation),
+ *      so attention scores are unchanged;
+ *   2. keys and values are stored as indices into K-Means codebooks:
+ *      2^8 entries x 4 dims (2 bits per element) or 2^12 entries x 8 dims
+ *      (1.5 bits per element);
+ *   3. attention dequantizes inside the kernel, reading only the codes.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers marked "device" point to GPU memory on the current HIP device;
+ *   pointers marked "host" point to CPU memory.  The caller owns every buffer.
+ *   The library never allocates, frees or synchronizes; all work is enqueued on
+ *   `stream` (a hipStream_t; NULL means the null stream) and is asynchronous.
+ * - Arguments are checked on the host before anything is enqueued.  A failed
+ *   check returns VQKV_ERR_INVALID_ARG or VQKV_ERR_UNSUPPORTED and leaves device
+ *   memory untouched.  A failed kernel launch returns VQKV_ERR_HIP.
+ *   vqkv_last_error() then gives a message for the calling thread.
+ * - head_dim is 128.  Hq must be a multiple of Hkv; q-head g uses KV head
+ *   g / (Hq / Hkv).  G = Hq / Hkv must be in [1, 8].
+ * - max_tokens (the cache capacity per (batch, KV head) stream) must be a
+ *   positive multiple of 64.
+ * - fp16 values are passed as their 16-bit patterns (uint16_t).
+ * - Every device pointer must be aligned to 16 bytes.
+ * - The library keeps no mutable global state; calls on different streams may
+ *   run concurrently as long as they do not write the same buffers.
+ *
+ * Cache layout (per (batch, KV head) stream; streams are [B][Hkv] in that
+ * order, each max_tokens * W bytes, W = vqkv_code_bytes_per_token(fmt)):
+ * - Key codes, token-major: token t occupies bytes [t*W, (t+1)*W).  2-bit:
+ *   byte j holds the code of sub-vector j (dims 4j..4j+3).  1.5-bit: the
+ *   12-bit codes of sub-vectors 2i and 2i+1 (dims 8*2i.. and 8*(2i+1)..) share
+ *   bytes 3i..3i+2 as b0 = c0 & 0xFF, b1 = (c0 >> 8) | ((c1 & 0xF) << 4),
+ *   b2 = c1 >> 4.
+ * - Value codes, blocked by sub-vector so that one lane reads one sub-vector
+ *   of many tokens with wide loads.  2-bit: blocks of 32 tokens, 1024 bytes
+ *   each; in a block, the 32 bytes at offset 32*j hold the codes of
+ *   sub-vector j for the block's tokens in order.  1.5-bit: blocks of 16
+ *   tokens, 384 bytes each; the 24 bytes at offset 24*j hold the 16 codes of
+ *   sub-vector j, tokens (2i, 2i+1) of the block packed in bytes 3i..3i+2 by
+ *   the 12-bit rule above.
+ * - Codebooks: fp16 [Hkv][E][dsub], one for keys and one for values per KV
+ *   head, shared by every sub-vector position.  Key codebooks live in the
+ *   rotated space.
+ * - Smoothing scales: fp32 [Hkv][128], every entry finite and > 0 (not
+ *   checked on device).
+ */
+#ifndef VQKV_H
+#define VQKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VQKV_OK = 0,
+    VQKV_ERR_INVALID_ARG = 1,   /* a null pointer, a bad size, misalignment, ... */
+    VQKV_ERR_UNSUPPORTED = 2,   /* a well-formed request this build does not implement */
+    VQKV_ERR_HIP = 3            /* the HIP runtime reported an error */
+} vqkv_status;
+
+typedef enum {
+    VQKV_FMT_2BIT = 0,          /* 256 entries x 4 dims, uint8 codes, 32 B per token */
+    VQKV_FMT_1P5BIT = 1         /* 4096 entries x 8 dims, 12-bit codes, 24 B per token */
+} vqkv_format;
+
+typedef enum {
+    VQKV_DTYPE_BF16 = 0,
+    VQKV_DTYPE_FP32 = 1
+} vqkv_dtype;
+
+typedef struct {
+    int32_t batch;              /* B >= 1 */
+    int32_t num_q_heads;        /* Hq >= 1 */
+    int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 8 */
+    int32_t head_dim;           /* must be 128 */
+    int32_t max_tokens;         /* cache capacity per stream, a positive multiple of 64 */
+    int32_t fmt;                /* vqkv_format */
+} vqkv_shape;
+
+/* ------------------------------------------------------------- size queries */
+
+/* Bytes per token per KV head for one of K or V: 32 (2-bit) or 24 (1.5-bit);
+ * 0 for an unknown format.  VecInfer card, "Key points" (codebook size). */
+size_t vqkv_code_bytes_per_token(int32_t fmt);
+
+/* Bytes of one code cache (keys or values): B * Hkv * max_tokens * W.
+ * 0 if the shape is invalid. */
+size_t vqkv_cache_bytes(const vqkv_shape* shape);
+
+/* Bytes of the split-context workspace that vqkv_decode_attention writes and
+ * vqkv_combine reads, for `num_splits` splits; 0 if the arguments are invalid. */
+size_t vqkv_workspace_bytes(const vqkv_shape* shape, int32_t num_splits);
+
+/* A split count that fills the GPU for this shape and context length
+ * (>= 1).  Any value in [1, ceil(seq_len / 64)] is valid for the decode. */
+int32_t vqkv_suggest_splits(const vqkv_shape* shape, int32_t seq_len);
+
+/* Static text for a status code. */
+const char* vqkv_status_string(int32_t status);
+
+/* Message describing the last failed call on the calling thread ("" if none). */
+const char* vqkv_last_error(void);
+
+/* ---------------------------------------------------------- hot-path calls */
+
+/* Query transform.  VecInfer card, "Summary": matching inverse operations on
+ * the queries keep attention scores unchanged.  For each (b, g), with
+ * h = g / G:  q'[b][g] = H (q[b][g] * s[h]), H the normalized 128 x 128
+ * Sylvester Hadamard matrix, computed in fp32 by an in-register fast
+ * Walsh-Hadamard transform.  Then q'.(H (k / s)) = q.k.
+ *   q        device, [B][Hq][128], dtype q_dtype (vqkv_dtype)
+ *   smooth   device, fp32 [Hkv][128]
+ *   q_prime  device, fp32 [B][Hq][128] (output)
+ * Only shape->batch, num_q_heads, num_kv_heads and head_dim are used. */
+vqkv_status vqkv_transform_query(const vqkv_shape* shape, const void* q, int32_t q_dtype,
+                                 const float* smooth, float* q_prime, void* stream);
+
+/* Append quantizer.  VecInfer card, "Summary", and the arXiv page's three
+ * stages (preprocess the keys, then vector-quantize the cache): for each new
+ * token, x' = H (k / s_h) in fp64 (butterflies in stage order h = 1..64, then a
+ * multiply by the fp64 nearest 1/sqrt(128)); for each sub-vector j the key
+ * code is argmin_e sum_i (x'_{j*dsub+i} - C_K[e][i])^2, the value code the same
+ * over the raw value and C_V, distances in fp64 summed left to right, ties to
+ * the lowest index.  Codes are written for positions
+ * [start_pos, start_pos + n_new) of every (b, h) stream; other positions keep
+ * their bytes.
+ *   k_new, v_new      device, [B][Hkv][n_new][128], dtype (vqkv_dtype)
+ *   n_new             host, >= 1;  start_pos: host, >= 0,
+ *                     start_pos + n_new <= max_tokens
+ *   smooth            device, fp32 [Hkv][128]
+ *   k_book, v_book    device, fp16 [Hkv][E][dsub]
+ *   k_codes, v_codes  device, cache buffers (layout above)
+ * Calls that write the same stream must not overlap in time. */
+vqkv_status vqkv_quantize_append(const vqkv_shape* shape, const void* k_new, const void* v_new,
+                                 int32_t dtype, int32_t n_new, int32_t start_pos,
+                                 const float* smooth, const uint16_t* k_book,
+                                 const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes,
+                                 void* stream);
+
+/* Split-context decode attention over the codes.  VecInfer abstract: a kernel
+ * that fuses dequantization into the attention computation to minimize memory
+ * access.  For each (b, g) and split i of `num_splits` equal 64-aligned token
+ * ranges of [0, seq_len):
+ *   z_t = sm_scale * q'[b][g] . concat_j C_K[kc_t,j];
+ *   o_i = sum_t softmax_i(z)_t * concat_j C_V[vc_t,j],  lse_i = log-sum-exp of z
+ * over the split's tokens (online softmax), written to `workspace`.
+ *   q_prime           device, fp32 [B][Hq][128] (from vqkv_transform_query)
+ *   k_book, v_book    device, fp16 [Hkv][E][dsub]
+ *   k_codes, v_codes  device, cache buffers holding tokens [0, seq_len)
+ *   seq_len           host, 1 <= seq_len <= max_tokens
+ *   sm_scale          host, finite (usually 1/sqrt(128))
+ *   num_splits        host, 1 <= num_splits <= ceil(seq_len / 64)
+ *   workspace         device, vqkv_workspace_bytes(shape, num_splits) bytes;
+ *                     its contents are private to vqkv_combine. */
+vqkv_status vqkv_decode_attention(const vqkv_shape* shape, const float* q_prime,
+                                  const uint16_t* k_book, const uint16_t* v_book,
+                                  const uint8_t* k_codes, const uint8_t* v_codes,
+                                  int32_t seq_len, float sm_scale, int32_t num_splits,
+                                  void* workspace, void* stream);
+
+/* Log-sum-exp merge of the splits (split-context flash decoding):
+ * out[b][g] = sum_i exp(lse_i - L) o_i, L = log sum_i exp(lse_i).
+ *   workspace   device, as written by vqkv_decode_attention with the same
+ *               shape and num_splits
+ *   out         device, fp32 [B][Hq][128] (output) */
+vqkv_status vqkv_combine(const vqkv_shape* shape, int32_t num_splits, const void* workspace,
+                         float* out, void* stream);
+
+/* ------------------------------------------------- offline calibration calls */
+
+/* Smoothing scales.  VecInfer card, "Summary" (channel-wise smoothing of the
+ * keys); the scale is not printed on the pages: this library uses
+ * s[h][c] = sqrt(max_t |k_cal[h][t][c]|), the fp32 nearest the fp64 root.
+ *   k_cal    device, [Hkv][n_cal][128], dtype;  n_cal >= 1 (host)
+ *   smooth   device, fp32 [Hkv][128] (output) */
+vqkv_status vqkv_smooth_scales(int32_t num_kv_heads, int32_t n_cal, const void* k_cal,
+                               int32_t dtype, float* smooth, void* stream);
+
+/* Bytes of device workspace vqkv_train_codebook needs for n_cal tokens. */
+size_t vqkv_train_workspace_bytes(int32_t fmt, int32_t n_cal);
+
+/* Offline K-Means codebook for one KV head (VecInfer card, "Summary": a
+ * K-Means codebook trained offline).  The points are the sub-vectors of the
+ * n_cal calibration rows: for keys (is_key != 0) the rotated x' = H (k / s),
+ * for values the raw rows.  Lloyd iterations from the initial points
+ * `init_idx` (device int64 [E], distinct indices into the n_cal * (128 / dsub)
+ * points, point p = row p / J, sub-vector p % J; an index outside that range
+ * is clamped into it): assign each point to its nearest
+ * centroid (same fp64 rule as vqkv_quantize_append), then move each centroid
+ * to the mean of its points; a centroid without points stays.  After `iters`
+ * iterations the centroids are rounded to fp16 (nearest, ties to even).
+ *   rows       device, [n_cal][128], dtype
+ *   smooth     device, fp32 [128] (keys only; may be NULL for values)
+ *   book       device, fp16 [E][dsub] (output)
+ *   centroids  device, fp64 [E][dsub] (output, before rounding; may be NULL)
+ *   workspace  device, vqkv_train_workspace_bytes(fmt, n_cal) bytes
+ * Each centroid's sum is accumulated in fp64 in increasing point order, so the
+ * result does not depend on scheduling and is the same on every run. */
+vqkv_status vqkv_train_codebook(int32_t fmt, int32_t n_cal, const void* rows, int32_t dtype,
+                                int32_t is_key, const float* smooth, const int64_t* init_idx,
+                                int32_t iters, uint16_t* book, double* centroids,
+                                void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQKV_H */

@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host with the documented status, before any
+device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import vector_quantized_bit_vqkv_amd as vq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED = 1, 2
+
+
+def _declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vqkv_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(vq.LIB_PATH)
+    names = _declared("vqkv.h")
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_size_queries():
+    assert vq.code_bytes_per_token(vq.FMT_2BIT) == 32
+    assert vq.code_bytes_per_token(vq.FMT_1P5BIT) == 24
+    assert vq.code_bytes_per_token(7) == 0
+    s = vq.make_shape(32, 32, 8, 196608, vq.FMT_2BIT)
+    assert vq.cache_bytes(s) == 32 * 8 * 196608 * 32
+    ws = vq.workspace_bytes(s, 2)
+    assert ws >= 32 * 32 * 2 * 129 * 4
+    assert vq.workspace_bytes(s, 0) == 0
+    bad = vq.make_shape(1, 32, 8, 100, vq.FMT_2BIT)
+    assert vq.cache_bytes(bad) == 0
+    assert 1 <= vq.suggest_splits(vq.make_shape(1, 32, 8, 196608, 0), 196608) <= 3072
+
+
+def _status(fn, *args):
+    return int(getattr(vq.lib(), fn)(*args))
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: checks fail first
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def test_shape_validation():
+    L = vq.lib()
+    good = vq.make_shape(1, 32, 8, 1024, vq.FMT_2BIT)
+    cases = [
+        (None, INVALID),
+        (vq.make_shape(1, 32, 8, 1024, vq.FMT_2BIT, head_dim=64), UNSUPPORTED),
+        (vq.make_shape(0, 32, 8, 1024, vq.FMT_2BIT), INVALID),
+        (vq.make_shape(1, 30, 8, 1024, vq.FMT_2BIT), INVALID),
+        (vq.make_shape(1, 72, 8, 1024, vq.FMT_2BIT), UNSUPPORTED),
+        (vq.make_shape(1, 32, 8, 1000, vq.FMT_2BIT), INVALID),
+        (vq.make_shape(1, 32, 8, 1024, 5), INVALID),
+    ]
+    for shp, want in cases:
+        arg = ctypes.byref(shp) if shp is not None else None
+        st = L.vqkv_decode_attention(arg, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 0.088, 1, FAKE, None)
+        assert st == want, (shp and (shp.batch, shp.num_q_heads, shp.head_dim, shp.max_tokens, shp.fmt), st)
+        assert L.vqkv_last_error().decode()
+    assert L.vqkv_decode_attention(ctypes.byref(good), None, FAKE, FAKE, FAKE, FAKE, 10, 0.088, 1, FAKE, None) == INVALID
+    assert b"q_prime" in L.vqkv_last_error()
+
+
+def test_decode_argument_checks():
+    L = vq.lib()
+    sh = ctypes.byref(vq.make_shape(1, 32, 8, 1024, vq.FMT_2BIT))
+    call = lambda seq, sm, S, ws=FAKE, q=FAKE: L.vqkv_decode_attention(sh, q, FAKE, FAKE, FAKE, FAKE, seq, sm, S, ws, None)
+    assert call(0, 0.088, 1) == INVALID                 # empty context
+    assert call(1025, 0.088, 1) == INVALID              # beyond capacity
+    assert call(100, float("nan"), 1) == INVALID
+    assert call(100, float("inf"), 1) == INVALID
+    assert call(100, 0.088, 0) == INVALID
+    assert call(100, 0.088, 3) == INVALID               # more splits than 64-token tiles
+    assert call(100, 0.088, 1, ws=MISALIGNED) == INVALID
+    assert call(100, 0.088, 1, q=None) == INVALID
+
+
+def test_append_argument_checks():
+    L = vq.lib()
+    sh = ctypes.byref(vq.make_shape(2, 8, 2, 128, vq.FMT_1P5BIT))
+    call = lambda dt, n, start, k=FAKE: L.vqkv_quantize_append(sh, k, FAKE, dt, n, start, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert call(0, 0, 0) == INVALID
+    assert call(0, 1, -1) == INVALID
+    assert call(0, 100, 29) == INVALID                  # 129 > capacity
+    assert call(9, 1, 0) == INVALID                     # dtype
+    assert call(0, 1, 0, k=MISALIGNED) == INVALID
+    assert call(0, 1, 0, k=None) == INVALID
+
+
+def test_transform_combine_and_calibration_checks():
+    L = vq.lib()
+    sh = ctypes.byref(vq.make_shape(1, 4, 1, 64, vq.FMT_2BIT))
+    assert L.vqkv_transform_query(sh, FAKE, 3, FAKE, FAKE, None) == INVALID
+    assert L.vqkv_transform_query(sh, FAKE, 0, None, FAKE, None) == INVALID
+    assert L.vqkv_combine(sh, 0, FAKE, FAKE, None) == INVALID
+    assert L.vqkv_combine(sh, 1, FAKE, None, None) == INVALID
+    assert L.vqkv_smooth_scales(0, 10, FAKE, 0, FAKE, None) == INVALID
+    assert L.vqkv_smooth_scales(1, 0, FAKE, 0, FAKE, None) == INVALID
+    assert vq.train_workspace_bytes(0, 4096) > 4096 * 128 * 8
+    assert vq.train_workspace_bytes(3, 4096) == 0
+    # 1.5-bit needs at least 4096 points: 255 rows x 16 sub-vectors is too few.
+    assert L.vqkv_train_codebook(1, 255, FAKE, 0, 0, None, FAKE, 20, FAKE, None, FAKE, None) == INVALID
+    assert L.vqkv_train_codebook(0, 64, FAKE, 0, 1, None, FAKE, 20, FAKE, None, FAKE, None) == INVALID  # key needs smooth
+    assert L.vqkv_train_codebook(0, 64, FAKE, 0, 0, None, FAKE, -1, FAKE, None, FAKE, None) == INVALID
+
+
+def test_status_strings():
+    L = vq.lib()
+    assert L.vqkv_status_string(0) == b"ok"
+    assert L.vqkv_status_string(1) == b"invalid argument"
+    assert L.vqkv_status_string(99) == b"unknown status"
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(vq, "_lib", None)
+    monkeypatch.setattr(vq, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        vq.lib()

@@ -1,0 +1,426 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars: codes, smoothing scales and codebooks bit-exact; attention outputs
+within 2e-3 max relative error, measured per (b, q-head) as
+max|o_gpu - o_ref| / max|o_ref|; the query transform within the fp32 bound
+derived below.  Inputs come from ``synth`` (seeded) or from torch's seeded
+device generator; no oracle input comes from the HIP path.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+import vector_quantized_bit_vqkv_amd as vq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-3
+D = 128
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def book_dev(bits):
+    return dev(np.ascontiguousarray(bits).view(np.int16))
+
+
+def rel_err(got, ref):
+    """Per (b, g): max|got - ref| / max|ref|; returns the worst."""
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return float((num / den).max())
+
+
+def run_decode(shape, q_prime, kb, vb, kc, vc, T, S, path=None):
+    ws = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+    out = torch.empty((shape.batch, shape.num_q_heads, D), dtype=torch.float32, device=DEV)
+    old = os.environ.get("VQKV_DECODE_PATH")
+    try:
+        if path:
+            os.environ["VQKV_DECODE_PATH"] = path
+        else:
+            os.environ.pop("VQKV_DECODE_PATH", None)
+        vq.decode_attention(shape, q_prime, kb, vb, kc, vc, T, S, ws)
+    finally:
+        if old is None:
+            os.environ.pop("VQKV_DECODE_PATH", None)
+        else:
+            os.environ["VQKV_DECODE_PATH"] = old
+    vq.combine(shape, S, ws, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+# ------------------------------------------------------------------ query transform
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("B,Hq,Hkv", [(1, 4, 1), (3, 32, 8), (2, 40, 8), (1, 8, 8)])
+def test_transform_query(dtype, B, Hq, Hkv):
+    say(f"transform_query {dtype} B{B} Hq{Hq} Hkv{Hkv}")
+    rng = np.random.default_rng(B * 100 + Hq)
+    q = synth.normal_numpy(rng, (B, Hq, D), dtype)
+    s = rng.uniform(0.3, 8.0, (Hkv, D)).astype(np.float32)
+    shape = vq.make_shape(B, Hq, Hkv, 64, 0)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    vq.transform_query(shape, dev(q, torch.bfloat16 if dtype == "bf16" else torch.float32), dev(s), qp)
+    got = qp.cpu().numpy()
+    G = Hq // Hkv
+    for b in range(B):
+        for g in range(Hq):
+            h = g // G
+            ref = oracle.transform_query(q[b, g], s[h])
+            # fp32: one rounding in q*s, seven butterfly stages and the scale, each
+            # at most 2^-24 relative, and H is orthogonal, so the error norm stays
+            # below 10 * 2^-24 * ||q * s||.
+            bound = 10 * 2.0 ** -24 * np.linalg.norm(q[b, g].astype(np.float64) * s[h])
+            assert np.abs(got[b, g] - ref).max() <= bound
+
+
+# ------------------------------------------------------------------- calibration
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_smooth_scales_bit_exact(dtype):
+    say(f"smooth_scales {dtype}")
+    case = synth.make_cpu_case(synth.dataclasses.replace(synth.WORKLOADS["llama8b_b1_t32k"], dtype=dtype), 3,
+                               seq_len=1, n_cal=777)
+    out = torch.empty((8, D), dtype=torch.float32, device=DEV)
+    vq.smooth_scales(dev(case.k_cal, torch.bfloat16 if dtype == "bf16" else torch.float32), out)
+    got = out.cpu().numpy()
+    for h in range(8):
+        assert np.array_equal(got[h], oracle.smooth_scales(case.k_cal[h]))
+
+
+@pytest.mark.parametrize("fmt,n_cal,iters", [(0, 1024, 20), (1, 512, 4)])
+@pytest.mark.parametrize("is_key", [True, False])
+def test_train_codebook_bit_exact(fmt, n_cal, iters, is_key):
+    say(f"train_codebook fmt{fmt} n_cal{n_cal} iters{iters} key{is_key}")
+    E, dsub = oracle.FORMATS[fmt]
+    case = synth.make_cpu_case(synth.WORKLOADS["llama8b_b1_t32k"], 4, seq_len=1, n_cal=n_cal)
+    rows = case.k_cal[0] if is_key else case.v_cal[0]
+    s = oracle.smooth_scales(case.k_cal[0])
+    init = synth.kmeans_init_indices(5 + fmt, n_cal * (D // dsub), E)
+    pts = (oracle.transform_keys(rows, s) if is_key else rows.astype(np.float64)).reshape(-1, dsub)
+    cent_ref, _ = oracle.kmeans(pts, init, iters)
+    book_ref = oracle.doubles_to_half(cent_ref)
+    book = torch.empty((E, dsub), dtype=torch.int16, device=DEV)
+    cent = torch.empty((E, dsub), dtype=torch.float64, device=DEV)
+    ws = torch.empty(vq.train_workspace_bytes(fmt, n_cal), dtype=torch.uint8, device=DEV)
+    vq.train_codebook(fmt, dev(rows, torch.bfloat16), is_key, dev(s), dev(init), iters, book, ws, cent)
+    torch.cuda.synchronize()
+    assert np.array_equal(cent.cpu().numpy().view(np.uint64), cent_ref.view(np.uint64))
+    assert np.array_equal(book.cpu().numpy().view(np.uint16), book_ref)
+
+
+# -------------------------------------------------------------------- quantizer
+
+def _quant_case(fmt, B, Hkv, n, dtype, seed):
+    E, dsub = oracle.FORMATS[fmt]
+    wl = synth.dataclasses.replace(synth.WORKLOADS["llama8b_b1_t32k"], num_kv_heads=Hkv, num_q_heads=Hkv,
+                                   dtype=dtype)
+    case = synth.make_cpu_case(wl, seed, seq_len=n, n_cal=256, batch=B)
+    s = np.stack([oracle.smooth_scales(case.k_cal[h]) for h in range(Hkv)])
+    # Books drawn near the data's scale; parity does not depend on book quality.
+    kb = synth.random_fp16_book(seed, (Hkv, E, dsub), 0.5)
+    vb = synth.random_fp16_book(seed + 1, (Hkv, E, dsub), 1.0)
+    return case, s, kb, vb
+
+
+def _oracle_codes(fmt, case, s, kb, vb):
+    B, Hkv, n, _ = case.k.shape
+    J = D // oracle.FORMATS[fmt][1]
+    kc = np.zeros((B, Hkv, n, J), np.uint16)
+    vc = np.zeros((B, Hkv, n, J), np.uint16)
+    for b in range(B):
+        for h in range(Hkv):
+            kc[b, h], vc[b, h] = oracle.quantize(fmt, case.k[b, h], case.v[b, h], s[h], kb[h], vb[h])
+    return kc, vc
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_append_bit_exact_with_ragged_appends(fmt, dtype):
+    """A prefill of 37 tokens at 0, then appends of 1, 2, 1, 17 and 64 tokens at
+    odd and even positions; every code bit-exact and every byte outside the
+    appended positions untouched (the 1.5-bit value rows share a byte between
+    neighbouring tokens)."""
+    say(f"quantize_append fmt{fmt} {dtype}")
+    B, Hkv, cap = 2, 3, 192
+    pieces = [(0, 37), (37, 1), (38, 2), (40, 1), (41, 17), (58, 64)]
+    n = 122
+    case, s, kb, vb = _quant_case(fmt, B, Hkv, n, dtype, 40 + fmt)
+    kc_ref, vc_ref = _oracle_codes(fmt, case, s, kb, vb)
+    shape = vq.make_shape(B, Hkv, Hkv, cap, fmt)
+    W = vq.code_bytes_per_token(fmt)
+    sentinel = np.random.default_rng(1).integers(0, 256, (B, Hkv, cap * W), dtype=np.uint8)
+    kcodes, vcodes = dev(sentinel), dev(sentinel)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for start, cnt in pieces:
+        k_new = dev(case.k[:, :, start:start + cnt], tdt).contiguous()
+        v_new = dev(case.v[:, :, start:start + cnt], tdt).contiguous()
+        vq.quantize_append(shape, k_new, v_new, start, dev(s), book_dev(kb), book_dev(vb), kcodes, vcodes)
+    torch.cuda.synchronize()
+    gk, gv = kcodes.cpu().numpy(), vcodes.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            assert np.array_equal(oracle.unpack_k(fmt, gk[b, h], n), kc_ref[b, h])
+            assert np.array_equal(oracle.unpack_v(fmt, gv[b, h], n), vc_ref[b, h])
+            # Bytes of positions >= n keep the sentinel: repack the reference over it.
+            expect_k = oracle.pack_k(fmt, kc_ref[b, h], cap, sentinel[b, h].copy())
+            expect_v = oracle.pack_v(fmt, vc_ref[b, h], cap, sentinel[b, h].copy())
+            assert np.array_equal(gk[b, h], expect_k)
+            assert np.array_equal(gv[b, h], expect_v)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_ties_go_to_lowest_index(fmt):
+    """Duplicate codebook entries and values exactly halfway between two entries."""
+    say(f"quantize ties fmt{fmt}")
+    E, dsub = oracle.FORMATS[fmt]
+    J = D // dsub
+    rng = np.random.default_rng(7)
+    kb = synth.random_fp16_book(3, (1, E, dsub), 0.5)
+    kb[0, 200] = kb[0, 17]                                      # duplicate: 17 must win over 200
+    vb = np.zeros((1, E, dsub), np.float16)
+    vb[0, :, 0] = np.arange(E, dtype=np.float64) * 0.25          # entries 0, .25, .5, ... on dim 0
+    vb = vb.view(np.uint16)
+    n = 64
+    v = np.zeros((n, D), np.float32)
+    v[:, ::dsub] = (rng.integers(0, 200, (n, J)) * 0.25 + 0.125).astype(np.float32)   # exact midpoints
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    s = np.ones(D, np.float32)
+    kc_ref, vc_ref = oracle.quantize(fmt, k, v, s, kb[0], vb[0])
+    shape = vq.make_shape(1, 1, 1, 64, fmt)
+    kcodes = torch.zeros((1, 1, 64 * vq.code_bytes_per_token(fmt)), dtype=torch.uint8, device=DEV)
+    vcodes = torch.zeros_like(kcodes)
+    vq.quantize_append(shape, dev(k[None, None]), dev(v[None, None]), 0, dev(s[None]), book_dev(kb),
+                       book_dev(vb), kcodes, vcodes)
+    torch.cuda.synchronize()
+    gk = oracle.unpack_k(fmt, kcodes[0, 0].cpu().numpy(), n)
+    gv = oracle.unpack_v(fmt, vcodes[0, 0].cpu().numpy(), n)
+    assert np.array_equal(gk, kc_ref) and np.array_equal(gv, vc_ref)
+    assert not np.any(gk == 200)
+    # Halfway between entries m and m+1 the lower index wins.
+    assert np.array_equal(gv, (v[:, ::dsub] / 0.25 - 0.5).astype(np.uint16))
+
+
+# ---------------------------------------------------------------------- attention
+
+def _attn_inputs(fmt, B, Hq, Hkv, T, seed, cap=None):
+    E, dsub = oracle.FORMATS[fmt]
+    J = D // dsub
+    cap = cap or ((T + 63) // 64) * 64
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    s = rng.uniform(0.5, 4.0, (Hkv, D)).astype(np.float32)
+    kb = synth.random_fp16_book(seed, (Hkv, E, dsub), 0.6)
+    vb = synth.random_fp16_book(seed + 1, (Hkv, E, dsub), 1.0)
+    kc = synth.random_codes(seed, (B, Hkv, T, J), E)
+    vc = synth.random_codes(seed + 1, (B, Hkv, T, J), E)
+    return q, s, kb, vb, kc, vc, cap
+
+
+def _gpu_attention(fmt, q, s, kb, vb, kc, vc, cap, S, path=None):
+    B, Hq, _ = q.shape
+    _, Hkv, T, _ = kc.shape
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    vq.transform_query(shape, dev(q), dev(s), qp)
+    return run_decode(shape, qp, book_dev(kb), book_dev(vb), dev(kbytes), dev(vbytes), T, S, path)
+
+
+ATTN_CASES = [
+    # fmt, B, Hq, Hkv, T, S, path
+    (0, 1, 4, 1, 2048, 1, "table"),
+    (0, 1, 4, 1, 2048, 32, "table"),
+    (0, 1, 4, 1, 2048, 4, "gather"),
+    (0, 2, 32, 8, 1, 1, None),
+    (0, 2, 32, 8, 65, 2, None),
+    (0, 1, 8, 8, 777, 5, "table"),
+    (0, 1, 8, 8, 777, 5, "gather"),
+    (0, 1, 6, 2, 1000, 3, "table"),
+    (0, 2, 12, 4, 4099, 9, "table"),
+    (0, 2, 12, 4, 4099, 9, "gather"),
+    (0, 1, 16, 2, 333, 2, None),           # G = 8: gather
+    (0, 1, 10, 2, 129, 3, None),           # G = 5: gather
+    (1, 1, 40, 8, 1000, 4, None),
+    (1, 2, 5, 1, 64, 1, None),
+    (1, 1, 8, 1, 129, 3, None),
+    (1, 1, 2, 2, 3001, 7, None),
+]
+
+
+@pytest.mark.parametrize("fmt,B,Hq,Hkv,T,S,path", ATTN_CASES)
+def test_decode_matches_oracle(fmt, B, Hq, Hkv, T, S, path):
+    say(f"decode fmt{fmt} B{B} Hq{Hq} Hkv{Hkv} T{T} S{S} path={path}")
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, B, Hq, Hkv, T, 1000 + T + Hq)
+    got = _gpu_attention(fmt, q, s, kb, vb, kc, vc, cap, S, path)
+    ref = oracle.attention(fmt, q, s, kb, vb, kc, vc)
+    err = rel_err(got, ref)
+    print(f"  max relative error {err:.3e}", flush=True)
+    assert err <= TOL
+
+
+def test_decode_single_token_returns_its_value():
+    say("decode T=1")
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(0, 1, 8, 2, 1, 77, cap=128)
+    got = _gpu_attention(0, q, s, kb, vb, kc, vc, cap, 1)
+    for g in range(8):
+        h = g // 4
+        v0 = vb[h].view(np.float16).astype(np.float64)[vc[0, h, 0]].reshape(D)
+        assert np.abs(got[0, g] - v0).max() <= 1e-6 * np.abs(v0).max()
+
+
+def test_decode_split_invariance_and_determinism():
+    say("decode splits 1 vs 64, rerun")
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(0, 1, 32, 8, 4096, 5)
+    a = _gpu_attention(0, q, s, kb, vb, kc, vc, cap, 1)
+    b = _gpu_attention(0, q, s, kb, vb, kc, vc, cap, 64)
+    c = _gpu_attention(0, q, s, kb, vb, kc, vc, cap, 64)
+    assert rel_err(b, a) < 1e-5
+    assert np.array_equal(b.view(np.uint32), c.view(np.uint32))
+
+
+def test_decode_ignores_bytes_past_seq_len():
+    """Codes beyond seq_len (inside the capacity) must not change the result."""
+    say("decode garbage past seq_len")
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(0, 1, 4, 1, 100, 9, cap=256)
+    shape = vq.make_shape(1, 4, 1, cap, 0)
+    kbytes, vbytes = oracle.pack_stream(0, kc, vc, cap)
+    noise = np.random.default_rng(3).integers(0, 256, kbytes.shape, dtype=np.uint8)
+    kb2, vb2 = noise.copy(), noise.copy()
+    kb2[..., :100 * 32] = kbytes[..., :100 * 32]
+    # value blocks are 32 tokens; the first 100 tokens live in blocks 0..3 (partly)
+    for t in range(100):
+        for j in range(32):
+            vb2[0, 0, (t // 32) * 1024 + j * 32 + t % 32] = vbytes[0, 0, (t // 32) * 1024 + j * 32 + t % 32]
+    qp = torch.empty((1, 4, D), dtype=torch.float32, device=DEV)
+    vq.transform_query(shape, dev(q), dev(s), qp)
+    a = run_decode(shape, qp, book_dev(kb), book_dev(vb), dev(kbytes), dev(vbytes), 100, 2)
+    b = run_decode(shape, qp, book_dev(kb), book_dev(vb), dev(kb2), dev(vb2), 100, 2)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_end_to_end_tiny_workload():
+    """The tiny 2-bit workload end to end: GPU calibration (scales, 20-iteration
+    K-Means books) equals the oracle's, GPU codes equal the oracle's, and the
+    GPU decode is within 2e-3 of the oracle's attention."""
+    wl = synth.WORKLOADS["tiny_g4_t2048"]
+    say(wl.name)
+    case = synth.make_cpu_case(wl, synth.seed_for(wl.name))
+    s_ref = oracle.smooth_scales(case.k_cal[0])
+    init_k = synth.kmeans_init_indices(11, synth.N_CALIB * 32, 256)
+    init_v = synth.kmeans_init_indices(12, synth.N_CALIB * 32, 256)
+    kb_ref, vb_ref = oracle.train_codebooks(0, case.k_cal[0], case.v_cal[0], s_ref, init_k, init_v, iters=20)
+
+    smooth = torch.empty((1, D), dtype=torch.float32, device=DEV)
+    vq.smooth_scales(dev(case.k_cal), smooth)
+    ws = torch.empty(vq.train_workspace_bytes(0, synth.N_CALIB), dtype=torch.uint8, device=DEV)
+    k_book = torch.empty((1, 256, 4), dtype=torch.int16, device=DEV)
+    v_book = torch.empty((1, 256, 4), dtype=torch.int16, device=DEV)
+    vq.train_codebook(0, dev(case.k_cal[0]), True, smooth[0], dev(init_k), 20, k_book[0], ws)
+    vq.train_codebook(0, dev(case.v_cal[0]), False, None, dev(init_v), 20, v_book[0], ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(smooth.cpu().numpy()[0], s_ref)
+    assert np.array_equal(k_book.cpu().numpy()[0].view(np.uint16), kb_ref)
+    assert np.array_equal(v_book.cpu().numpy()[0].view(np.uint16), vb_ref)
+
+    shape = vq.make_shape(1, 4, 1, 2048, 0)
+    cache = vq.VQCache.allocate(shape, smooth, k_book, v_book, DEV)
+    cache.append(dev(case.k), dev(case.v), 0)
+    out = cache.attend(dev(case.q), 2048, num_splits=8).cpu().numpy()
+    kc, vc = oracle.quantize(0, case.k[0, 0], case.v[0, 0], s_ref, kb_ref, vb_ref)
+    assert np.array_equal(oracle.unpack_k(0, cache.k_codes[0, 0].cpu().numpy(), 2048), kc)
+    assert np.array_equal(oracle.unpack_v(0, cache.v_codes[0, 0].cpu().numpy(), 2048), vc)
+    ref = oracle.attention(0, case.q, s_ref[None], kb_ref[None], vb_ref[None], kc[None, None], vc[None, None])
+    assert rel_err(out, ref) <= TOL
+    # Quality, not parity: the 2-bit cache stays close to full-precision attention.
+    fp = oracle.attention_fp(case.q, case.k, case.v)
+    print(f"  VQ vs full precision: {rel_err(ref, fp):.3f}", flush=True)
+
+
+# ---------------------------------------------------------- full sizes, sampled
+
+FULL = ["llama8b_b1_t32k", "llama8b_b1_t196k", "llama8b_b32_t196k", "qwen14b_b8_t128k_1p5"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    """The workload at its full size, in the benchmark's launch configuration
+    (suggested split count, auto path), with random codes drawn on the device;
+    sampled (b, KV head) slices are checked against the oracle."""
+    wl = synth.WORKLOADS[name]
+    say(f"full size {name}")
+    fmt, B, Hq, Hkv, T = wl.fmt, wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.seq_len
+    E, dsub = oracle.FORMATS[fmt]
+    seed = synth.seed_for(name)
+    W = vq.code_bytes_per_token(fmt)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    kbytes = torch.randint(0, 256, (B, Hkv, T * W), generator=gen, dtype=torch.uint8, device=DEV)
+    vbytes = torch.randint(0, 256, (B, Hkv, T * W), generator=gen, dtype=torch.uint8, device=DEV)
+    kb = synth.random_fp16_book(seed, (Hkv, E, dsub), 0.6)
+    vb = synth.random_fp16_book(seed + 1, (Hkv, E, dsub), 1.0)
+    rng = np.random.default_rng(seed)
+    q = synth.normal_numpy(rng, (B, Hq, D), "bf16")
+    s = rng.uniform(0.5, 4.0, (Hkv, D)).astype(np.float32)
+    shape = vq.make_shape(B, Hq, Hkv, T, fmt)
+    S = vq.suggest_splits(shape, T)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    vq.transform_query(shape, dev(q, torch.bfloat16), dev(s), qp)
+    got = run_decode(shape, qp, book_dev(kb), book_dev(vb), kbytes, vbytes, T, S)
+    G = Hq // Hkv
+    samples = [(b, h) for b in range(B) for h in range(Hkv)]
+    pick = np.random.default_rng(seed).permutation(len(samples))[: (8 if B == 1 else 4)]
+    worst = 0.0
+    for i in pick:
+        b, h = samples[i]
+        kc = oracle.unpack_k(fmt, kbytes[b, h].cpu().numpy(), T)[None, None]
+        vc = oracle.unpack_v(fmt, vbytes[b, h].cpu().numpy(), T)[None, None]
+        ref = oracle.attention(fmt, q[b:b + 1, h * G:(h + 1) * G], s[h:h + 1], kb[h:h + 1], vb[h:h + 1], kc, vc)
+        worst = max(worst, rel_err(got[b:b + 1, h * G:(h + 1) * G], ref))
+    print(f"  S={S} max relative error over {len(pick)} slices: {worst:.3e}", flush=True)
+    assert worst <= TOL
+
+
+def test_full_size_append_one_token():
+    """The 196k single-sequence workload's per-step append: one bf16 token at
+    the last position of every KV head, bit-exact against the oracle."""
+    wl = synth.WORKLOADS["llama8b_b1_t196k"]
+    say("append one token at position 196607")
+    T, Hkv = wl.seq_len, wl.num_kv_heads
+    case, s, kb, vb = _quant_case(0, 1, Hkv, 1, "bf16", 99)
+    shape = vq.make_shape(1, Hkv, Hkv, T, 0)
+    kcodes = torch.zeros((1, Hkv, T * 32), dtype=torch.uint8, device=DEV)
+    vcodes = torch.zeros_like(kcodes)
+    vq.quantize_append(shape, dev(case.k, torch.bfloat16), dev(case.v, torch.bfloat16), T - 1, dev(s),
+                       book_dev(kb), book_dev(vb), kcodes, vcodes)
+    torch.cuda.synchronize()
+    kc_ref, vc_ref = _oracle_codes(0, case, s, kb, vb)
+    gk = kcodes[0, :, (T - 1) * 32:].cpu().numpy()
+    t = T - 1
+    gv = vcodes[0].cpu().numpy()[:, [(t // 32) * 1024 + j * 32 + t % 32 for j in range(32)]]
+    assert np.array_equal(gk, kc_ref[0, :, 0])
+    assert np.array_equal(gv, vc_ref[0, :, 0])
+
+
+def test_library_is_the_in_tree_build():
+    path = vq.lib()._name
+    assert os.path.abspath(path) == os.path.abspath(vq.LIB_PATH)
+    maps = open("/proc/self/maps").read()
+    assert os.path.realpath(vq.LIB_PATH) in maps or vq.LIB_PATH in maps

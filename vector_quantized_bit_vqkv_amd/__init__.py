@@ -1,0 +1,231 @@
+"""libvqkv: decode attention over a vector-quantized KV cache on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/vqkv.h``.  Every function
+here only checks and marshals arguments (torch tensors supply device memory
+and the current HIP stream); all computation runs in the HIP kernels of
+``libvqkv.so``.  There is no CPU fallback: if the library is missing, importing
+this package raises.
+
+Method (VecInfer, arXiv 2510.06175; research.elamur.ai summary card): keys are
+smoothed per channel and Hadamard-rotated, keys and values are stored as
+K-Means codebook indices (2^8 x 4 for 2 bits, 2^12 x 8 for 1.5 bits), the
+query gets the inverse transform, and attention dequantizes inside the kernel.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvqkv.so")
+
+FMT_2BIT = 0
+FMT_1P5BIT = 1
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+HEAD_DIM = 128
+ENTRIES = {FMT_2BIT: 256, FMT_1P5BIT: 4096}
+DSUB = {FMT_2BIT: 4, FMT_1P5BIT: 8}
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP runtime error"}
+
+
+class VqkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("fmt", ctypes.c_int32)]
+
+
+def make_shape(batch: int, num_q_heads: int, num_kv_heads: int, max_tokens: int, fmt: int,
+               head_dim: int = HEAD_DIM) -> Shape:
+    return Shape(batch, num_q_heads, num_kv_heads, head_dim, max_tokens, fmt)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvqkv.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with `python -m vector_quantized_bit_vqkv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    SP = ctypes.POINTER(Shape)
+    sig = {
+        "vqkv_code_bytes_per_token": (SZ, [I32]),
+        "vqkv_cache_bytes": (SZ, [SP]),
+        "vqkv_workspace_bytes": (SZ, [SP, I32]),
+        "vqkv_suggest_splits": (I32, [SP, I32]),
+        "vqkv_status_string": (ctypes.c_char_p, [I32]),
+        "vqkv_last_error": (ctypes.c_char_p, []),
+        "vqkv_transform_query": (I32, [SP, P, I32, P, P, P]),
+        "vqkv_quantize_append": (I32, [SP, P, P, I32, I32, I32, P, P, P, P, P, P]),
+        "vqkv_decode_attention": (I32, [SP, P, P, P, P, P, I32, F32, I32, P, P]),
+        "vqkv_combine": (I32, [SP, I32, P, P, P]),
+        "vqkv_smooth_scales": (I32, [I32, I32, P, I32, P, P]),
+        "vqkv_train_workspace_bytes": (SZ, [I32, I32]),
+        "vqkv_train_codebook": (I32, [I32, I32, P, I32, I32, P, P, I32, P, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise VqkvError(status, lib().vqkv_last_error().decode())
+
+
+def _ptr(t) -> ctypes.c_void_p | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t) -> ctypes.c_void_p:
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------------- sizes
+
+def code_bytes_per_token(fmt: int) -> int:
+    return int(lib().vqkv_code_bytes_per_token(fmt))
+
+
+def cache_bytes(shape: Shape) -> int:
+    return int(lib().vqkv_cache_bytes(ctypes.byref(shape)))
+
+
+def workspace_bytes(shape: Shape, num_splits: int) -> int:
+    return int(lib().vqkv_workspace_bytes(ctypes.byref(shape), num_splits))
+
+
+def suggest_splits(shape: Shape, seq_len: int) -> int:
+    return int(lib().vqkv_suggest_splits(ctypes.byref(shape), seq_len))
+
+
+# ---------------------------------------------------------------------- hot path
+
+def transform_query(shape: Shape, q, smooth, q_prime) -> None:
+    """q' = H (q * s): q [B][Hq][128] bf16/fp32, smooth fp32 [Hkv][128], q_prime fp32 out."""
+    _check(lib().vqkv_transform_query(ctypes.byref(shape), _ptr(q), _dtype_code(q), _ptr(smooth),
+                                      _ptr(q_prime), _stream(q)))
+
+
+def quantize_append(shape: Shape, k_new, v_new, start_pos: int, smooth, k_book, v_book, k_codes, v_codes) -> None:
+    """Codes for positions [start_pos, start_pos + n) from k_new, v_new [B][Hkv][n][128]."""
+    n_new = k_new.shape[2]
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must have the same shape and dtype")
+    _check(lib().vqkv_quantize_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), n_new,
+                                      start_pos, _ptr(smooth), _ptr(k_book), _ptr(v_book), _ptr(k_codes),
+                                      _ptr(v_codes), _stream(k_new)))
+
+
+def decode_attention(shape: Shape, q_prime, k_book, v_book, k_codes, v_codes, seq_len: int, num_splits: int,
+                     workspace, sm_scale: float | None = None) -> None:
+    """Split-context attention over the codes; partials go to `workspace`."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    _check(lib().vqkv_decode_attention(ctypes.byref(shape), _ptr(q_prime), _ptr(k_book), _ptr(v_book),
+                                       _ptr(k_codes), _ptr(v_codes), seq_len, sm_scale, num_splits,
+                                       _ptr(workspace), _stream(q_prime)))
+
+
+def combine(shape: Shape, num_splits: int, workspace, out) -> None:
+    """Log-sum-exp merge of the splits into out [B][Hq][128] fp32."""
+    _check(lib().vqkv_combine(ctypes.byref(shape), num_splits, _ptr(workspace), _ptr(out), _stream(out)))
+
+
+# ------------------------------------------------------------------- calibration
+
+def smooth_scales(k_cal, smooth) -> None:
+    """s[h][c] = sqrt(max_t |k_cal[h][t][c]|) for k_cal [Hkv][n][128]; smooth fp32 [Hkv][128] out."""
+    hkv, n = k_cal.shape[0], k_cal.shape[1]
+    _check(lib().vqkv_smooth_scales(hkv, n, _ptr(k_cal), _dtype_code(k_cal), _ptr(smooth), _stream(k_cal)))
+
+
+def train_workspace_bytes(fmt: int, n_cal: int) -> int:
+    return int(lib().vqkv_train_workspace_bytes(fmt, n_cal))
+
+
+def train_codebook(fmt: int, rows, is_key: bool, smooth, init_idx, iters: int, book, workspace,
+                   centroids=None) -> None:
+    """K-Means codebook for one KV head from calibration rows [n][128] (see vqkv.h)."""
+    n = rows.shape[0]
+    _check(lib().vqkv_train_codebook(fmt, n, _ptr(rows), _dtype_code(rows), int(bool(is_key)),
+                                     _ptr(smooth) if is_key else None, _ptr(init_idx), iters, _ptr(book),
+                                     _ptr(centroids), _ptr(workspace), _stream(rows)))
+
+
+# ------------------------------------------------------------------ a whole cache
+
+@dataclass
+class VQCache:
+    """Device buffers of one layer's quantized cache plus the decode scratch.
+
+    A convenience holder: it allocates with torch and calls the functions above.
+    """
+    shape: Shape
+    smooth: "object"        # fp32 [Hkv][128]
+    k_book: "object"        # fp16 bits (int16 tensor) [Hkv][E][dsub]
+    v_book: "object"
+    k_codes: "object"       # uint8 [B][Hkv][max_tokens * W]
+    v_codes: "object"
+
+    @staticmethod
+    def allocate(shape: Shape, smooth, k_book, v_book, device) -> "VQCache":
+        import torch
+        W = code_bytes_per_token(shape.fmt)
+        dims = (shape.batch, shape.num_kv_heads, shape.max_tokens * W)
+        return VQCache(shape, smooth, k_book, v_book,
+                       torch.zeros(dims, dtype=torch.uint8, device=device),
+                       torch.zeros(dims, dtype=torch.uint8, device=device))
+
+    def append(self, k_new, v_new, start_pos: int) -> None:
+        quantize_append(self.shape, k_new, v_new, start_pos, self.smooth, self.k_book, self.v_book,
+                        self.k_codes, self.v_codes)
+
+    def attend(self, q, seq_len: int, num_splits: int | None = None, out=None, q_prime=None, workspace=None):
+        import torch
+        if num_splits is None:
+            num_splits = suggest_splits(self.shape, seq_len)
+        B, Hq = self.shape.batch, self.shape.num_q_heads
+        if q_prime is None:
+            q_prime = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(workspace_bytes(self.shape, num_splits), dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        transform_query(self.shape, q, self.smooth, q_prime)
+        decode_attention(self.shape, q_prime, self.k_book, self.v_book, self.k_codes, self.v_codes, seq_len,
+                         num_splits, workspace)
+        combine(self.shape, num_splits, workspace, out)
+        return out

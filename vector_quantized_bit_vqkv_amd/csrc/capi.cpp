@@ -1,0 +1,266 @@
+// capi.cpp -- the extern "C" boundary of libvqkv: argument checks on the host,
+// then kernel launches on the caller's stream.  No allocation, no
+// synchronization, no global mutable state besides the per-thread error text.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/vqkv.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+vqkv_status fail(vqkv_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+vqkv_status ok() {
+    g_last_error[0] = '\0';
+    return VQKV_OK;
+}
+
+vqkv_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(VQKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int entries_of(int fmt) { return fmt == VQKV_FMT_2BIT ? 256 : 4096; }
+int dsub_of(int fmt) { return fmt == VQKV_FMT_2BIT ? 4 : 8; }
+
+// Checks shared by every call that takes a shape.  `need_cache` adds the
+// capacity and format checks.
+vqkv_status check_shape(const vqkv_shape* s, bool need_cache) {
+    if (!s) return fail(VQKV_ERR_INVALID_ARG, "shape is NULL");
+    if (s->head_dim != 128) return fail(VQKV_ERR_UNSUPPORTED, "head_dim %d unsupported (must be 128)", s->head_dim);
+    if (s->batch < 1) return fail(VQKV_ERR_INVALID_ARG, "batch %d < 1", s->batch);
+    if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+        return fail(VQKV_ERR_INVALID_ARG, "head counts must be >= 1 (Hq %d, Hkv %d)", s->num_q_heads, s->num_kv_heads);
+    if (s->num_q_heads % s->num_kv_heads != 0)
+        return fail(VQKV_ERR_INVALID_ARG, "Hq %d is not a multiple of Hkv %d", s->num_q_heads, s->num_kv_heads);
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if (G > 8) return fail(VQKV_ERR_UNSUPPORTED, "group size Hq/Hkv = %d exceeds 8", G);
+    if ((int64_t)s->batch * s->num_q_heads > (1 << 24))
+        return fail(VQKV_ERR_UNSUPPORTED, "batch * Hq too large");
+    if (need_cache) {
+        if (s->fmt != VQKV_FMT_2BIT && s->fmt != VQKV_FMT_1P5BIT)
+            return fail(VQKV_ERR_INVALID_ARG, "unknown format %d", s->fmt);
+        if (s->max_tokens < 64 || s->max_tokens % 64 != 0)
+            return fail(VQKV_ERR_INVALID_ARG, "max_tokens %d must be a positive multiple of 64", s->max_tokens);
+    }
+    return VQKV_OK;
+}
+
+#define VQKV_CHECK(expr)                         \
+    do {                                         \
+        vqkv_status _st = (expr);                \
+        if (_st != VQKV_OK) return _st;          \
+    } while (0)
+
+vqkv_status check_ptr(const void* p, const char* name) {
+    if (!p) return fail(VQKV_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(VQKV_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return VQKV_OK;
+}
+
+vqkv_status check_dtype(int32_t dt) {
+    if (dt != VQKV_DTYPE_BF16 && dt != VQKV_DTYPE_FP32) return fail(VQKV_ERR_INVALID_ARG, "unknown dtype %d", dt);
+    return VQKV_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Token range per split: 64-aligned, covering [0, seq_len) with `splits` ranges.
+int split_chunk(int seq_len, int splits) {
+    const int64_t tiles = ceil_div(seq_len, 64);
+    return (int)(ceil_div(tiles, splits) * 64);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Decode path override for measurement: VQKV_DECODE_PATH = "table" | "gather".
+int decode_path_from_env() {
+    const char* v = getenv("VQKV_DECODE_PATH");
+    if (!v || !*v) return 0;
+    if (!strcmp(v, "table")) return 1;
+    if (!strcmp(v, "gather")) return 2;
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t vqkv_code_bytes_per_token(int32_t fmt) {
+    if (fmt == VQKV_FMT_2BIT) return 32;
+    if (fmt == VQKV_FMT_1P5BIT) return 24;
+    return 0;
+}
+
+size_t vqkv_cache_bytes(const vqkv_shape* s) {
+    if (check_shape(s, true) != VQKV_OK) return 0;
+    return (size_t)s->batch * s->num_kv_heads * s->max_tokens * vqkv_code_bytes_per_token(s->fmt);
+}
+
+size_t vqkv_workspace_bytes(const vqkv_shape* s, int32_t num_splits) {
+    if (check_shape(s, false) != VQKV_OK || num_splits < 1) return 0;
+    const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
+    return align256(rows * 128 * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int32_t vqkv_suggest_splits(const vqkv_shape* s, int32_t seq_len) {
+    if (check_shape(s, false) != VQKV_OK || seq_len < 1) return 1;
+    const int64_t streams = (int64_t)s->batch * s->num_kv_heads;
+    const int64_t want = ceil_div(512, streams);              // two work-groups per CU on 256 CUs
+    const int64_t cap = ceil_div(seq_len, 1024);              // keep >= 1024 tokens per split
+    int64_t S = want < cap ? want : cap;
+    if (S < 1) S = 1;
+    return (int32_t)S;
+}
+
+const char* vqkv_status_string(int32_t st) {
+    switch (st) {
+        case VQKV_OK: return "ok";
+        case VQKV_ERR_INVALID_ARG: return "invalid argument";
+        case VQKV_ERR_UNSUPPORTED: return "unsupported";
+        case VQKV_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* vqkv_last_error(void) { return g_last_error; }
+
+vqkv_status vqkv_transform_query(const vqkv_shape* s, const void* q, int32_t q_dtype, const float* smooth,
+                                 float* q_prime, void* stream) {
+    VQKV_CHECK(check_shape(s, false));
+    VQKV_CHECK(check_dtype(q_dtype));
+    VQKV_CHECK(check_ptr(q, "q"));
+    VQKV_CHECK(check_ptr(smooth, "smooth"));
+    VQKV_CHECK(check_ptr(q_prime, "q_prime"));
+    vqkv::TransformQueryArgs a{q, q_dtype, smooth, q_prime, s->batch, s->num_q_heads, s->num_kv_heads};
+    return hip_status(vqkv::launch_transform_query(a, (hipStream_t)stream), "transform_query launch");
+}
+
+vqkv_status vqkv_quantize_append(const vqkv_shape* s, const void* k_new, const void* v_new, int32_t dtype,
+                                 int32_t n_new, int32_t start_pos, const float* smooth, const uint16_t* k_book,
+                                 const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, void* stream) {
+    VQKV_CHECK(check_shape(s, true));
+    VQKV_CHECK(check_dtype(dtype));
+    if (n_new < 1) return fail(VQKV_ERR_INVALID_ARG, "n_new %d < 1", n_new);
+    if (start_pos < 0) return fail(VQKV_ERR_INVALID_ARG, "start_pos %d < 0", start_pos);
+    if ((int64_t)start_pos + n_new > s->max_tokens)
+        return fail(VQKV_ERR_INVALID_ARG, "start_pos + n_new = %lld exceeds max_tokens %d",
+                    (long long)start_pos + n_new, s->max_tokens);
+    VQKV_CHECK(check_ptr(k_new, "k_new"));
+    VQKV_CHECK(check_ptr(v_new, "v_new"));
+    VQKV_CHECK(check_ptr(smooth, "smooth"));
+    VQKV_CHECK(check_ptr(k_book, "k_book"));
+    VQKV_CHECK(check_ptr(v_book, "v_book"));
+    VQKV_CHECK(check_ptr(k_codes, "k_codes"));
+    VQKV_CHECK(check_ptr(v_codes, "v_codes"));
+    vqkv::AppendArgs a{k_new, v_new, dtype, n_new, start_pos, smooth, k_book, v_book, k_codes, v_codes,
+                       s->batch, s->num_kv_heads, s->max_tokens, s->fmt};
+    return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append launch");
+}
+
+vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
+                                  const uint16_t* v_book, const uint8_t* k_codes, const uint8_t* v_codes,
+                                  int32_t seq_len, float sm_scale, int32_t num_splits, void* workspace,
+                                  void* stream) {
+    VQKV_CHECK(check_shape(s, true));
+    if (seq_len < 1 || seq_len > s->max_tokens)
+        return fail(VQKV_ERR_INVALID_ARG, "seq_len %d outside [1, max_tokens = %d]", seq_len, s->max_tokens);
+    if (!std::isfinite(sm_scale)) return fail(VQKV_ERR_INVALID_ARG, "sm_scale is not finite");
+    if (num_splits < 1 || num_splits > ceil_div(seq_len, 64))
+        return fail(VQKV_ERR_INVALID_ARG, "num_splits %d outside [1, ceil(seq_len / 64) = %lld]", num_splits,
+                    (long long)ceil_div(seq_len, 64));
+    VQKV_CHECK(check_ptr(q_prime, "q_prime"));
+    VQKV_CHECK(check_ptr(k_book, "k_book"));
+    VQKV_CHECK(check_ptr(v_book, "v_book"));
+    VQKV_CHECK(check_ptr(k_codes, "k_codes"));
+    VQKV_CHECK(check_ptr(v_codes, "v_codes"));
+    VQKV_CHECK(check_ptr(workspace, "workspace"));
+    const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
+    float* part_o = (float*)workspace;
+    float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
+    const int path = decode_path_from_env();
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if (path == 1 && !(s->fmt == VQKV_FMT_2BIT && G <= 4))
+        return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
+    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
+                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
+                       seq_len, num_splits, split_chunk(seq_len, num_splits),
+                       (float)((double)sm_scale * 1.4426950408889634), path};
+    return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention launch");
+}
+
+vqkv_status vqkv_combine(const vqkv_shape* s, int32_t num_splits, const void* workspace, float* out, void* stream) {
+    VQKV_CHECK(check_shape(s, false));
+    if (num_splits < 1) return fail(VQKV_ERR_INVALID_ARG, "num_splits %d < 1", num_splits);
+    VQKV_CHECK(check_ptr(workspace, "workspace"));
+    VQKV_CHECK(check_ptr(out, "out"));
+    const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
+    const float* part_o = (const float*)workspace;
+    const float* part_lse = (const float*)((const char*)workspace + align256(rows * 128 * sizeof(float)));
+    vqkv::CombineArgs a{part_o, part_lse, out, s->batch, s->num_q_heads, num_splits};
+    return hip_status(vqkv::launch_combine(a, (hipStream_t)stream), "combine launch");
+}
+
+vqkv_status vqkv_smooth_scales(int32_t num_kv_heads, int32_t n_cal, const void* k_cal, int32_t dtype,
+                               float* smooth, void* stream) {
+    if (num_kv_heads < 1) return fail(VQKV_ERR_INVALID_ARG, "num_kv_heads %d < 1", num_kv_heads);
+    if (n_cal < 1) return fail(VQKV_ERR_INVALID_ARG, "n_cal %d < 1", n_cal);
+    VQKV_CHECK(check_dtype(dtype));
+    VQKV_CHECK(check_ptr(k_cal, "k_cal"));
+    VQKV_CHECK(check_ptr(smooth, "smooth"));
+    return hip_status(vqkv::launch_smooth_scales(num_kv_heads, n_cal, k_cal, dtype, smooth, (hipStream_t)stream),
+                      "smooth_scales launch");
+}
+
+size_t vqkv_train_workspace_bytes(int32_t fmt, int32_t n_cal) {
+    if ((fmt != VQKV_FMT_2BIT && fmt != VQKV_FMT_1P5BIT) || n_cal < 1) return 0;
+    const size_t n_pts = (size_t)n_cal * (128 / dsub_of(fmt));
+    return align256((size_t)n_cal * 128 * sizeof(double)) + align256(n_pts * sizeof(int32_t)) +
+           align256((size_t)entries_of(fmt) * dsub_of(fmt) * sizeof(double));
+}
+
+vqkv_status vqkv_train_codebook(int32_t fmt, int32_t n_cal, const void* rows, int32_t dtype, int32_t is_key,
+                                const float* smooth, const int64_t* init_idx, int32_t iters, uint16_t* book,
+                                double* centroids, void* workspace, void* stream) {
+    if (fmt != VQKV_FMT_2BIT && fmt != VQKV_FMT_1P5BIT) return fail(VQKV_ERR_INVALID_ARG, "unknown format %d", fmt);
+    const int E = entries_of(fmt);
+    const int64_t n_pts = (int64_t)n_cal * (128 / dsub_of(fmt));
+    if (n_cal < 1 || n_pts < E)
+        return fail(VQKV_ERR_INVALID_ARG, "n_cal %d gives %lld points, fewer than %d entries", n_cal,
+                    (long long)n_pts, E);
+    if (n_cal > (1 << 22)) return fail(VQKV_ERR_UNSUPPORTED, "n_cal %d too large", n_cal);
+    if (iters < 0) return fail(VQKV_ERR_INVALID_ARG, "iters %d < 0", iters);
+    VQKV_CHECK(check_dtype(dtype));
+    VQKV_CHECK(check_ptr(rows, "rows"));
+    if (is_key) VQKV_CHECK(check_ptr(smooth, "smooth"));
+    VQKV_CHECK(check_ptr(init_idx, "init_idx"));
+    VQKV_CHECK(check_ptr(book, "book"));
+    if (centroids) VQKV_CHECK(check_ptr(centroids, "centroids"));
+    VQKV_CHECK(check_ptr(workspace, "workspace"));
+    char* ws = (char*)workspace;
+    double* points = (double*)ws;
+    ws += align256((size_t)n_cal * 128 * sizeof(double));
+    int32_t* assign = (int32_t*)ws;
+    ws += align256((size_t)n_pts * sizeof(int32_t));
+    double* cent = centroids ? centroids : (double*)ws;
+    vqkv::TrainArgs a{fmt, n_cal, dtype, is_key, iters, rows, smooth, init_idx, book, cent, points, assign};
+    return hip_status(vqkv::launch_train_codebook(a, (hipStream_t)stream), "train_codebook launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// internal.h -- launch functions shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vqkv {
+
+struct TransformQueryArgs {
+    const void* q;          // [B][Hq][128], bf16 or fp32
+    int dtype;              // 0 bf16, 1 fp32
+    const float* smooth;    // [Hkv][128]
+    float* q_prime;         // [B][Hq][128]
+    int batch, hq, hkv;
+};
+hipError_t launch_transform_query(const TransformQueryArgs& a, hipStream_t stream);
+
+struct AppendArgs {
+    const void* k_new;      // [B][Hkv][n][128]
+    const void* v_new;
+    int dtype;
+    int n_new, start_pos;
+    const float* smooth;    // [Hkv][128]
+    const uint16_t* k_book; // [Hkv][E][dsub]
+    const uint16_t* v_book;
+    uint8_t* k_codes;       // [B][Hkv][cap * W]
+    uint8_t* v_codes;
+    int batch, hkv, cap, fmt;
+};
+hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+    const float* q_prime;   // [B][Hq][128]
+    const uint16_t* k_book; // [Hkv][E][dsub]
+    const uint16_t* v_book;
+    const uint8_t* k_codes; // [B][Hkv][cap * W]
+    const uint8_t* v_codes;
+    float* part_o;          // [B][Hq][S][128]
+    float* part_lse;        // [B][Hq][S]  (log2 units)
+    int batch, hq, hkv, cap, fmt;
+    int seq_len, splits, chunk;
+    float qscale;           // sm_scale * log2(e)
+    int path;               // 0 auto, 1 score table (2-bit), 2 gather
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct CombineArgs {
+    const float* part_o;
+    const float* part_lse;
+    float* out;             // [B][Hq][128]
+    int batch, hq, splits;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// Offline calibration.
+hipError_t launch_smooth_scales(int hkv, int n_cal, const void* k_cal, int dtype, float* smooth,
+                                hipStream_t stream);
+
+struct TrainArgs {
+    int fmt, n_cal, dtype, is_key, iters;
+    const void* rows;       // [n_cal][128]
+    const float* smooth;    // [128] (keys)
+    const int64_t* init;    // [E] device
+    uint16_t* book;         // [E][dsub] fp16 out
+    double* centroids;      // [E][dsub] fp64 (workspace or caller buffer)
+    double* points;         // [n_cal * 128] fp64 workspace
+    int32_t* assign;        // [n_cal * J] workspace
+};
+hipError_t launch_train_codebook(const TrainArgs& a, hipStream_t stream);
+
+}  // namespace vqkv

@@ -1,0 +1,392 @@
+// quantize.hip -- key/value quantization into codebook indices, and the offline
+// calibration that produces the smoothing scales and K-Means codebooks.
+//
+// VecInfer summary card, "Summary", and the arXiv 2510.06175 page's
+// "technical framework" paragraph: keys are smoothed per channel and rotated
+// by a Hadamard transform, then keys and values are vector-quantized against
+// codebooks trained offline with K-Means ("Key points": 2^8 x 4 entries for
+// 2-bit, 2^12 x 8 for 1.5-bit).
+//
+// Every decision that turns floating point into an integer (a code, a K-Means
+// assignment) is taken in fp64 with one fixed operation sequence, so the
+// result is exactly reproducible:
+//   x = k / s            (fp64 divide, correctly rounded)
+//   FWHT butterflies     stage h = 1, 2, ..., 64, pair (j, j + h) -> (a + b, a - b)
+//   x *= 0x1.6a09e667f3bcdp-4   (fp64 nearest 1/sqrt(128))
+//   d_e = (x0 - c0)^2 + (x1 - c1)^2 + ...   left to right, no fused multiply-add
+//   code = the lowest e with the smallest d_e
+// This file is compiled with -ffp-contract=off and also says so below.
+#include "device_util.h"
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace vqkv {
+
+namespace {
+
+constexpr double kInvSqrtHeadDimD = 0x1.6a09e667f3bcdp-4;
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<0> { static constexpr int E = 256, DS = 4, J = 32, W = 32; };
+template <> struct Fmt<1> { static constexpr int E = 4096, DS = 8, J = 16, W = 24; };
+
+__device__ __forceinline__ double load_elem_d(const void* base, int64_t i, int dtype) {
+    return (double)load_elem(base, i, dtype);
+}
+
+// In-place normalized FWHT of `ntok` rows of 128 fp64 values in LDS, by the
+// whole block.  Caller synchronizes before (data written) and after.
+__device__ void block_fwht(double* x, int ntok) {
+    const int nb = ntok * 64;   // butterflies per stage
+    for (int h = 1; h < kHeadDim; h <<= 1) {
+        for (int idx = threadIdx.x; idx < nb; idx += blockDim.x) {
+            const int tok = idx >> 6, pr = idx & 63;
+            const int i = (pr / h) * 2 * h + (pr % h);
+            double* r = x + tok * kHeadDim;
+            const double a = r[i], b = r[i + h];
+            r[i] = a + b;
+            r[i + h] = a - b;
+        }
+        __syncthreads();
+    }
+    for (int idx = threadIdx.x; idx < ntok * kHeadDim; idx += blockDim.x) x[idx] = x[idx] * kInvSqrtHeadDimD;
+    __syncthreads();
+}
+
+// Squared L2 distance, fixed left-to-right order.
+template <int DS>
+__device__ __forceinline__ double dist(const double* x, const float* c) {
+    double t = x[0] - (double)c[0];
+    double d = t * t;
+#pragma unroll
+    for (int i = 1; i < DS; ++i) {
+        t = x[i] - (double)c[i];
+        d = d + t * t;
+    }
+    return d;
+}
+
+template <int DS>
+__device__ __forceinline__ double dist_d(const double* x, const double* c) {
+    double t = x[0] - c[0];
+    double d = t * t;
+#pragma unroll
+    for (int i = 1; i < DS; ++i) {
+        t = x[i] - c[i];
+        d = d + t * t;
+    }
+    return d;
+}
+
+// Nearest entry among [e0, e1) of an fp32 book in LDS; strict "<" keeps the lowest index.
+template <int DS>
+__device__ __forceinline__ void argmin_range(const double* x, const float* book, int e0, int e1,
+                                             double& best, int& idx) {
+    best = __builtin_inf();
+    idx = e0;
+    for (int e = e0; e < e1; ++e) {
+        const double d = dist<DS>(x, book + e * DS);
+        if (d < best) { best = d; idx = e; }
+    }
+}
+
+// -------------------------------------------------------------- append kernel
+
+template <int FMT> struct AppendTile { static constexpr int TT = FMT == 0 ? 32 : 16; };
+
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
+    using F = Fmt<FMT>;
+    constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
+    constexpr int TT = AppendTile<FMT>::TT;
+    __shared__ float book[E * DS];              // one codebook at a time (K, then V)
+    __shared__ double xk[TT * kHeadDim];        // transformed keys of the tile
+    __shared__ uint16_t codes[2][TT * J];
+    __shared__ double red_d[256];
+    __shared__ int red_i[256];
+
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int tile_base = (a.start_pos / TT + blockIdx.x) * TT;
+    const int lo = max(tile_base, a.start_pos);
+    const int hi = min(tile_base + TT, a.start_pos + a.n_new);
+    const int off = lo - tile_base;             // first valid row of the tile
+    const int nt = hi - lo;                     // >= 1
+    const int64_t stream = (int64_t)b * a.hkv + h;
+    const int64_t row0 = stream * a.n_new + (lo - a.start_pos);   // input row of position lo
+
+    // Keys: x = k / s, into LDS rows [off, off + nt).
+    const float* s = a.smooth + (int64_t)h * kHeadDim;
+    for (int idx = threadIdx.x; idx < nt * kHeadDim; idx += blockDim.x) {
+        const int r = idx / kHeadDim, c = idx % kHeadDim;
+        xk[(off + r) * kHeadDim + c] = load_elem_d(a.k_new, (row0 + r) * kHeadDim + c, a.dtype) / (double)s[c];
+    }
+    __syncthreads();
+    block_fwht(xk + off * kHeadDim, nt);
+
+    const int P = nt * J;                       // points per phase
+    int ES = 1;                                 // centroid slices per point
+    while (ES * 2 * P <= 256 && ES * 2 <= E / 16) ES *= 2;
+
+    for (int phase = 0; phase < 2; ++phase) {
+        const uint16_t* src = (phase == 0 ? a.k_book : a.v_book) + (int64_t)h * E * DS;
+        for (int i = threadIdx.x; i < E * DS; i += blockDim.x) book[i] = half_bits_to_float(src[i]);
+        __syncthreads();
+        const int items = P * ES;
+        for (int it = threadIdx.x; it < items; it += blockDim.x) {
+            const int pt = it / ES, sl = it % ES;
+            const int r = pt / J, j = pt % J;
+            double x[DS];
+            if (phase == 0) {
+#pragma unroll
+                for (int i = 0; i < DS; ++i) x[i] = xk[(off + r) * kHeadDim + j * DS + i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < DS; ++i) x[i] = load_elem_d(a.v_new, (row0 + r) * kHeadDim + j * DS + i, a.dtype);
+            }
+            double best;
+            int idx;
+            argmin_range<DS>(x, book, sl * (E / ES), (sl + 1) * (E / ES), best, idx);
+            if (ES == 1) {
+                codes[phase][(off + r) * J + j] = (uint16_t)idx;
+            } else {
+                red_d[it] = best;
+                red_i[it] = idx;
+            }
+        }
+        __syncthreads();
+        if (ES > 1) {
+            for (int pt = threadIdx.x; pt < P; pt += blockDim.x) {
+                double best = red_d[pt * ES];
+                int idx = red_i[pt * ES];
+                for (int sl = 1; sl < ES; ++sl)
+                    if (red_d[pt * ES + sl] < best) { best = red_d[pt * ES + sl]; idx = red_i[pt * ES + sl]; }
+                codes[phase][(off + pt / J) * J + pt % J] = (uint16_t)idx;
+            }
+        }
+        __syncthreads();
+    }
+
+    // Write the codes of positions [lo, hi) in the cache layout.
+    uint8_t* kc = a.k_codes + stream * (int64_t)a.cap * W;
+    uint8_t* vc = a.v_codes + stream * (int64_t)a.cap * W;
+    if (FMT == 0) {
+        for (int idx = threadIdx.x; idx < nt * J; idx += blockDim.x) {
+            const int r = off + idx / J, j = idx % J;
+            const int64_t t = tile_base + r;
+            kc[t * W + j] = (uint8_t)codes[0][r * J + j];
+            vc[(t / 32) * 1024 + j * 32 + (t % 32)] = (uint8_t)codes[1][r * J + j];
+        }
+    } else {
+        // Keys: sub-vectors (2i, 2i+1) of a token share 3 bytes.
+        for (int idx = threadIdx.x; idx < nt * (J / 2); idx += blockDim.x) {
+            const int r = off + idx / (J / 2), i = idx % (J / 2);
+            const int64_t t = tile_base + r;
+            const uint32_t c0 = codes[0][r * J + 2 * i], c1 = codes[0][r * J + 2 * i + 1];
+            uint8_t* p = kc + t * W + 3 * i;
+            p[0] = (uint8_t)(c0 & 0xff);
+            p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
+            p[2] = (uint8_t)(c1 >> 4);
+        }
+        // Values: tokens (2i, 2i+1) of a 16-token block share 3 bytes of row j.
+        // Tiles are aligned to even positions, so both tokens of a pair belong
+        // to this block; a pair with only one token in range keeps the other
+        // token's nibble.
+        const int pr0 = lo / 2, pr1 = (hi - 1) / 2;     // absolute pair indices
+        const int npr = pr1 - pr0 + 1;
+        for (int idx = threadIdx.x; idx < npr * J; idx += blockDim.x) {
+            const int pr = pr0 + idx / J, j = idx % J;
+            const int64_t t0 = 2 * (int64_t)pr;
+            uint8_t* p = vc + (t0 / 16) * 384 + j * 24 + 3 * ((t0 % 16) / 2);
+            const bool has0 = t0 >= lo, has1 = t0 + 1 < hi;
+            if (has0) {
+                const uint32_t c0 = codes[1][(int)(t0 - tile_base) * J + j];
+                p[0] = (uint8_t)(c0 & 0xff);
+                p[1] = has1 ? (uint8_t)((c0 >> 8) | ((codes[1][(int)(t0 + 1 - tile_base) * J + j] & 0xf) << 4))
+                            : (uint8_t)((p[1] & 0xf0) | (c0 >> 8));
+            }
+            if (has1) {
+                const uint32_t c1 = codes[1][(int)(t0 + 1 - tile_base) * J + j];
+                if (!has0) p[1] = (uint8_t)((p[1] & 0x0f) | ((c1 & 0xf) << 4));
+                p[2] = (uint8_t)(c1 >> 4);
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------- smoothing scales
+
+// s[h][c] = fp32 nearest sqrt(max_t |k[h][t][c]|).  The fp64 root is checked
+// against the two fp32 rounding midpoints with exact fp64 squares, so the
+// result is the correctly rounded fp32 root whatever the accuracy of sqrt.
+__global__ __launch_bounds__(128) void smooth_scales_kernel(int n_cal, const void* k_cal, int dtype, float* smooth) {
+    const int h = blockIdx.x, c = threadIdx.x;
+    float m = 0.0f;
+    const int64_t base = (int64_t)h * n_cal * kHeadDim + c;
+    for (int t = 0; t < n_cal; ++t) m = fmaxf(m, fabsf(load_elem(k_cal, base + (int64_t)t * kHeadDim, dtype)));
+    const double md = (double)m;
+    float r = (float)sqrt(md);
+    // Correct to the nearest fp32: midpoints have 25 significant bits, their squares are exact in fp64.
+    for (int it = 0; it < 2; ++it) {
+        const float up = nextafterf(r, __builtin_inff());
+        const double mid_up = 0.5 * ((double)r + (double)up);
+        if (md >= mid_up * mid_up) { r = up; continue; }
+        const float dn = nextafterf(r, 0.0f);
+        const double mid_dn = 0.5 * ((double)r + (double)dn);
+        if (r > 0.0f && md < mid_dn * mid_dn) { r = dn; continue; }
+        break;
+    }
+    smooth[h * kHeadDim + c] = r;
+}
+
+// ------------------------------------------------------------ codebook training
+
+// Points for K-Means: rotated keys or raw values, fp64 [n_cal][128].
+__global__ __launch_bounds__(256) void calib_points_kernel(TrainArgs a) {
+    constexpr int R = 8;                               // rows per block
+    __shared__ double x[R * kHeadDim];
+    const int r0 = blockIdx.x * R;
+    const int nr = min(R, a.n_cal - r0);
+    for (int idx = threadIdx.x; idx < nr * kHeadDim; idx += blockDim.x) {
+        const int r = idx / kHeadDim, c = idx % kHeadDim;
+        const double v = load_elem_d(a.rows, (int64_t)(r0 + r) * kHeadDim + c, a.dtype);
+        x[idx] = a.is_key ? v / (double)a.smooth[c] : v;
+    }
+    __syncthreads();
+    if (a.is_key) block_fwht(x, nr);
+    for (int idx = threadIdx.x; idx < nr * kHeadDim; idx += blockDim.x)
+        a.points[(int64_t)r0 * kHeadDim + idx] = x[idx];
+}
+
+template <int DS>
+__global__ __launch_bounds__(256) void kmeans_init_kernel(const double* pts, int64_t n, const int64_t* init, int E,
+                                                          double* cent) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= E * DS) return;
+    int64_t p = init[i / DS];
+    p = p < 0 ? 0 : (p >= n ? n - 1 : p);
+    cent[i] = pts[p * DS + i % DS];
+}
+
+// Assignment: one point per thread, centroids staged through LDS in chunks;
+// chunks are visited in increasing index order with strict "<".
+template <int DS>
+__global__ __launch_bounds__(256) void kmeans_assign_kernel(const double* pts, int64_t n, const double* cent,
+                                                            int E, int32_t* assign) {
+    constexpr int CH = 8192 / DS;                      // centroids per chunk (64 KB)
+    __shared__ double c[CH * DS];
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    double x[DS];
+    if (p < n) {
+#pragma unroll
+        for (int i = 0; i < DS; ++i) x[i] = pts[p * DS + i];
+    }
+    double best = __builtin_inf();
+    int idx = 0;
+    for (int e0 = 0; e0 < E; e0 += CH) {
+        const int ne = min(CH, E - e0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < ne * DS; i += blockDim.x) c[i] = cent[(int64_t)e0 * DS + i];
+        __syncthreads();
+        if (p < n) {
+            for (int e = 0; e < ne; ++e) {
+                const double d = dist_d<DS>(x, c + e * DS);
+                if (d < best) { best = d; idx = e0 + e; }
+            }
+        }
+    }
+    if (p < n) assign[p] = idx;
+}
+
+// Update: one wave per centroid scans the assignment in point order; lane i < DS
+// keeps the running fp64 sum of dimension i, so every sum is taken in
+// increasing point order.
+template <int DS>
+__global__ __launch_bounds__(256) void kmeans_update_kernel(const double* pts, int64_t n, const int32_t* assign,
+                                                            int E, double* cent) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    double sum = 0.0;
+    int64_t count = 0;
+    for (int64_t base = 0; base < n; base += 64) {
+        const int64_t p = base + lane;
+        const bool hit = p < n && assign[p] == e;
+        uint64_t mask = __ballot(hit);
+        count += __popcll(mask);
+        while (mask) {
+            const int l = __ffsll((unsigned long long)mask) - 1;
+            mask &= mask - 1;
+            if (lane < DS) sum = sum + pts[(base + l) * DS + lane];
+        }
+    }
+    if (count > 0 && lane < DS) cent[(int64_t)e * DS + lane] = sum / (double)count;
+}
+
+// fp64 -> fp16, round to nearest, ties to even; overflow to infinity.
+__device__ uint16_t double_to_half_rne(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint16_t sign = (uint16_t)((u >> 48) & 0x8000);
+    const uint64_t mag = u & 0x7fffffffffffffffull;
+    if (mag > 0x7ff0000000000000ull) return (uint16_t)(sign | 0x7e00);        // NaN
+    const double a = __builtin_bit_cast(double, mag);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);
+    if (a < 0x1p-14) {                                                        // subnormal halves
+        const double q = a * 0x1p24;                                          // exact scaling
+        double n = __builtin_rint(q);                                         // rint: ties to even
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    const int e = (int)((mag >> 52) & 0x7ff) - 1023;                          // a in [2^e, 2^(e+1))
+    const double q = a * __builtin_ldexp(1.0, 10 - e);                        // in [1024, 2048)
+    const double n = __builtin_rint(q);                                       // may reach 2048
+    const uint32_t m = (uint32_t)n;
+    if (m == 2048) return (uint16_t)(sign | ((e + 16) << 10));
+    return (uint16_t)(sign | ((e + 15) << 10) | (m - 1024));
+}
+
+__global__ __launch_bounds__(256) void round_book_kernel(const double* cent, int count, uint16_t* book) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) book[i] = double_to_half_rne(cent[i]);
+}
+
+template <int FMT>
+hipError_t train_codebook(const TrainArgs& a, hipStream_t stream) {
+    using F = Fmt<FMT>;
+    constexpr int E = F::E, DS = F::DS, J = F::J;
+    const int64_t n = (int64_t)a.n_cal * J;
+    hipLaunchKernelGGL(calib_points_kernel, dim3((a.n_cal + 7) / 8), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kmeans_init_kernel<DS>, dim3((E * DS + 255) / 256), dim3(256), 0, stream,
+                       (const double*)a.points, n, a.init, E, a.centroids);
+    const int ablocks = (int)((n + 255) / 256);
+    for (int it = 0; it < a.iters; ++it) {
+        hipLaunchKernelGGL(kmeans_assign_kernel<DS>, dim3(ablocks), dim3(256), 0, stream,
+                           (const double*)a.points, n, (const double*)a.centroids, E, a.assign);
+        hipLaunchKernelGGL(kmeans_update_kernel<DS>, dim3(E / 4), dim3(256), 0, stream,
+                           (const double*)a.points, n, (const int32_t*)a.assign, E, a.centroids);
+    }
+    hipLaunchKernelGGL(round_book_kernel, dim3((E * DS + 255) / 256), dim3(256), 0, stream,
+                       (const double*)a.centroids, E * DS, a.book);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
+    const int TT = a.fmt == 0 ? AppendTile<0>::TT : AppendTile<1>::TT;
+    const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
+    const dim3 grid(last - first + 1, a.hkv, a.batch);
+    if (a.fmt == 0) hipLaunchKernelGGL(quantize_append_kernel<0>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(quantize_append_kernel<1>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_smooth_scales(int hkv, int n_cal, const void* k_cal, int dtype, float* smooth, hipStream_t stream) {
+    hipLaunchKernelGGL(smooth_scales_kernel, dim3(hkv), dim3(128), 0, stream, n_cal, k_cal, dtype, smooth);
+    return hipGetLastError();
+}
+
+hipError_t launch_train_codebook(const TrainArgs& a, hipStream_t stream) {
+    return a.fmt == 0 ? train_codebook<0>(a, stream) : train_codebook<1>(a, stream);
+}
+
+}  // namespace vqkv
