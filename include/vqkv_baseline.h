@@ -1,0 +1,54 @@
+/*
+ * vqkv_baseline.h -- measurement kernels shipped in libvqkv next to the VQ
+ * path.  They are not part of the method; they give the numbers the VQ decode
+ * is compared with.
+ *
+ * The VecInfer pages quote their attention speedups against an unquantized
+ * FP16 KV cache ("VecInfer: ... Outlier-Suppressed Vector Quantization",
+ * research.elamur.ai summary card, "Key points": up to 2.7x on H100 and 2.8x on
+ * A100 for large-batch self-attention, Llama-3.1-8B, 196k tokens, 2-bit).
+ * The same comparison on this GPU needs an unquantized decode written with
+ * the same care; vqkv_baseline_bf16_decode is that kernel.
+ * Conventions (pointers, streams, alignment, errors) as in vqkv.h.
+ */
+#ifndef VQKV_BASELINE_H
+#define VQKV_BASELINE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "vqkv.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Split-context decode attention over a bf16 cache, same work split and
+ * workspace format as vqkv_decode_attention (merge with vqkv_combine):
+ * for each (b, g) and split, softmax(sm_scale * q.k) v over the split's tokens.
+ *   shape      fmt is ignored; max_tokens is the bf16 cache capacity (multiple
+ *              of 64); Hq / Hkv in {1, 2, 4, 5, 8}
+ *   q          device, bf16 [B][Hq][128] (untransformed query)
+ *   k, v       device, bf16 [B][Hkv][max_tokens][128]
+ *   seq_len    host, 1 <= seq_len <= max_tokens
+ *   num_splits host, 1 <= num_splits <= ceil(seq_len / 64)
+ *   workspace  device, vqkv_workspace_bytes(shape, num_splits) bytes */
+vqkv_status vqkv_baseline_bf16_decode(const vqkv_shape* shape, const void* q, const void* k, const void* v,
+                                      int32_t seq_len, float sm_scale, int32_t num_splits, void* workspace,
+                                      void* stream);
+
+/* Reads `bytes` (rounded down to 16) of device memory once with 16-byte
+ * loads on a grid of `blocks` x 256 threads; XOR-folds into sink[1024]
+ * (device) so the loads cannot be dropped.  Measures achievable HBM read
+ * bandwidth. */
+vqkv_status vqkv_baseline_read_stream(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
+                                      void* stream);
+
+/* Message for the last failed baseline call on the calling thread. */
+const char* vqkv_baseline_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQKV_BASELINE_H */

@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
         "vqkv_smooth_scales": (I32, [I32, I32, P, I32, P, P]),
         "vqkv_train_workspace_bytes": (SZ, [I32, I32]),
         "vqkv_train_codebook": (I32, [I32, I32, P, I32, I32, P, P, I32, P, P, P, P]),
+        "vqkv_baseline_bf16_decode": (I32, [SP, P, P, P, I32, F32, I32, P, P]),
+        "vqkv_baseline_read_stream": (I32, [P, SZ, P, I32, P]),
+        "vqkv_baseline_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -229,3 +232,24 @@ class VQCache:
                          num_splits, workspace)
         combine(self.shape, num_splits, workspace, out)
         return out
+
+
+# ------------------------------------------------------------- measurement only
+
+def baseline_bf16_decode(shape: Shape, q, k, v, seq_len: int, num_splits: int, workspace,
+                         sm_scale: float | None = None) -> None:
+    """Unquantized bf16 decode (same splits and workspace format; merge with combine())."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = lib().vqkv_baseline_bf16_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), seq_len, sm_scale,
+                                         num_splits, _ptr(workspace), _stream(q))
+    if st != 0:
+        raise VqkvError(st, lib().vqkv_baseline_last_error().decode())
+
+
+def baseline_read_stream(buf, sink, blocks: int = 4096) -> None:
+    """Read every byte of `buf` once (HBM read-bandwidth probe)."""
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().vqkv_baseline_read_stream(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(buf))
+    if st != 0:
+        raise VqkvError(st, lib().vqkv_baseline_last_error().decode())

@@ -1,0 +1,122 @@
+// attn_common.h -- online-softmax and split-merge steps shared by the decode kernels.
+#pragma once
+
+#include "device_util.h"
+#include "internal.h"
+
+namespace vqkv {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// Online-softmax update for one tile: sc holds this lane's G scores (log2 units,
+// -inf for masked tokens); returns p and rescales l and acc.
+template <int G, int NACC>
+__device__ __forceinline__ void softmax_tile(float (&sc)[G], float (&m)[G], float (&l)[G],
+                                             float (&acc)[G][NACC], float (&p)[G]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float tm = wave_max(sc[g]);
+        const float mn = fmaxf(m[g], tm);
+        if (mn != m[g]) {                                   // wave-uniform
+            const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
+            l[g] *= alpha;
+#pragma unroll
+            for (int i = 0; i < NACC; ++i) acc[g][i] *= alpha;
+            m[g] = mn;
+        }
+        p[g] = __builtin_amdgcn_exp2f(sc[g] - m[g]);
+        l[g] += p[g];
+    }
+}
+
+// The same update for tiles whose scores rarely raise the running max: a
+// ballot checks whether any lane exceeds it, and only then are the tile
+// maxima reduced across the wave and the state rescaled.  p comes out
+// multiplied by 2^P_LOG2 (the caller's fixed scale for l and acc).
+template <int G, int NACC, int P_LOG2>
+__device__ __forceinline__ void softmax_tile_lazy(float (&sc)[G], float (&m)[G], float (&l)[G],
+                                                  float (&acc)[G][NACC], float (&p)[G]) {
+    bool up = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) up = up || (sc[g] > m[g]);
+    if (__ballot(up)) {                                     // wave-uniform
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mn = fmaxf(m[g], wave_max(sc[g]));
+            if (mn != m[g]) {
+                const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
+                l[g] *= alpha;
+#pragma unroll
+                for (int i = 0; i < NACC; ++i) acc[g][i] *= alpha;
+                m[g] = mn;
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) p[g] = __builtin_amdgcn_exp2f(sc[g] - m[g] + (float)P_LOG2);
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi, a and b holding fp16 pairs; fp32 accumulate.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+// (lo, hi) -> fp16 pair, round to nearest even (one v_cvt_pk_f16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+    const half2_t h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Merge the NW waves' states and write the split's (o, lse).  Every thread of
+// the block calls this.  `scratch` must hold NW * G * (128 + 2) floats and be
+// free for reuse (caller synchronizes before).  Lanes [0, 128 / DS) of each
+// wave hold the wave's (already token-group-reduced) accumulators for dims
+// [lane * DS, lane * DS + DS).
+template <int G, int DS, int NW>
+__device__ __forceinline__ void merge_and_store(float* scratch, const float (&m)[G], const float (&l)[G],
+                                                const float (&acc)[G][DS], const DecodeArgs& a,
+                                                int b, int h, int s, float l_log2_scale = 0.0f) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float* mo = scratch;                                   // [NW][G][128]
+    float* ml = scratch + NW * G * kHeadDim;               // [NW][G][2]
+    if (lane < kHeadDim / DS) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int i = 0; i < DS; ++i) mo[(wave * G + g) * kHeadDim + lane * DS + i] = acc[g][i];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            ml[(wave * G + g) * 2] = m[g];
+            ml[(wave * G + g) * 2 + 1] = l[g];
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += NW * 64) {
+        const int g = idx / kHeadDim, d = idx % kHeadDim;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, ml[(w * G + g) * 2]);
+        float o = 0.0f, lse = kNegInf;
+        if (M != kNegInf) {
+            float L = 0.0f, O = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = ml[(w * G + g) * 2];
+                const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+                L += f * ml[(w * G + g) * 2 + 1];
+                O += f * mo[(w * G + g) * kHeadDim + d];
+            }
+            o = O / L;
+            lse = M + (__builtin_log2f(L) - l_log2_scale);
+        }
+        const int64_t row = ((int64_t)b * a.hq + h * G + g) * a.splits + s;
+        a.part_o[row * kHeadDim + d] = o;
+        if (d == 0) a.part_lse[row] = lse;
+    }
+}
+
+}  // namespace vqkv

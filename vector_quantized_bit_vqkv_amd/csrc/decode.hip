@@ -29,14 +29,13 @@
 //   * gather: the token's centroids are read from the LDS codebook and dotted
 //     with q' (held in LDS, pre-scaled) -- needed for 1.5-bit, where the table
 //     would be 16 x 4096 x G floats.
+#include "attn_common.h"
 #include "device_util.h"
 #include "internal.h"
 
 namespace vqkv {
 
 namespace {
-
-constexpr float kNegInf = -__builtin_inff();
 
 // Bytes of the per-(b, h) code stream per token.
 template <int FMT> struct DFmt;
@@ -57,116 +56,86 @@ __device__ __forceinline__ uint32_t code12_at(const uint32_t (&w)[N], int i) {
     return (i & 1) ? ((b1 >> 4) | (b2 << 4)) : (b0 | ((b1 & 0xfu) << 8));
 }
 
-// Online-softmax update for one tile: sc holds this lane's G scores (log2 units,
-// -inf for masked tokens); returns p and rescales l and acc.
-template <int G, int NACC>
-__device__ __forceinline__ void softmax_tile(float (&sc)[G], float (&m)[G], float (&l)[G],
-                                             float (&acc)[G][NACC], float (&p)[G]) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float tm = wave_max(sc[g]);
-        const float mn = fmaxf(m[g], tm);
-        if (mn != m[g]) {                                   // wave-uniform
-            const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
-            l[g] *= alpha;
-#pragma unroll
-            for (int i = 0; i < NACC; ++i) acc[g][i] *= alpha;
-            m[g] = mn;
-        }
-        p[g] = __builtin_amdgcn_exp2f(sc[g] - m[g]);
-        l[g] += p[g];
-    }
-}
-
-// Merge the NW waves' states and write the split's (o, lse).  Every thread of
-// the block calls this.  `scratch` must hold NW * G * (128 + 2) floats and be
-// free for reuse (caller synchronizes before).  Lanes [0, 128 / DS) of each
-// wave hold the wave's (already token-group-reduced) accumulators for dims
-// [lane * DS, lane * DS + DS).
-template <int G, int DS, int NW>
-__device__ __forceinline__ void merge_and_store(float* scratch, const float (&m)[G], const float (&l)[G],
-                                                const float (&acc)[G][DS], const DecodeArgs& a,
-                                                int b, int h, int s) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float* mo = scratch;                                   // [NW][G][128]
-    float* ml = scratch + NW * G * kHeadDim;               // [NW][G][2]
-    if (lane < kHeadDim / DS) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int i = 0; i < DS; ++i) mo[(wave * G + g) * kHeadDim + lane * DS + i] = acc[g][i];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            ml[(wave * G + g) * 2] = m[g];
-            ml[(wave * G + g) * 2 + 1] = l[g];
-        }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += NW * 64) {
-        const int g = idx / kHeadDim, d = idx % kHeadDim;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, ml[(w * G + g) * 2]);
-        float o = 0.0f, lse = kNegInf;
-        if (M != kNegInf) {
-            float L = 0.0f, O = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float mw = ml[(w * G + g) * 2];
-                const float f = mw == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-                L += f * ml[(w * G + g) * 2 + 1];
-                O += f * mo[(w * G + g) * kHeadDim + d];
-            }
-            o = O / L;
-            lse = M + __builtin_log2f(L);
-        }
-        const int64_t row = ((int64_t)b * a.hq + h * G + g) * a.splits + s;
-        a.part_o[row * kHeadDim + d] = o;
-        if (d == 0) a.part_lse[row] = lse;
-    }
-}
-
 // ------------------------------------------------------------ score-table path
+
+// Score table layout.  Entry (j, e) holds the four heads' fixed-point scores
+// (16 bytes).  Rows are indexed by the code e: half h = j / 16 of the table is
+// [256 codes][16 columns][16 B], so a row is 256 bytes and column j % 16 sits
+// in bank group j % 16.  At step s lane l reads sub-vector j = s ^ (l % 16):
+// the 16 lanes of each 16-byte-read pass then touch 16 different bank groups
+// whatever their codes are (no bank conflicts), and the address is a byte
+// permutation: code -> byte 1, column * 16 -> byte 0, half -> byte 2.
+constexpr int kTabHalfBytes = 256 * 16 * 16;
+
+// b in the lanes whose bit is set in `mask`, a elsewhere.
+__device__ __forceinline__ uint32_t lane_select(uint32_t a, uint32_t b, uint64_t mask) {
+    uint32_t d;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(mask));
+    return d;
+}
+// Value codebook: 8 copies, copy c of entry e at e * 64 + c * 8; lane l uses
+// copy l % 8, which spreads a pass of 32 lanes over all 32 bank pairs.
+constexpr int kVCopies = 8;
 
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
-    constexpr int GP = G == 3 ? 4 : G;                     // table entry width (floats)
-    constexpr int J = 32, E = 256;
-    __shared__ __align__(16) float table[J * E * GP];
-    __shared__ __align__(16) uint2 vbook[E];               // 4 fp16 per entry
-    __shared__ __align__(16) float pbuf[NW][64 * GP];
+    static_assert(G >= 1 && G <= 4, "score table holds four heads");
+    constexpr int E = 256;
+    __shared__ __align__(16) int32_t table[2 * kTabHalfBytes / 4];
+    __shared__ __align__(16) uint2 vrep[E * kVCopies];
+    __shared__ __align__(16) uint32_t pbuf[NW][32 * 4];   // fp16 probability pairs, 4 heads
+    __shared__ float wmax[NW];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t_begin = s * a.chunk;
     const int t_end = min(a.seq_len, t_begin + a.chunk);
 
-    const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * E * 4);
-    for (int i = threadIdx.x; i < E; i += NW * 64) vbook[i] = vb[i];
+    {
+        const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * E * 4);
+        for (int i = threadIdx.x; i < E * kVCopies; i += NW * 64) vrep[i] = vb[i / kVCopies];
+    }
+    // Build the table in fp32, find max |L|, then convert in place to int32
+    // round(L * 2^F) with 2^F * max|L| <= 2^26 (32 entries cannot overflow).
+    float* tablef = (float*)table;
+    float lmax = 0.0f;
     {
         const uint2* kb = (const uint2*)(a.k_book + (int64_t)h * E * 4);
         const float* qp = a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim;
-        for (int idx = threadIdx.x; idx < J * E; idx += NW * 64) {
-            const int j = idx >> 8, e = idx & 255;
+        for (int idx = threadIdx.x; idx < 32 * E; idx += NW * 64) {
+            const int e = idx & 255, j = idx >> 8;
             const uint2 c = kb[e];
             const float c0 = lo_half(c.x), c1 = hi_half(c.x), c2 = lo_half(c.y), c3 = hi_half(c.y);
-            float v[GP];
+            float v[4];
 #pragma unroll
-            for (int g = 0; g < GP; ++g) {
+            for (int g = 0; g < 4; ++g) {
+                v[g] = 0.0f;
                 if (g < G) {
                     const float4 q = *(const float4*)(qp + g * kHeadDim + 4 * j);
                     v[g] = (q.x * c0 + q.y * c1 + q.z * c2 + q.w * c3) * a.qscale;
-                } else {
-                    v[g] = 0.0f;
                 }
+                lmax = fmaxf(lmax, fabsf(v[g]));
             }
-            if constexpr (GP == 4) *(float4*)(table + idx * 4) = make_float4(v[0], v[1], v[2], v[3]);
-            else if constexpr (GP == 2) *(float2*)(table + idx * 2) = make_float2(v[0], v[1]);
-            else table[idx] = v[0];
+            const int off = (j >> 4) * kTabHalfBytes + e * 256 + (j & 15) * 16;
+            *(float4*)((char*)tablef + off) = make_float4(v[0], v[1], v[2], v[3]);
         }
     }
+    lmax = wave_max(lmax);
+    if (lane == 0) wmax[wave] = lmax;
+    __syncthreads();
+    lmax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) lmax = fmaxf(lmax, wmax[w]);
+    int fexp = 26;
+    if (lmax > 0.0f) {
+        int ex;
+        frexpf(lmax, &ex);                                  // lmax < 2^ex
+        fexp = 26 - ex;
+    }
+    const float to_fixed = __builtin_ldexpf(1.0f, fexp);
+    const float from_fixed = __builtin_ldexpf(1.0f, -fexp);
+    for (int i = threadIdx.x; i < 2 * kTabHalfBytes / 4; i += NW * 64)
+        table[i] = (int32_t)__builtin_rintf(tablef[i] * to_fixed);
     __syncthreads();
 
     float m[G], l[G], acc[G][4];
@@ -181,85 +150,108 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
     const uint8_t* kbase = a.k_codes + stream * (int64_t)a.cap * 32;
     const uint8_t* vbase = a.v_codes + stream * (int64_t)a.cap * 32;
     const int jv = lane & 31, half = lane >> 5;
-    float* pw = pbuf[wave];
+    uint32_t* pw = pbuf[wave];
+    // Lane constants of the conflict-free table walk.
+    const uint32_t lam = lane & 15;
+    const uint32_t lam3 = lam & 3;
+    const uint32_t byte_sel = (0u ^ lam3) | ((1u ^ lam3) << 8) | ((2u ^ lam3) << 16) | ((3u ^ lam3) << 24);
+    const uint32_t lx = lam << 4;
+    const uint32_t vslot = (lane & (kVCopies - 1)) * 8;
+    // p is produced as exp2(score - max + 15): the fp16 pairs then stay clear of
+    // the subnormal range down to 2^-29 of the maximum.  l and acc carry the
+    // same 2^15, removed from lse at the end.
+    constexpr int P_LOG2 = 15;
+    constexpr uint32_t kOnes = 0x3c003c00u;                 // (1.0, 1.0) in fp16
+    const char* tab = (const char*)table;
+
+    // Codes of the next tile are loaded while the current one is processed
+    // (two register buffers), hiding HBM latency behind a whole tile of work.
+    uint4 nk0, nk1, nv0, nv1;
+    auto load_tile = [&](int tl) {
+        const uint4* kc = (const uint4*)(kbase + (int64_t)(tl + lane) * 32);
+        nk0 = kc[0];
+        nk1 = kc[1];
+        const uint4* vc = (const uint4*)(vbase + (int64_t)(tl + half * 32) * 32 + jv * 32);
+        nv0 = vc[0];
+        nv1 = vc[1];
+    };
+    if (t_begin + wave * 64 < t_end) load_tile(t_begin + wave * 64);
 
     for (int tile = t_begin + wave * 64; tile < t_end; tile += NW * 64) {
         const int t = tile + lane;
         uint32_t kw[8], vw[8];
+        kw[0] = nk0.x; kw[1] = nk0.y; kw[2] = nk0.z; kw[3] = nk0.w;
+        kw[4] = nk1.x; kw[5] = nk1.y; kw[6] = nk1.z; kw[7] = nk1.w;
+        vw[0] = nv0.x; vw[1] = nv0.y; vw[2] = nv0.z; vw[3] = nv0.w;
+        vw[4] = nv1.x; vw[5] = nv1.y; vw[6] = nv1.z; vw[7] = nv1.w;
+        if (tile + NW * 64 < t_end) load_tile(tile + NW * 64);
+        // Permute the code bytes so that byte s holds sub-vector s ^ lam.
+        uint32_t pk[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pk[w] = __builtin_amdgcn_perm(0u, kw[w], byte_sel);
         {
-            const uint4* kc = (const uint4*)(kbase + (int64_t)t * 32);
-            const uint4 k0 = kc[0], k1 = kc[1];
-            kw[0] = k0.x; kw[1] = k0.y; kw[2] = k0.z; kw[3] = k0.w;
-            kw[4] = k1.x; kw[5] = k1.y; kw[6] = k1.z; kw[7] = k1.w;
-            const uint4* vc = (const uint4*)(vbase + (int64_t)(tile + half * 32) * 32 + jv * 32);
-            const uint4 v0 = vc[0], v1 = vc[1];
-            vw[0] = v0.x; vw[1] = v0.y; vw[2] = v0.z; vw[3] = v0.w;
-            vw[4] = v1.x; vw[5] = v1.y; vw[6] = v1.z; vw[7] = v1.w;
+            // Dword swaps by bits 2 and 3 of the lane index: fixed lane masks,
+            // one v_cndmask per word and stage.
+            uint32_t q[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) q[w] = lane_select(pk[w], pk[w ^ 1], 0xF0F0F0F0F0F0F0F0ull);
+#pragma unroll
+            for (int w = 0; w < 8; ++w) pk[w] = lane_select(q[w], q[w ^ 2], 0xFF00FF00FF00FF00ull);
+        }
+        // Scores, lane = token: 32 table reads, summed two at a time.
+        int32_t si[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < 32; st += 2) {
+            int4 x[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int s2 = st + u;
+                const uint32_t ofs = lx ^ ((uint32_t)((s2 & 15) << 4) | ((uint32_t)(s2 >> 4) << 16));
+                const uint32_t sel = 0x0c020000u | ((4u + (uint32_t)(s2 & 3)) << 8);
+                const uint32_t addr = __builtin_amdgcn_perm(pk[s2 >> 2], ofs, sel);
+                x[u] = *(const int4*)(tab + addr);
+            }
+            si[0] += x[0].x + x[1].x;
+            si[1] += x[0].y + x[1].y;
+            si[2] += x[0].z + x[1].z;
+            si[3] += x[0].w + x[1].w;
         }
         float sc[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) sc[g] = 0.0f;
-        // One dword (four sub-vectors) per step; the code words rotate through
-        // kw[0] so that indexing stays static while the loop is only partly unrolled.
-#pragma unroll 2
-        for (int w = 0; w < 8; ++w) {
-            const uint32_t d = kw[0];
-#pragma unroll
-            for (int i = 0; i < 7; ++i) kw[i] = kw[i + 1];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float* e = table + ((4 * w + k) * E + ((d >> (8 * k)) & 0xffu)) * GP;
-                if constexpr (GP == 4) {
-                    const float4 x = *(const float4*)e;
-                    sc[0] += x.x;
-                    if (G > 1) sc[1 % G] += x.y;
-                    if (G > 2) sc[2 % G] += x.z;
-                    if (G > 3) sc[3 % G] += x.w;
-                } else if constexpr (GP == 2) {
-                    const float2 x = *(const float2*)e;
-                    sc[0] += x.x;
-                    sc[1 % G] += x.y;
-                } else {
-                    sc[0] += e[0];
-                }
-            }
-        }
-        if (t >= t_end) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) sc[g] = kNegInf;
-        }
+        for (int g = 0; g < G; ++g) sc[g] = t < t_end ? (float)si[g] * from_fixed : kNegInf;
         float p[G];
-        softmax_tile<G, 4>(sc, m, l, acc, p);
+        softmax_tile_lazy<G, 4, P_LOG2>(sc, m, l, acc, p);
+        // Even lanes hold (p_t, p_t+1) as fp16; odd lanes the swapped pair, so
+        // summing every lane's pair counts each token twice (halved at the end)
+        // and l uses exactly the rounded weights the values are multiplied by.
+        uint32_t pkp[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int g = 0; g < G; ++g) pw[lane * GP + g] = p[g];
+        for (int g = 0; g < G; ++g) {
+            pkp[g] = pack_half2(p[g], dpp<0xB1>(p[g]));
+            l[g] = dot2(pkp[g], kOnes, l[g]);
+        }
+        if (!(lane & 1)) *(uint4*)(pw + (lane >> 1) * 4) = make_uint4(pkp[0], pkp[1], pkp[2], pkp[3]);
         wave_lds_sync();
-#pragma unroll 2
+        // Values, lane = (sub-vector jv, half): pairs of tokens with fp16 dot2.
+#pragma unroll
         for (int w = 0; w < 8; ++w) {
-            const uint32_t d = vw[0];
 #pragma unroll
-            for (int i = 0; i < 7; ++i) vw[i] = vw[i + 1];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float* pp = pw + (half * 32 + 4 * w + k) * GP;
-                float pv[G];
-                if constexpr (GP == 4) {
-                    const float4 x = *(const float4*)pp;
-                    pv[0] = x.x;
-                    if (G > 1) pv[1 % G] = x.y;
-                    if (G > 2) pv[2 % G] = x.z;
-                    if (G > 3) pv[3 % G] = x.w;
-                } else {
-#pragma unroll
-                    for (int g = 0; g < G; ++g) pv[g] = pp[g];
-                }
-                const uint2 c = vbook[(d >> (8 * k)) & 0xffu];
-                const float x0 = lo_half(c.x), x1 = hi_half(c.x), x2 = lo_half(c.y), x3 = hi_half(c.y);
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t c0 = (vw[w] >> (16 * q)) & 0xffu, c1 = (vw[w] >> (16 * q + 8)) & 0xffu;
+                const uint2 e0 = *(const uint2*)((const char*)vrep + ((c0 << 6) | vslot));
+                const uint2 e1 = *(const uint2*)((const char*)vrep + ((c1 << 6) | vslot));
+                const uint32_t x0 = __builtin_amdgcn_perm(e1.x, e0.x, 0x05040100u);   // (t.d0, t'.d0)
+                const uint32_t x1 = __builtin_amdgcn_perm(e1.x, e0.x, 0x07060302u);   // (t.d1, t'.d1)
+                const uint32_t x2 = __builtin_amdgcn_perm(e1.y, e0.y, 0x05040100u);
+                const uint32_t x3 = __builtin_amdgcn_perm(e1.y, e0.y, 0x07060302u);
+                const uint4 pv4 = *(const uint4*)(pw + (half * 16 + 2 * w + q) * 4);
+                const uint32_t pv[4] = {pv4.x, pv4.y, pv4.z, pv4.w};
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    acc[g][0] += pv[g] * x0;
-                    acc[g][1] += pv[g] * x1;
-                    acc[g][2] += pv[g] * x2;
-                    acc[g][3] += pv[g] * x3;
+                    acc[g][0] = dot2(pv[g], x0, acc[g][0]);
+                    acc[g][1] = dot2(pv[g], x1, acc[g][1]);
+                    acc[g][2] = dot2(pv[g], x2, acc[g][2]);
+                    acc[g][3] = dot2(pv[g], x3, acc[g][3]);
                 }
             }
         }
@@ -268,12 +260,12 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        l[g] = wave_sum(l[g]);
+        l[g] = 0.5f * wave_sum(l[g]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[g][i] += xor_lane(acc[g][i], 32);
     }
     __syncthreads();
-    merge_and_store<G, 4, NW>(table, m, l, acc, a, b, h, s);
+    merge_and_store<G, 4, NW>((float*)table, m, l, acc, a, b, h, s, (float)P_LOG2);
 }
 
 // ------------------------------------------------------------------ gather path

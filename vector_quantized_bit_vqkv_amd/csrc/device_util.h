@@ -58,6 +58,15 @@ __device__ __forceinline__ float wave_sum(float x) {
     return (readlane(x, 0) + readlane(x, 16)) + (readlane(x, 32) + readlane(x, 48));
 }
 
+// Sum over each row of 16 lanes; every lane of the row receives it.
+__device__ __forceinline__ float row_sum16(float x) {
+    x = x + dpp<0xB1>(x);
+    x = x + dpp<0x4E>(x);
+    x = x + dpp<0x141>(x);
+    x = x + dpp<0x140>(x);
+    return x;
+}
+
 // Value of x in lane (this lane ^ mask) for mask in {16, 32}.
 __device__ __forceinline__ float xor_lane(float x, int mask) {
     return __shfl_xor(x, mask, kWave);
