@@ -33,6 +33,35 @@ MALL_BYTES = 256 << 20
 
 _head = {}
 
+# HBM traffic of the decode kernel comes from rocprofv3 counters recorded in
+# this file, valid only while the kernel sources still hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_table_kernel__llama8b_b32_t196k__hbm_traffic.txt")
+KERNEL_SOURCES = ["decode.hip", "attn_common.h", "device_util.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "vector_quantized_bit_vqkv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary, or None."""
+    if workload != "llama8b_b32_t196k" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
 
 def head_start(dev, ms=12.0):
     """Enqueue about `ms` of HBM read-stream work so that the host can queue every
@@ -341,7 +370,7 @@ def main():
                    "format": "2-bit, 256x4 fp16 codebooks, uint8 codes"} if args.workload == "llama8b_b32_t196k"
         else {"workload": args.workload},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args.workload),
                      "kernel": "decode_attention", "per_launch_bytes": head["decode_bytes"],
                      "avg_launch_us": head["decode_us"]},
         "cpu_baseline": cpu,
