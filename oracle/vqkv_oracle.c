@@ -413,7 +413,15 @@ int vqo_unpack_k(int fmt, int64_t T, const uint8_t* in, uint16_t* codes)
 
 static int64_t v_offset(int fmt, int64_t t, int j, int* which)
 {
-    if (fmt == 0) { *which = 0; return (t / 32) * 1024 + j * 32 + (t % 32); }
+    if (fmt == 0) {
+        /* 64-token blocks of 2048 bytes, 64 chunks of 32 bytes.  Chunk
+           16*((j%16)/4) + 4*(u%4) + j%4 (u = t % 64) holds, at byte
+           2*(u/4) + j/16, the code of sub-vector j of token t. */
+        int64_t u = t % 64;
+        int64_t chunk = 16 * ((j % 16) / 4) + 4 * (u % 4) + (j % 4);
+        *which = 0;
+        return (t / 64) * 2048 + 32 * chunk + 2 * (u / 4) + j / 16;
+    }
     int64_t r = t % 16;
     *which = (int)(r & 1);
     return (t / 16) * 384 + j * 24 + 3 * (r / 2);

@@ -286,20 +286,20 @@ def test_decode_single_token_returns_its_value():
         assert np.abs(got[0, g] - v0).max() <= 1e-6 * np.abs(v0).max()
 
 
-@pytest.mark.parametrize("path", ["table", "gather"])
-def test_decode_split_invariance_and_determinism(path):
-    """1 split vs 64 splits, and a rerun.  The gather path weighs values in fp32
-    (agreement to fp32 rounding, 1e-5).  The score-table path rounds each weight
+@pytest.mark.parametrize("fmt,path", [(0, "table"), (0, "gather"), (1, "gather")])
+def test_decode_split_invariance_and_determinism(fmt, path):
+    """1 split vs 64 splits, and a rerun.  The 1.5-bit path weighs values in
+    fp32 (agreement to fp32 rounding, 1e-5).  The 2-bit paths round each weight
     to fp16 (round to nearest, relative error <= 2^-11) against a running
-    maximum that depends on the split, and normalizes by the sum of the same
+    maximum that depends on the split, and normalize by the sum of the same
     rounded weights; two split counts give two independent roundings, so the
     outputs may differ by up to about 2 * 2^-11 of the value range: 1e-3."""
-    say(f"decode splits 1 vs 64, rerun, {path}")
-    q, s, kb, vb, kc, vc, cap = _attn_inputs(0, 1, 32, 8, 4096, 5)
-    a = _gpu_attention(0, q, s, kb, vb, kc, vc, cap, 1, path)
-    b = _gpu_attention(0, q, s, kb, vb, kc, vc, cap, 64, path)
-    c = _gpu_attention(0, q, s, kb, vb, kc, vc, cap, 64, path)
-    assert rel_err(b, a) < (1e-5 if path == "gather" else 1e-3)
+    say(f"decode splits 1 vs 64, rerun, fmt {fmt} {path}")
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, 1, 32, 8, 4096, 5)
+    a = _gpu_attention(fmt, q, s, kb, vb, kc, vc, cap, 1, path)
+    b = _gpu_attention(fmt, q, s, kb, vb, kc, vc, cap, 64, path)
+    c = _gpu_attention(fmt, q, s, kb, vb, kc, vc, cap, 64, path)
+    assert rel_err(b, a) < (1e-5 if fmt == 1 else 1e-3)
     assert np.array_equal(b.view(np.uint32), c.view(np.uint32))
 
 
@@ -310,12 +310,13 @@ def test_decode_ignores_bytes_past_seq_len():
     shape = vq.make_shape(1, 4, 1, cap, 0)
     kbytes, vbytes = oracle.pack_stream(0, kc, vc, cap)
     noise = np.random.default_rng(3).integers(0, 256, kbytes.shape, dtype=np.uint8)
-    kb2, vb2 = noise.copy(), noise.copy()
-    kb2[..., :100 * 32] = kbytes[..., :100 * 32]
-    # value blocks are 32 tokens; the first 100 tokens live in blocks 0..3 (partly)
-    for t in range(100):
-        for j in range(32):
-            vb2[0, 0, (t // 32) * 1024 + j * 32 + t % 32] = vbytes[0, 0, (t // 32) * 1024 + j * 32 + t % 32]
+    # The bytes that hold tokens [0, 100): pack an all-ones code array (unused
+    # bytes stay 0), whatever the layout is.
+    ones = np.ones((1, 1, 100, 32), dtype=np.uint16)
+    kmask, vmask = (m != 0 for m in oracle.pack_stream(0, ones, ones, cap))
+    assert kmask.sum() == vmask.sum() == 100 * 32
+    kb2 = np.where(kmask, kbytes, noise)
+    vb2 = np.where(vmask, vbytes, noise)
     qp = torch.empty((1, 4, D), dtype=torch.float32, device=DEV)
     vq.transform_query(shape, dev(q), dev(s), qp)
     a = run_decode(shape, qp, book_dev(kb), book_dev(vb), dev(kbytes), dev(vbytes), 100, 2)
@@ -420,8 +421,9 @@ def test_full_size_append_one_token():
     torch.cuda.synchronize()
     kc_ref, vc_ref = _oracle_codes(0, case, s, kb, vb)
     gk = kcodes[0, :, (T - 1) * 32:].cpu().numpy()
-    t = T - 1
-    gv = vcodes[0].cpu().numpy()[:, [(t // 32) * 1024 + j * 32 + t % 32 for j in range(32)]]
+    # The value layout is blocked by 64 tokens: unpack the last block alone.
+    last = vcodes[0, :, (T - 64) * 32:].cpu().numpy()
+    gv = np.stack([oracle.unpack_v(0, last[h], 64)[63] for h in range(Hkv)])
     assert np.array_equal(gk, kc_ref[0, :, 0])
     assert np.array_equal(gv, vc_ref[0, :, 0])
 

@@ -415,10 +415,14 @@ def test_pack_2bit_positions():
     vb = oracle.pack_v(0, c, 128)
     for t, j in [(0, 0), (0, 31), (1, 0), (33, 7), (95, 31)]:
         assert kb[t * 32 + j] == c[t, j]
-    assert vb[0 * 32 + 0] == c[0, 0]
-    assert vb[7 * 32 + 1] == c[1, 7]
-    assert vb[1024 + 7 * 32 + 1] == c[33, 7]
-    assert vb[2048 + 31 * 32 + 31] == c[95, 31]
+    # Values: 64-token blocks; (t, j) -> chunk 16*((j%16)//4) + 4*(t%4) + j%4,
+    # byte 2*((t%64)//4) + j//16 of that 32-byte chunk.
+    assert vb[0] == c[0, 0]
+    assert vb[32 * 23 + 0] == c[1, 7]            # chunk 16 + 4 + 3
+    assert vb[32 * 23 + 16] == c[33, 7]          # same chunk, byte 2 * 8
+    assert vb[2048 + 32 * 63 + 15] == c[95, 31]  # block 1, u = 31: chunk 48 + 12 + 3, byte 14 + 1
+    assert vb[2048 + 32 * 24 + 1] == c[66, 20]   # block 1, u = 2: chunk 16 + 8 + 0, byte 0 + 1
+    assert vb[32 * 3 + 1] == c[0, 19]            # chunk 3, byte 1
     assert np.array_equal(oracle.unpack_v(0, vb, T), c)
     assert np.array_equal(oracle.unpack_k(0, kb, T), c)
 

@@ -31,11 +31,12 @@ __device__ __forceinline__ void softmax_tile(float (&sc)[G], float (&m)[G], floa
 
 // The same update for tiles whose scores rarely raise the running max: a
 // ballot checks whether any lane exceeds it, and only then are the tile
-// maxima reduced across the wave and the state rescaled.  p comes out
-// multiplied by 2^P_LOG2 (the caller's fixed scale for l and acc).
-template <int G, int NACC, int P_LOG2>
-__device__ __forceinline__ void softmax_tile_lazy(float (&sc)[G], float (&m)[G], float (&l)[G],
-                                                  float (&acc)[G][NACC], float (&p)[G]) {
+// maxima reduced across the wave and the state rescaled (rescale(g, alpha)
+// multiplies head g's output accumulators by alpha).  p comes out multiplied
+// by 2^P_LOG2 (the caller's fixed scale for l and the accumulators).
+template <int G, int P_LOG2, class Rescale>
+__device__ __forceinline__ void softmax_tile_lazy(float (&sc)[G], float (&m)[G], float (&l)[G], float (&p)[G],
+                                                  Rescale&& rescale) {
     bool up = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) up = up || (sc[g] > m[g]);
@@ -46,8 +47,7 @@ __device__ __forceinline__ void softmax_tile_lazy(float (&sc)[G], float (&m)[G],
             if (mn != m[g]) {
                 const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
                 l[g] *= alpha;
-#pragma unroll
-                for (int i = 0; i < NACC; ++i) acc[g][i] *= alpha;
+                rescale(g, alpha);
                 m[g] = mn;
             }
         }
@@ -69,32 +69,17 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// Merge the NW waves' states and write the split's (o, lse).  Every thread of
-// the block calls this.  `scratch` must hold NW * G * (128 + 2) floats and be
-// free for reuse (caller synchronizes before).  Lanes [0, 128 / DS) of each
-// wave hold the wave's (already token-group-reduced) accumulators for dims
-// [lane * DS, lane * DS + DS).
-template <int G, int DS, int NW>
-__device__ __forceinline__ void merge_and_store(float* scratch, const float (&m)[G], const float (&l)[G],
-                                                const float (&acc)[G][DS], const DecodeArgs& a,
-                                                int b, int h, int s, float l_log2_scale = 0.0f) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float* mo = scratch;                                   // [NW][G][128]
-    float* ml = scratch + NW * G * kHeadDim;               // [NW][G][2]
-    if (lane < kHeadDim / DS) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int i = 0; i < DS; ++i) mo[(wave * G + g) * kHeadDim + lane * DS + i] = acc[g][i];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            ml[(wave * G + g) * 2] = m[g];
-            ml[(wave * G + g) * 2 + 1] = l[g];
-        }
-    }
-    __syncthreads();
+// Merge the NW waves' states and write the split's (o, lse).  `scratch`
+// holds, per wave w and head g, the unnormalized output at
+// scratch[(w * G + g) * 128 + d] and (m, l) at scratch[NW * G * 128 +
+// (w * G + g) * 2 + {0, 1}]; every thread of the block calls this after a
+// barrier.  l_log2_scale is a power-of-two factor carried by l and the
+// outputs (removed from lse).
+template <int G, int NW>
+__device__ __forceinline__ void merge_waves(const float* scratch, const DecodeArgs& a, int b, int h, int s,
+                                            float l_log2_scale) {
+    const float* mo = scratch;
+    const float* ml = scratch + NW * G * kHeadDim;
     for (int idx = threadIdx.x; idx < G * kHeadDim; idx += NW * 64) {
         const int g = idx / kHeadDim, d = idx % kHeadDim;
         float M = kNegInf;
@@ -117,6 +102,40 @@ __device__ __forceinline__ void merge_and_store(float* scratch, const float (&m)
         a.part_o[row * kHeadDim + d] = o;
         if (d == 0) a.part_lse[row] = lse;
     }
+}
+
+// Stash one wave's (m, l) for merge_waves (lane 0 writes).
+template <int G, int NW>
+__device__ __forceinline__ void stash_ml(float* scratch, const float (&m)[G], const float (&l)[G]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float* ml = scratch + NW * G * kHeadDim;
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            ml[(wave * G + g) * 2] = m[g];
+            ml[(wave * G + g) * 2 + 1] = l[g];
+        }
+    }
+}
+
+// Stash and merge for accumulators laid out as lanes [0, 128 / DS) of each
+// wave holding dims [lane * DS, lane * DS + DS) (already token-group reduced).
+// `scratch` must hold NW * G * (128 + 2) floats and be free for reuse (the
+// caller synchronizes before).
+template <int G, int DS, int NW>
+__device__ __forceinline__ void merge_and_store(float* scratch, const float (&m)[G], const float (&l)[G],
+                                                const float (&acc)[G][DS], const DecodeArgs& a,
+                                                int b, int h, int s, float l_log2_scale = 0.0f) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane < kHeadDim / DS) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int i = 0; i < DS; ++i) scratch[(wave * G + g) * kHeadDim + lane * DS + i] = acc[g][i];
+    }
+    stash_ml<G, NW>(scratch, m, l);
+    __syncthreads();
+    merge_waves<G, NW>(scratch, a, b, h, s, l_log2_scale);
 }
 
 }  // namespace vqkv

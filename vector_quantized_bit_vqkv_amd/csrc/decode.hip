@@ -73,6 +73,58 @@ __device__ __forceinline__ uint32_t lane_select(uint32_t a, uint32_t b, uint64_t
     asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(mask));
     return d;
 }
+// ------------------------------------------------------ values on the matrix cores
+//
+// The value product o_g += sum_t p_{g,t} * C_V[vc_{t,j}] of a 64-token tile
+// runs on v_mfma_f32_4x4x4f16: 16 independent 4x4x4 products per wave, block
+// b = lane / 4, A row i in lane 4b + i, B column j in lane 4b + j, result
+// D[i][j] in register i of lane 4b + j.  Per step of 4 tokens and per half of
+// the sub-vectors (16 of them, 64 dims): A = the probabilities (row i = head
+// i, the same in every block) and B of block b = the 4 tokens' dims of
+// sub-vector 16*half + b.  B comes straight from the codebook in LDS through
+// the transposing read ds_read_b64_tr_b16, where lane 16r + i receives
+// element i % 4 of the 8-byte rows addressed by lanes 16r + 4e + i / 4, as
+// its elements e = 0..3.  So lane 16r + 4k + q looks up the centroid of the
+// step's token k for sub-vector 16*half + 4r + q, and block b = 4r + q
+// receives exactly its (token, dim) operand.  Lane L ends up accumulating
+// dims L and 64 + L of every head.  The value-code layout gives each lane one
+// 32-byte chunk per tile: byte 2s + half is its lookup for step s.
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ half4_t lds_read_tr16(const lds_char* p) {
+    return __builtin_bit_cast(half4_t,
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(lds_char*)p));
+}
+
+__device__ __forceinline__ float4_t mfma_4x4x4(half4_t a, half4_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
+}
+
+// Store this lane's fp16 probabilities (scaled, G heads) into the wave's
+// A-operand buffer: step s (tokens 4s..4s+3) takes 8 * HB dwords, head g's
+// four tokens in dwords 2g and 2g + 1.  Even lanes write the pair (t, t+1).
+// l accumulates the same rounded pairs; every lane adds its pair (the odd lane
+// in swapped order), so l counts each token twice.
+template <int G, int HB>
+__device__ __forceinline__ void store_probs(uint32_t* pw, const float (&p)[G], float (&l)[G], int lane) {
+    constexpr uint32_t kOnes = 0x3c003c00u;                 // (1.0, 1.0) in fp16
+    uint32_t pkp[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        pkp[g] = pack_half2(p[g], dpp<0xB1>(p[g]));
+        l[g] = dot2(pkp[g], kOnes, l[g]);
+    }
+    if (!(lane & 1)) {
+        uint32_t* dst = pw + (lane >> 2) * (8 * HB) + ((lane >> 1) & 1);
+#pragma unroll
+        for (int g = 0; g < G; ++g) dst[2 * g] = pkp[g];
+    }
+}
+
 // Value codebook: 8 copies, copy c of entry e at e * 64 + c * 8; lane l uses
 // copy l % 8, which spreads a pass of 32 lanes over all 32 bank pairs.
 constexpr int kVCopies = 8;
@@ -83,7 +135,7 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
     constexpr int E = 256;
     __shared__ __align__(16) int32_t table[2 * kTabHalfBytes / 4];
     __shared__ __align__(16) uint2 vrep[E * kVCopies];
-    __shared__ __align__(16) uint32_t pbuf[NW][32 * 4];   // fp16 probability pairs, 4 heads
+    __shared__ __align__(16) uint32_t pbuf[NW][16 * 8];   // fp16 probabilities, [step][head][4 tokens]
     __shared__ float wmax[NW];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -94,6 +146,8 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
     {
         const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * E * 4);
         for (int i = threadIdx.x; i < E * kVCopies; i += NW * 64) vrep[i] = vb[i / kVCopies];
+        // Rows of heads >= G stay zero (their products are computed and dropped).
+        for (int i = threadIdx.x; i < NW * 16 * 8; i += NW * 64) (&pbuf[0][0])[i] = 0u;
     }
     // Build the table in fp32, find max |L|, then convert in place to int32
     // round(L * 2^F) with 2^F * max|L| <= 2^26 (32 entries cannot overflow).
@@ -138,19 +192,19 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
         table[i] = (int32_t)__builtin_rintf(tablef[i] * to_fixed);
     __syncthreads();
 
-    float m[G], l[G], acc[G][4];
+    float m[G], l[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = kNegInf;
         l[g] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
     }
+    float4_t o[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
     const int64_t stream = (int64_t)b * a.hkv + h;
     const uint8_t* kbase = a.k_codes + stream * (int64_t)a.cap * 32;
     const uint8_t* vbase = a.v_codes + stream * (int64_t)a.cap * 32;
-    const int jv = lane & 31, half = lane >> 5;
     uint32_t* pw = pbuf[wave];
+    const char* pa_base = (const char*)pw + (lane & 3) * 8;
+    const lds_char* vt = (const lds_char*)vrep;
     // Lane constants of the conflict-free table walk.
     const uint32_t lam = lane & 15;
     const uint32_t lam3 = lam & 3;
@@ -161,30 +215,29 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
     // the subnormal range down to 2^-29 of the maximum.  l and acc carry the
     // same 2^15, removed from lse at the end.
     constexpr int P_LOG2 = 15;
-    constexpr uint32_t kOnes = 0x3c003c00u;                 // (1.0, 1.0) in fp16
     const char* tab = (const char*)table;
 
-    // Codes of the next tile are loaded while the current one is processed
-    // (two register buffers), hiding HBM latency behind a whole tile of work.
-    uint4 nk0, nk1, nv0, nv1;
-    auto load_tile = [&](int tl) {
-        const uint4* kc = (const uint4*)(kbase + (int64_t)(tl + lane) * 32);
-        nk0 = kc[0];
-        nk1 = kc[1];
-        const uint4* vc = (const uint4*)(vbase + (int64_t)(tl + half * 32) * 32 + jv * 32);
-        nv0 = vc[0];
-        nv1 = vc[1];
-    };
-    if (t_begin + wave * 64 < t_end) load_tile(t_begin + wave * 64);
+    // Each code register is reloaded with the next tile's codes right after its
+    // last use in this tile: key codes once they are permuted (a whole tile of
+    // work hides the latency), value codes one 16-byte half at a time during
+    // the value phase.  No second buffer and no copies; the next tile index is
+    // clamped to a valid tile so the loads are unconditional and in bounds.
+    constexpr int kStride = NW * 64;
+    const int first = t_begin + wave * 64;
+    const uint4* kc0 = (const uint4*)(kbase + (int64_t)lane * 32);
+    const uint4* vc0 = (const uint4*)(vbase + (int64_t)lane * 32);
+    uint4 ck0, ck1, cv0, cv1;
+    if (first < t_end) {
+        ck0 = kc0[(int64_t)first * 2];
+        ck1 = kc0[(int64_t)first * 2 + 1];
+        cv0 = vc0[(int64_t)first * 2];
+        cv1 = vc0[(int64_t)first * 2 + 1];
+    }
 
-    for (int tile = t_begin + wave * 64; tile < t_end; tile += NW * 64) {
+    for (int tile = first; tile < t_end; tile += kStride) {
         const int t = tile + lane;
-        uint32_t kw[8], vw[8];
-        kw[0] = nk0.x; kw[1] = nk0.y; kw[2] = nk0.z; kw[3] = nk0.w;
-        kw[4] = nk1.x; kw[5] = nk1.y; kw[6] = nk1.z; kw[7] = nk1.w;
-        vw[0] = nv0.x; vw[1] = nv0.y; vw[2] = nv0.z; vw[3] = nv0.w;
-        vw[4] = nv1.x; vw[5] = nv1.y; vw[6] = nv1.z; vw[7] = nv1.w;
-        if (tile + NW * 64 < t_end) load_tile(tile + NW * 64);
+        const int nxt = tile + kStride < t_end ? tile + kStride : tile;
+        uint32_t kw[8] = {ck0.x, ck0.y, ck0.z, ck0.w, ck1.x, ck1.y, ck1.z, ck1.w};
         // Permute the code bytes so that byte s holds sub-vector s ^ lam.
         uint32_t pk[8];
 #pragma unroll
@@ -198,6 +251,9 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
 #pragma unroll
             for (int w = 0; w < 8; ++w) pk[w] = lane_select(q[w], q[w ^ 2], 0xFF00FF00FF00FF00ull);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        ck0 = kc0[(int64_t)nxt * 2];
+        ck1 = kc0[(int64_t)nxt * 2 + 1];
         // Scores, lane = token: 32 table reads, summed two at a time.
         int32_t si[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -220,52 +276,49 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) sc[g] = t < t_end ? (float)si[g] * from_fixed : kNegInf;
         float p[G];
-        softmax_tile_lazy<G, 4, P_LOG2>(sc, m, l, acc, p);
-        // Even lanes hold (p_t, p_t+1) as fp16; odd lanes the swapped pair, so
-        // summing every lane's pair counts each token twice (halved at the end)
-        // and l uses exactly the rounded weights the values are multiplied by.
-        uint32_t pkp[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            pkp[g] = pack_half2(p[g], dpp<0xB1>(p[g]));
-            l[g] = dot2(pkp[g], kOnes, l[g]);
-        }
-        if (!(lane & 1)) *(uint4*)(pw + (lane >> 1) * 4) = make_uint4(pkp[0], pkp[1], pkp[2], pkp[3]);
+        softmax_tile_lazy<G, P_LOG2>(sc, m, l, p, [&](int g, float alpha) {
+            o[0][g] *= alpha;
+            o[1][g] *= alpha;
+        });
+        store_probs<G, 1>(pw, p, l, lane);
         wave_lds_sync();
-        // Values, lane = (sub-vector jv, half): pairs of tokens with fp16 dot2.
+        // Values on the matrix cores, 8 steps (one 16-byte code half) at a time.
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
+        for (int hv = 0; hv < 2; ++hv) {
+            const uint4 cv = hv == 0 ? cv0 : cv1;
+            const uint32_t vwh[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const uint32_t c0 = (vw[w] >> (16 * q)) & 0xffu, c1 = (vw[w] >> (16 * q + 8)) & 0xffu;
-                const uint2 e0 = *(const uint2*)((const char*)vrep + ((c0 << 6) | vslot));
-                const uint2 e1 = *(const uint2*)((const char*)vrep + ((c1 << 6) | vslot));
-                const uint32_t x0 = __builtin_amdgcn_perm(e1.x, e0.x, 0x05040100u);   // (t.d0, t'.d0)
-                const uint32_t x1 = __builtin_amdgcn_perm(e1.x, e0.x, 0x07060302u);   // (t.d1, t'.d1)
-                const uint32_t x2 = __builtin_amdgcn_perm(e1.y, e0.y, 0x05040100u);
-                const uint32_t x3 = __builtin_amdgcn_perm(e1.y, e0.y, 0x07060302u);
-                const uint4 pv4 = *(const uint4*)(pw + (half * 16 + 2 * w + q) * 4);
-                const uint32_t pv[4] = {pv4.x, pv4.y, pv4.z, pv4.w};
+            for (int w = 0; w < 4; ++w) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    acc[g][0] = dot2(pv[g], x0, acc[g][0]);
-                    acc[g][1] = dot2(pv[g], x1, acc[g][1]);
-                    acc[g][2] = dot2(pv[g], x2, acc[g][2]);
-                    acc[g][3] = dot2(pv[g], x3, acc[g][3]);
+                for (int q = 0; q < 2; ++q) {
+                    const half4_t pa = *(const half4_t*)(pa_base + (8 * hv + 2 * w + q) * 32);
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const uint32_t code = (vwh[w] >> (16 * q + 8 * hh)) & 0xffu;
+                        o[hh] = mfma_4x4x4(pa, lds_read_tr16(vt + ((code << 6) | vslot)), o[hh]);
+                    }
                 }
             }
+            // Issue the reload only after the old codes' last use (no copies).
+            __builtin_amdgcn_sched_barrier(0);
+            if (hv == 0) cv0 = vc0[(int64_t)nxt * 2];
+            else cv1 = vc0[(int64_t)nxt * 2 + 1];
         }
         wave_lds_sync();
     }
 
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] = 0.5f * wave_sum(l[g]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[g][i] += xor_lane(acc[g][i], 32);
-    }
+    for (int g = 0; g < G; ++g) l[g] = 0.5f * wave_sum(l[g]);
     __syncthreads();
-    merge_and_store<G, 4, NW>((float*)table, m, l, acc, a, b, h, s, (float)P_LOG2);
+    float* scratch = (float*)table;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        scratch[(wave * G + g) * kHeadDim + lane] = o[0][g];
+        scratch[(wave * G + g) * kHeadDim + 64 + lane] = o[1][g];
+    }
+    stash_ml<G, NW>(scratch, m, l);
+    __syncthreads();
+    merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2);
 }
 
 // ------------------------------------------------------------------ gather path
@@ -282,7 +335,11 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
     __shared__ __align__(16) unsigned char region_a[A_BYTES];      // K book, then merge scratch
     __shared__ __align__(16) uint16_t vbook[E * DS];
     __shared__ __align__(16) float qs[G * kHeadDim];
-    __shared__ __align__(16) float pbuf[NW][64 * G];
+    // Probabilities: fp32 [token][head] (1.5-bit), or the fp16 A-operand
+    // buffer of the matrix-core value product (2-bit, HB blocks of 4 heads).
+    constexpr int HB = (G + 3) / 4;
+    constexpr int PB = FMT == 0 ? 16 * 8 * HB : 64 * G;
+    __shared__ __align__(16) float pbuf[NW][PB];
     uint16_t* kbook = (uint16_t*)region_a;
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -299,10 +356,13 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
         }
         const float* qp = a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim;
         for (int i = threadIdx.x; i < G * kHeadDim; i += NW * 64) qs[i] = qp[i] * a.qscale;
+        if (FMT == 0 && G % 4 != 0)                          // padding heads stay zero
+            for (int i = threadIdx.x; i < NW * PB; i += NW * 64) (&pbuf[0][0])[i] = 0.0f;
     }
     __syncthreads();
 
     float m[G], l[G], acc[G][DS];
+    float4_t o[HB][2];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = kNegInf;
@@ -310,6 +370,9 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < DS; ++i) acc[g][i] = 0.0f;
     }
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) o[hb][0] = o[hb][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int P_LOG2 = 15;                               // 2-bit: p and l carry 2^15
     const int64_t stream = (int64_t)b * a.hkv + h;
     const uint8_t* kbase = a.k_codes + stream * (int64_t)a.cap * W;
     const uint8_t* vbase = a.v_codes + stream * (int64_t)a.cap * W;
@@ -325,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
             const uint4 k0 = kc[0], k1 = kc[1];
             kw[0] = k0.x; kw[1] = k0.y; kw[2] = k0.z; kw[3] = k0.w;
             kw[4] = k1.x; kw[5] = k1.y; kw[6] = k1.z; kw[7] = k1.w;
-            const uint4* vc = (const uint4*)(vbase + (int64_t)(tile + grp * 32) * 32 + jv * 32);
+            const uint4* vc = (const uint4*)(vbase + (int64_t)tile * 32 + lane * 32);
             const uint4 v0 = vc[0], v1 = vc[1];
             vw[0] = v0.x; vw[1] = v0.y; vw[2] = v0.z; vw[3] = v0.w;
             vw[4] = v1.x; vw[5] = v1.y; vw[6] = v1.z; vw[7] = v1.w;
@@ -376,54 +439,90 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
             for (int g = 0; g < G; ++g) sc[g] = kNegInf;
         }
         float p[G];
-        softmax_tile<G, DS>(sc, m, l, acc, p);
+        if constexpr (FMT == 0) {
+            softmax_tile_lazy<G, P_LOG2>(sc, m, l, p, [&](int g, float alpha) {
+                o[g >> 2][0][g & 3] *= alpha;
+                o[g >> 2][1][g & 3] *= alpha;
+            });
+            uint32_t* pw32 = (uint32_t*)pw;
+            store_probs<G, HB>(pw32, p, l, lane);
+            wave_lds_sync();
+            const lds_char* vt = (const lds_char*)vbook;
 #pragma unroll
-        for (int g = 0; g < G; ++g) pw[lane * G + g] = p[g];
-        wave_lds_sync();
-        constexpr int VW = TPG * (FMT == 0 ? 1 : 3) / (FMT == 0 ? 1 : 2) / 4;
+            for (int st = 0; st < 16; ++st) {
+                half4_t pa[HB];
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb)
+                    pa[hb] = *(const half4_t*)((const char*)pw32 + st * 32 * HB + (4 * hb + (lane & 3)) * 8);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t code = byte_at(vw, 2 * st + hh);
+                    const half4_t vb = lds_read_tr16(vt + code * 8);
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_4x4x4(pa[hb], vb, o[hb][hh]);
+                }
+            }
+            wave_lds_sync();
+        } else {
+            softmax_tile<G, DS>(sc, m, l, acc, p);
+#pragma unroll
+            for (int g = 0; g < G; ++g) pw[lane * G + g] = p[g];
+            wave_lds_sync();
+            constexpr int VW = TPG * 3 / 2 / 4;
 #pragma unroll 1
-        for (int t0 = 0; t0 < TPG; t0 += SUB) {
-            uint32_t cw[RW];
+            for (int t0 = 0; t0 < TPG; t0 += SUB) {
+                uint32_t cw[RW];
 #pragma unroll
-            for (int i = 0; i < RW; ++i) cw[i] = vw[i];
+                for (int i = 0; i < RW; ++i) cw[i] = vw[i];
 #pragma unroll
-            for (int i = 0; i < VW - RW; ++i) vw[i] = vw[i + RW];
+                for (int i = 0; i < VW - RW; ++i) vw[i] = vw[i + RW];
 #pragma unroll
-          for (int ti = 0; ti < SUB; ++ti) {
-            const int tt = t0 + ti;
-            const float* pp = pw + (grp * TPG + tt) * G;
-            const uint32_t code = FMT == 0 ? byte_at(cw, ti) : code12_at(cw, ti);
-            float c[DS];
-            if constexpr (DS == 4) {
-                const uint2 w = *(const uint2*)(vbook + code * 4);
-                c[0] = lo_half(w.x); c[1] = hi_half(w.x); c[2] = lo_half(w.y); c[3] = hi_half(w.y);
-            } else {
-                const uint4 w = *(const uint4*)(vbook + code * 8);
-                c[0] = lo_half(w.x); c[1] = hi_half(w.x); c[2] = lo_half(w.y); c[3] = hi_half(w.y);
-                c[4] = lo_half(w.z); c[5] = hi_half(w.z); c[6] = lo_half(w.w); c[7] = hi_half(w.w);
+                for (int ti = 0; ti < SUB; ++ti) {
+                    const int tt = t0 + ti;
+                    const float* pp = pw + (grp * TPG + tt) * G;
+                    const uint32_t code = code12_at(cw, ti);
+                    const uint4 w = *(const uint4*)(vbook + code * 8);
+                    float c[8];
+                    c[0] = lo_half(w.x); c[1] = hi_half(w.x); c[2] = lo_half(w.y); c[3] = hi_half(w.y);
+                    c[4] = lo_half(w.z); c[5] = hi_half(w.z); c[6] = lo_half(w.w); c[7] = hi_half(w.w);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float pv = pp[g];
+#pragma unroll
+                        for (int i = 0; i < DS; ++i) acc[g][i] += pv * c[i];
+                    }
+                }
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float pv = pp[g];
-#pragma unroll
-                for (int i = 0; i < DS; ++i) acc[g][i] += pv * c[i];
-            }
-          }
+            wave_lds_sync();
         }
-        wave_lds_sync();
     }
 
+    if constexpr (FMT == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] = wave_sum(l[g]);
+        for (int g = 0; g < G; ++g) l[g] = 0.5f * wave_sum(l[g]);
+        __syncthreads();
+        float* scratch = (float*)region_a;
 #pragma unroll
-        for (int i = 0; i < DS; ++i) {
-            if (NG >= 4) acc[g][i] += xor_lane(acc[g][i], 16);
-            acc[g][i] += xor_lane(acc[g][i], 32);
+        for (int g = 0; g < G; ++g) {
+            scratch[(wave * G + g) * kHeadDim + lane] = o[g >> 2][0][g & 3];
+            scratch[(wave * G + g) * kHeadDim + 64 + lane] = o[g >> 2][1][g & 3];
         }
+        stash_ml<G, NW>(scratch, m, l);
+        __syncthreads();
+        merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2);
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            l[g] = wave_sum(l[g]);
+#pragma unroll
+            for (int i = 0; i < DS; ++i) {
+                if (NG >= 4) acc[g][i] += xor_lane(acc[g][i], 16);
+                acc[g][i] += xor_lane(acc[g][i], 32);
+            }
+        }
+        __syncthreads();
+        merge_and_store<G, DS, NW>((float*)region_a, m, l, acc, a, b, h, s);
     }
-    __syncthreads();
-    merge_and_store<G, DS, NW>((float*)region_a, m, l, acc, a, b, h, s);
 }
 
 // ----------------------------------------------------------------------- combine

@@ -72,11 +72,14 @@ __device__ __forceinline__ float xor_lane(float x, int mask) {
     return __shfl_xor(x, mask, kWave);
 }
 
-// Compiler-and-LDS ordering point between a wave's own LDS writes and reads.
+// Ordering point between a wave's own LDS writes and its later LDS reads of
+// the same data.  A wavefront's LDS instructions execute in order, so the
+// hardware needs no wait; this only stops the compiler from moving memory
+// operations across it.  (A fence would also wait for every outstanding
+// global load, including prefetches.)
 __device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace vqkv

@@ -6,6 +6,18 @@
 
 namespace vqkv {
 
+// Byte offset of the value code of (token t, sub-vector j) in a 2-bit stream.
+// Blocks of 64 tokens x 32 sub-vectors = 2048 bytes, cut into 64 chunks of 32
+// bytes, chunk c being what lane c of the decode wave reads for the block:
+// chunk 16*((j%16)/4) + 4*(t%4) + j%4, byte 2*((t%64)/4) + j/16.  In that
+// order a lane's bytes are exactly the centroids it looks up for the value
+// product, step by step (see the decode kernel).
+__host__ __device__ __forceinline__ int64_t v_code_offset_2bit(int64_t t, int j) {
+    const int u = (int)(t & 63);
+    const int chunk = 16 * ((j & 15) >> 2) + 4 * (u & 3) + (j & 3);
+    return (t >> 6) * 2048 + 32 * chunk + 2 * (u >> 2) + (j >> 4);
+}
+
 struct TransformQueryArgs {
     const void* q;          // [B][Hq][128], bf16 or fp32
     int dtype;              // 0 bf16, 1 fp32

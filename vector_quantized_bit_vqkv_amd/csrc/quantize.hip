@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
             const int r = off + idx / J, j = idx % J;
             const int64_t t = tile_base + r;
             kc[t * W + j] = (uint8_t)codes[0][r * J + j];
-            vc[(t / 32) * 1024 + j * 32 + (t % 32)] = (uint8_t)codes[1][r * J + j];
+            vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[1][r * J + j];
         }
     } else {
         // Keys: sub-vectors (2i, 2i+1) of a token share 3 bytes.
