@@ -40,10 +40,12 @@
  *   12-bit codes of sub-vectors 2i and 2i+1 (dims 8*2i.. and 8*(2i+1)..) share
  *   bytes 3i..3i+2 as b0 = c0 & 0xFF, b1 = (c0 >> 8) | ((c1 & 0xF) << 4),
  *   b2 = c1 >> 4.
- * - Value codes, blocked by sub-vector so that one lane reads one sub-vector
- *   of many tokens with wide loads.  2-bit: blocks of 32 tokens, 1024 bytes
- *   each; in a block, the 32 bytes at offset 32*j hold the codes of
- *   sub-vector j for the block's tokens in order.  1.5-bit: blocks of 16
+ * - Value codes, blocked by tokens and arranged so that every lane of the
+ *   decode kernel reads its codes for a block with one wide load.  2-bit:
+ *   blocks of 64 tokens, 2048 bytes each, cut into 64 chunks of 32 bytes;
+ *   the code of token t (u = t % 64) and sub-vector j sits in chunk
+ *   16*((j%16)/4) + 4*(u%4) + j%4, at byte 2*(u/4) + j/16 of the chunk.
+ *   1.5-bit: blocks of 16
  *   tokens, 384 bytes each; the 24 bytes at offset 24*j hold the 16 codes of
  *   sub-vector j, tokens (2i, 2i+1) of the block packed in bytes 3i..3i+2 by
  *   the 12-bit rule above.
