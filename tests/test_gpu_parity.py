@@ -256,8 +256,16 @@ ATTN_CASES = [
     (0, 1, 6, 2, 1000, 3, "table"),
     (0, 2, 12, 4, 4099, 9, "table"),
     (0, 2, 12, 4, 4099, 9, "gather"),
-    (0, 1, 16, 2, 333, 2, None),           # G = 8: gather
-    (0, 1, 10, 2, 129, 3, None),           # G = 5: gather
+    (0, 1, 16, 2, 333, 2, "gather"),       # G = 8
+    (0, 1, 10, 2, 129, 3, "gather"),       # G = 5
+    (0, 1, 4, 1, 2048, 1, "mfma"),
+    (0, 1, 4, 1, 2048, 32, "mfma"),
+    (0, 1, 8, 8, 777, 5, "mfma"),          # G = 1
+    (0, 1, 6, 2, 1000, 3, "mfma"),         # G = 3
+    (0, 2, 12, 4, 4099, 9, "mfma"),
+    (0, 1, 16, 2, 333, 2, "mfma"),         # G = 8: two head blocks
+    (0, 1, 10, 2, 129, 3, "mfma"),         # G = 5
+    (0, 2, 32, 8, 1, 1, "mfma"),
     (1, 1, 40, 8, 1000, 4, None),
     (1, 2, 5, 1, 64, 1, None),
     (1, 1, 8, 1, 129, 3, None),
@@ -286,7 +294,7 @@ def test_decode_single_token_returns_its_value():
         assert np.abs(got[0, g] - v0).max() <= 1e-6 * np.abs(v0).max()
 
 
-@pytest.mark.parametrize("fmt,path", [(0, "table"), (0, "gather"), (1, "gather")])
+@pytest.mark.parametrize("fmt,path", [(0, "table"), (0, "gather"), (0, "mfma"), (1, "gather")])
 def test_decode_split_invariance_and_determinism(fmt, path):
     """1 split vs 64 splits, and a rerun.  The 1.5-bit path weighs values in
     fp32 (agreement to fp32 rounding, 1e-5).  The 2-bit paths round each weight

@@ -32,10 +32,10 @@ __device__ __forceinline__ void softmax_tile(float (&sc)[G], float (&m)[G], floa
 // The same update for tiles whose scores rarely raise the running max: a
 // ballot checks whether any lane exceeds it, and only then are the tile
 // maxima reduced across the wave and the state rescaled (rescale(g, alpha)
-// multiplies head g's output accumulators by alpha).  p comes out multiplied
-// by 2^P_LOG2 (the caller's fixed scale for l and the accumulators).
+// multiplies head g's sum l and output accumulators by alpha).  p comes out
+// multiplied by 2^P_LOG2 (the caller's fixed scale for l and the accumulators).
 template <int G, int P_LOG2, class Rescale>
-__device__ __forceinline__ void softmax_tile_lazy(float (&sc)[G], float (&m)[G], float (&l)[G], float (&p)[G],
+__device__ __forceinline__ void softmax_tile_lazy(float (&sc)[G], float (&m)[G], float (&p)[G],
                                                   Rescale&& rescale) {
     bool up = false;
 #pragma unroll
@@ -45,9 +45,7 @@ __device__ __forceinline__ void softmax_tile_lazy(float (&sc)[G], float (&m)[G],
         for (int g = 0; g < G; ++g) {
             const float mn = fmaxf(m[g], wave_max(sc[g]));
             if (mn != m[g]) {
-                const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
-                l[g] *= alpha;
-                rescale(g, alpha);
+                rescale(g, __builtin_amdgcn_exp2f(m[g] - mn));
                 m[g] = mn;
             }
         }

@@ -89,12 +89,13 @@ int split_chunk(int seq_len, int splits) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Decode path override for measurement: VQKV_DECODE_PATH = "table" | "gather".
+// Decode path override for measurement: VQKV_DECODE_PATH = "table" | "gather" | "mfma".
 int decode_path_from_env() {
     const char* v = getenv("VQKV_DECODE_PATH");
     if (!v || !*v) return 0;
     if (!strcmp(v, "table")) return 1;
     if (!strcmp(v, "gather")) return 2;
+    if (!strcmp(v, "mfma")) return 3;
     return 0;
 }
 

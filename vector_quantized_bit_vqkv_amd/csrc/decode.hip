@@ -276,7 +276,8 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) sc[g] = t < t_end ? (float)si[g] * from_fixed : kNegInf;
         float p[G];
-        softmax_tile_lazy<G, P_LOG2>(sc, m, l, p, [&](int g, float alpha) {
+        softmax_tile_lazy<G, P_LOG2>(sc, m, p, [&](int g, float alpha) {
+            l[g] *= alpha;
             o[0][g] *= alpha;
             o[1][g] *= alpha;
         });
@@ -315,6 +316,222 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
     for (int g = 0; g < G; ++g) {
         scratch[(wave * G + g) * kHeadDim + lane] = o[0][g];
         scratch[(wave * G + g) * kHeadDim + 64 + lane] = o[1][g];
+    }
+    stash_ml<G, NW>(scratch, m, l);
+    __syncthreads();
+    merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2);
+}
+
+// --------------------------------------------------------- matrix-core path (2-bit)
+//
+// Scores and values both on v_mfma_f32_4x4x4f16.  Scores, lane = token: block
+// b holds tokens 4b..4b+3 (B = their centroids of one sub-vector, one plain
+// 8-byte LDS read per lane) and A = the query dims of that sub-vector (row i =
+// head i).  The A operands of all 32 sub-vectors live in two register pairs:
+// with CBSZ = 4 the instruction broadcasts block ABID's A to all 16 blocks,
+// so lane 4c + i keeps head i's dims of sub-vectors c and 16 + c.  The query
+// enters as fp16 (round to nearest; relative error 2^-11, finer than the bf16
+// query it comes from); products are exact and sums fp32.  The result lands
+// as lane = token, register = head, the layout the online softmax works in.  The probabilities are then
+// turned to lane 4s + i = head i's tokens 4s..4s+3 (one 8-byte LDS write and
+// one transposing read) and broadcast as the A operand of step s of the value
+// product described above.
+//
+// Codebooks sit at a 256-byte stride per code: 32 copies of each 8-byte
+// centroid, lane l reading copy l % 32, so the 32 lanes of an LDS pass hit 32
+// distinct bank pairs whatever their codes.  A lookup address is then one byte
+// permutation: copy * 8 in byte 0, the code in byte 1, the book in byte 2.
+constexpr int kBookStride = 256;
+constexpr int kBookBytes = 256 * kBookStride;
+
+template <int V> struct IntC { static constexpr int value = V; };
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+template <int ABID>
+__device__ __forceinline__ float4_t mfma_bcast(half4_t a, half4_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, ABID, 0);
+}
+
+// Selector of v_perm_b32(word, ofs, sel): byte 0 and 2 from ofs, byte 1 =
+// byte k of word, byte 3 = 0.
+template <int K>
+constexpr uint32_t lookup_sel() { return 0x0c020000u | ((4u + K) << 8); }
+
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+    constexpr int HB = (G + 3) / 4;
+    constexpr int PT_BYTES = NW * HB * 512;
+    constexpr int MERGE_BYTES = NW * G * (kHeadDim + 2) * 4;
+    constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES;
+    constexpr int SMEM = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
+    __shared__ __align__(16) unsigned char smem[SMEM];
+
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t_begin = s * a.chunk;
+    const int t_end = min(a.seq_len, t_begin + a.chunk);
+
+    {
+        const uint2* kb = (const uint2*)(a.k_book + (int64_t)h * 256 * 4);
+        const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * 256 * 4);
+        for (int i = threadIdx.x; i < 256 * 32; i += NW * 64) {
+            ((uint2*)smem)[i] = kb[i >> 5];
+            ((uint2*)(smem + kBookBytes))[i] = vb[i >> 5];
+        }
+    }
+    // Query operands: lane 4c + i holds head 4hb + i's dims of sub-vector
+    // 16r + c, times sm_scale * log2(e), rounded to fp16.
+    half4_t qa[HB][2];
+    {
+        const float* qp = a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim;
+        const int c = lane >> 2, i = lane & 3;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int g = 4 * hb + i;
+                float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (g < G) q = *(const float4*)(qp + g * kHeadDim + 4 * (16 * r + c));
+                qa[hb][r] = half4_t{(_Float16)(q.x * a.qscale), (_Float16)(q.y * a.qscale),
+                                    (_Float16)(q.z * a.qscale), (_Float16)(q.w * a.qscale)};
+            }
+    }
+    __syncthreads();
+
+    float m[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = kNegInf;
+    float lsum[HB];                                         // head 4hb + lane % 4
+    float4_t o[HB][2];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        lsum[hb] = 0.0f;
+        o[hb][0] = o[hb][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int64_t stream = (int64_t)b * a.hkv + h;
+    const uint8_t* kbase = a.k_codes + stream * (int64_t)a.cap * 32;
+    const uint8_t* vbase = a.v_codes + stream * (int64_t)a.cap * 32;
+    const uint32_t kofs = (uint32_t)(lane & 31) * 8;
+    const uint32_t vofs = kofs | (1u << 16);                // the value book starts at 64 KB
+    unsigned char* pt = smem + 2 * kBookBytes + wave * (HB * 512);
+    const int row_w = lane * 8;
+    const int row_r = ((lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3)) * 8;
+    constexpr int P_LOG2 = 15;
+    constexpr uint32_t kOnes = 0x3c003c00u;
+
+    // Each code register is reloaded with the next tile's codes right after
+    // its last use (a whole phase of work hides the load); the next tile
+    // index is clamped to a valid tile so the loads stay in bounds.
+    constexpr int kStride = NW * 64;
+    const int first = t_begin + wave * 64;
+    const uint4* kc0 = (const uint4*)(kbase + (int64_t)lane * 32);
+    const uint4* vc0 = (const uint4*)(vbase + (int64_t)lane * 32);
+    uint4 ck0, ck1, cv0, cv1;
+    if (first < t_end) {
+        ck0 = kc0[(int64_t)first * 2];
+        ck1 = kc0[(int64_t)first * 2 + 1];
+        cv0 = vc0[(int64_t)first * 2];
+        cv1 = vc0[(int64_t)first * 2 + 1];
+    }
+
+    for (int tile = first; tile < t_end; tile += kStride) {
+        const int t = tile + lane;
+        const int nxt = tile + kStride < t_end ? tile + kStride : tile;
+        // Scores: 32 sub-vectors, 16 per code half.
+        float4_t sacc[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) sacc[hb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint4 ck = half == 0 ? ck0 : ck1;
+            const uint32_t kw[4] = {ck.x, ck.y, ck.z, ck.w};
+            static_for<0, 16>([&](auto jc) {
+                constexpr int jj = decltype(jc)::value;     // sub-vector 16 * half + jj
+                const uint32_t addr = __builtin_amdgcn_perm(kw[jj >> 2], kofs, lookup_sel<jj & 3>());
+                const half4_t kv = *(const half4_t*)(smem + addr);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) sacc[hb] = mfma_bcast<jj>(qa[hb][half], kv, sacc[hb]);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            if (half == 0) ck0 = kc0[(int64_t)nxt * 2];
+            else ck1 = kc0[(int64_t)nxt * 2 + 1];
+        }
+        float sc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[g] = t < t_end ? sacc[g >> 2][g & 3] : kNegInf;
+        float p[G];
+        softmax_tile_lazy<G, P_LOG2>(sc, m, p, [&](int g, float alpha) {
+            o[g >> 2][0][g & 3] *= alpha;
+            o[g >> 2][1][g & 3] *= alpha;
+            if ((lane & 3) == (g & 3)) lsum[g >> 2] *= alpha;
+        });
+        // Probabilities to lane 4s + i = head i, tokens 4s..4s+3.
+        half4_t pt_op[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            half4_t v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = 4 * hb + i < G ? (_Float16)p[4 * hb + i] : (_Float16)0.0f;
+            *(half4_t*)(pt + hb * 512 + row_w) = v;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            pt_op[hb] = lds_read_tr16((const lds_char*)(pt + hb * 512 + row_r));
+            const uint2 pw = __builtin_bit_cast(uint2, pt_op[hb]);
+            lsum[hb] = dot2(pw.x, kOnes, dot2(pw.y, kOnes, lsum[hb]));
+        }
+        // Values: step st takes byte 2 st + half of the lane's code chunk.
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+            const uint4 cv = hv == 0 ? cv0 : cv1;
+            const uint32_t vw[4] = {cv.x, cv.y, cv.z, cv.w};
+            static_for<0, 8>([&](auto sc8) {
+                constexpr int st8 = decltype(sc8)::value;   // step 8 * hv + st8
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t sel = hh == 0 ? lookup_sel<2 * (st8 & 1)>() : lookup_sel<2 * (st8 & 1) + 1>();
+                    const uint32_t addr = __builtin_amdgcn_perm(vw[st8 >> 1], vofs, sel);
+                    const half4_t vv = lds_read_tr16((const lds_char*)(smem + addr));
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) {
+                        if (hv == 0) o[hb][hh] = mfma_bcast<st8>(pt_op[hb], vv, o[hb][hh]);
+                        else o[hb][hh] = mfma_bcast<8 + st8>(pt_op[hb], vv, o[hb][hh]);
+                    }
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            if (hv == 0) cv0 = vc0[(int64_t)nxt * 2];
+            else cv1 = vc0[(int64_t)nxt * 2 + 1];
+        }
+        wave_lds_sync();
+    }
+
+    float l[G];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        float x = lsum[hb];
+        x += xor_lane(x, 4);
+        x += xor_lane(x, 8);
+        x += xor_lane(x, 16);
+        x += xor_lane(x, 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * hb + i < G) l[4 * hb + i] = readlane(x, i);
+    }
+    __syncthreads();
+    float* scratch = (float*)smem;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        scratch[(wave * G + g) * kHeadDim + lane] = o[g >> 2][0][g & 3];
+        scratch[(wave * G + g) * kHeadDim + 64 + lane] = o[g >> 2][1][g & 3];
     }
     stash_ml<G, NW>(scratch, m, l);
     __syncthreads();
@@ -440,7 +657,8 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
         }
         float p[G];
         if constexpr (FMT == 0) {
-            softmax_tile_lazy<G, P_LOG2>(sc, m, l, p, [&](int g, float alpha) {
+            softmax_tile_lazy<G, P_LOG2>(sc, m, p, [&](int g, float alpha) {
+                l[g] *= alpha;
                 o[g >> 2][0][g & 3] *= alpha;
                 o[g >> 2][1][g & 3] *= alpha;
             });
@@ -563,10 +781,9 @@ hipError_t launch_gather(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid(a.splits, a.hkv, a.batch);
     const int G = a.hq / a.hkv;
-    const bool table_ok = a.fmt == 0 && G <= 4;
-    const bool use_table = table_ok && a.path != 2;
-    if (a.path == 1 && !table_ok) return hipErrorInvalidValue;
-    if (use_table) {
+    // 2-bit: the matrix-core kernel unless a measurement override asks for
+    // the score-table (G <= 4) or gather kernel.  1.5-bit: gather.
+    if (a.fmt == 0 && a.path == 1) {
         constexpr int NW = 16;
         switch (G) {
             case 1: hipLaunchKernelGGL((decode_table_kernel<1, NW>), grid, dim3(NW * 64), 0, stream, a); break;
@@ -577,6 +794,17 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         }
         return hipGetLastError();
     }
+    if (a.fmt == 0 && a.path != 2) {
+        constexpr int NW = 16;
+        switch (G) {
+#define VQKV_G(GV) case GV: hipLaunchKernelGGL((decode_mfma_kernel<GV, NW>), grid, dim3(NW * 64), 0, stream, a); break;
+            VQKV_G(1) VQKV_G(2) VQKV_G(3) VQKV_G(4) VQKV_G(5) VQKV_G(6) VQKV_G(7) VQKV_G(8)
+#undef VQKV_G
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    if (a.path == 1) return hipErrorInvalidValue;
     if (a.fmt == 0) return launch_gather<0, 8>(a, grid, stream);
     return launch_gather<1, 8>(a, grid, stream);
 }

@@ -52,7 +52,7 @@ struct DecodeArgs {
     int batch, hq, hkv, cap, fmt;
     int seq_len, splits, chunk;
     float qscale;           // sm_scale * log2(e)
-    int path;               // 0 auto, 1 score table (2-bit), 2 gather
+    int path;               // 0 auto, 1 score table (2-bit), 2 gather, 3 matrix cores (2-bit)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
