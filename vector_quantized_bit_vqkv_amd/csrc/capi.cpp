@@ -123,7 +123,7 @@ size_t vqkv_workspace_bytes(const vqkv_shape* s, int32_t num_splits) {
 int32_t vqkv_suggest_splits(const vqkv_shape* s, int32_t seq_len) {
     if (check_shape(s, false) != VQKV_OK || seq_len < 1) return 1;
     const int64_t streams = (int64_t)s->batch * s->num_kv_heads;
-    const int64_t want = ceil_div(512, streams);              // two work-groups per CU on 256 CUs
+    const int64_t want = ceil_div(256, streams);              // one work-group per CU on 256 CUs
     const int64_t cap = ceil_div(seq_len, 1024);              // keep >= 1024 tokens per split
     int64_t S = want < cap ? want : cap;
     if (S < 1) S = 1;
