@@ -15,20 +15,16 @@
 // (o normalized, lse) to the workspace.  Scores carry the factor
 // sm_scale * log2(e), so exp2 is the exponential and lse is in log2 units.
 //
-// Per tile, lane = token for the scores (each lane sums its token's J
-// sub-vector contributions), then lane = (sub-vector j, token group) for the
-// value accumulation (each lane owns dims [j*dsub, (j+1)*dsub) of all G
-// outputs).  The probabilities move between the two mappings through a
-// per-wave LDS buffer.  Value codes are stored blocked by sub-vector so that
-// this second mapping also reads contiguous 16-byte chunks.
-//
-// Scores, two ways (chosen by measurement):
-//   * score table (2-bit, G <= 4): per work-group, L[j][e][g] =
-//     c * q'_g[4j..4j+3] . C_K[e] for all 32 x 256 (j, e); a token's score is
-//     then 32 table reads and adds (one 16-byte read serves all heads);
-//   * gather: the token's centroids are read from the LDS codebook and dotted
-//     with q' (held in LDS, pre-scaled) -- needed for 1.5-bit, where the table
-//     would be 16 x 4096 x G floats.
+// Kernels (the 2-bit one chosen by measurement; the others stay selectable):
+//   * decode_mfma_kernel (2-bit, default): scores and values both on the
+//     matrix cores, v_mfma_f32_4x4x4f16, with the centroids gathered from
+//     LDS codebooks (details at the kernel);
+//   * decode_table_kernel (2-bit, G <= 4): per work-group score table
+//     L[j][e][g] = c * q'_g[4j..4j+3] . C_K[e] for all 32 x 256 (j, e), so a
+//     token's score is 32 table reads and adds; values on the matrix cores;
+//   * decode_gather_kernel: the token's centroids are read from the LDS
+//     codebook and dotted with q' (held in LDS, pre-scaled) -- the 1.5-bit
+//     path, where a table would be 16 x 4096 x G floats.
 #include "attn_common.h"
 #include "device_util.h"
 #include "internal.h"
