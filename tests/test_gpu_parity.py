@@ -216,6 +216,15 @@ def test_quantize_ties_go_to_lowest_index(fmt):
     assert not np.any(gk == 200)
     # Halfway between entries m and m+1 the lower index wins.
     assert np.array_equal(gv, (v[:, ::dsub] / 0.25 - 0.5).astype(np.uint16))
+    # The same tokens appended one at a time (the per-step append path).
+    kcodes1 = torch.zeros_like(kcodes)
+    vcodes1 = torch.zeros_like(kcodes)
+    for t in range(9):
+        vq.quantize_append(shape, dev(k[None, None, t:t + 1]), dev(v[None, None, t:t + 1]), t, dev(s[None]),
+                           book_dev(kb), book_dev(vb), kcodes1, vcodes1)
+    torch.cuda.synchronize()
+    assert np.array_equal(oracle.unpack_k(fmt, kcodes1[0, 0].cpu().numpy(), 9), kc_ref[:9])
+    assert np.array_equal(oracle.unpack_v(fmt, vcodes1[0, 0].cpu().numpy(), 9), vc_ref[:9])
 
 
 # ---------------------------------------------------------------------- attention

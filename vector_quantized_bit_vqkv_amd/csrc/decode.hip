@@ -741,22 +741,40 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
 
 // ----------------------------------------------------------------------- combine
 
+// One block per (b, q-head), thread d = output dim.  The split maximum and the
+// normalizer are reduced by all threads; the weighted sum over splits keeps
+// eight loads in flight per thread (empty splits, lse = -inf, weigh 0).
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
+    __shared__ float red[2];
     const int64_t bg = blockIdx.x;
-    const int d = threadIdx.x;
-    const float* lse = a.part_lse + bg * a.splits;
+    const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
+    const int S = a.splits;
+    const float* lse = a.part_lse + bg * S;
     float M = kNegInf;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, lse[s]);
-    float num = 0.0f, den = 0.0f;
+    for (int s = d; s < S; s += 128) M = fmaxf(M, lse[s]);
+    M = wave_max(M);
+    if (lane == 0) red[wave] = M;
+    __syncthreads();
+    M = fmaxf(red[0], red[1]);
+    __syncthreads();
+    float den = 0.0f, num = 0.0f;
     if (M != kNegInf) {
-        for (int s = 0; s < a.splits; ++s) {
+        for (int s = d; s < S; s += 128) {
             const float ls = lse[s];
-            if (ls == kNegInf) continue;
-            const float w = __builtin_amdgcn_exp2f(ls - M);
-            den += w;
-            num += w * a.part_o[(bg * a.splits + s) * kHeadDim + d];
+            den += ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
+        }
+        const float* po = a.part_o + bg * S * kHeadDim + d;
+#pragma unroll 8
+        for (int s = 0; s < S; ++s) {
+            const float ls = lse[s];
+            const float w = ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
+            num += w * po[(int64_t)s * kHeadDim];
         }
     }
+    den = wave_sum(den);
+    if (lane == 0) red[wave] = den;
+    __syncthreads();
+    den = red[0] + red[1];
     a.out[bg * kHeadDim + d] = den > 0.0f ? num / den : 0.0f;
 }
 

@@ -214,6 +214,123 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
     }
 }
 
+// ------------------------------------------------- append of a single token
+
+// The per-step append (one new token per sequence), latency-bound: one block
+// per (b, KV head); both codebooks, the key and the value row are staged in
+// LDS at once, one wave rotates the key (the same butterflies as block_fwht,
+// stage h exchanged between lanes l and l ^ h, so the result is identical),
+// and the K and V nearest-centroid searches run in one pass over slices of
+// the codebooks, merged in slice order (ties keep the lowest index).
+template <int FMT>
+__global__ __launch_bounds__(512) void quantize_token_kernel(AppendArgs a) {
+    using F = Fmt<FMT>;
+    constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
+    constexpr int NT = 512;
+    constexpr int P = 2 * J;                    // points: K sub-vectors, then V
+    constexpr int ES = NT / P;                  // slices per point
+    constexpr int EPS = E / ES;                 // centroids per slice
+    __shared__ __align__(16) uint16_t books[2][E * DS];
+    __shared__ double x[2][kHeadDim];
+    __shared__ double red_d[NT];
+    __shared__ int red_i[NT];
+    __shared__ uint16_t codes[P];
+
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int64_t stream = (int64_t)b * a.hkv + h;
+    {
+        const uint4* kb = (const uint4*)(a.k_book + (int64_t)h * E * DS);
+        const uint4* vb = (const uint4*)(a.v_book + (int64_t)h * E * DS);
+        for (int i = threadIdx.x; i < E * DS / 8; i += NT) {
+            ((uint4*)books[0])[i] = kb[i];
+            ((uint4*)books[1])[i] = vb[i];
+        }
+        const float* sm = a.smooth + (int64_t)h * kHeadDim;
+        if (threadIdx.x < kHeadDim) {
+            const int c = threadIdx.x;
+            x[0][c] = load_elem_d(a.k_new, stream * kHeadDim + c, a.dtype) / (double)sm[c];
+            x[1][c] = load_elem_d(a.v_new, stream * kHeadDim + c, a.dtype);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int l = threadIdx.x;
+        double lo = x[0][l], hi = x[0][l + 64];
+        for (int st = 1; st < 64; st <<= 1) {
+            const double olo = __shfl_xor(lo, st, 64), ohi = __shfl_xor(hi, st, 64);
+            if (l & st) { lo = olo - lo; hi = ohi - hi; }
+            else { lo = lo + olo; hi = hi + ohi; }
+        }
+        const double a0 = lo + hi, a1 = lo - hi;     // stage 64, within the lane
+        x[0][l] = a0 * kInvSqrtHeadDimD;
+        x[0][l + 64] = a1 * kInvSqrtHeadDimD;
+    }
+    __syncthreads();
+    {
+        const int pt = threadIdx.x / ES, sl = threadIdx.x % ES;
+        const int ph = pt / J, j = pt % J;
+        double xs[DS];
+#pragma unroll
+        for (int i = 0; i < DS; ++i) xs[i] = x[ph][j * DS + i];
+        const uint16_t* bk = books[ph];
+        double best = __builtin_inf();
+        int idx = sl * EPS;
+        for (int e = sl * EPS; e < (sl + 1) * EPS; ++e) {
+            double t = xs[0] - (double)half_bits_to_float(bk[e * DS]);
+            double d = t * t;
+#pragma unroll
+            for (int i = 1; i < DS; ++i) {
+                t = xs[i] - (double)half_bits_to_float(bk[e * DS + i]);
+                d = d + t * t;
+            }
+            if (d < best) { best = d; idx = e; }
+        }
+        red_d[threadIdx.x] = best;
+        red_i[threadIdx.x] = idx;
+    }
+    __syncthreads();
+    if (threadIdx.x < P) {
+        const int pt = threadIdx.x;
+        double best = red_d[pt * ES];
+        int idx = red_i[pt * ES];
+        for (int sl = 1; sl < ES; ++sl)
+            if (red_d[pt * ES + sl] < best) { best = red_d[pt * ES + sl]; idx = red_i[pt * ES + sl]; }
+        codes[pt] = (uint16_t)idx;
+    }
+    __syncthreads();
+    const int64_t t = a.start_pos;
+    uint8_t* kc = a.k_codes + stream * (int64_t)a.cap * W;
+    uint8_t* vc = a.v_codes + stream * (int64_t)a.cap * W;
+    if (FMT == 0) {
+        if (threadIdx.x < J) {
+            const int j = threadIdx.x;
+            kc[t * W + j] = (uint8_t)codes[j];
+            vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[J + j];
+        }
+    } else if (threadIdx.x < J / 2) {
+        // Keys: sub-vectors (2i, 2i+1) share 3 bytes.  Values: token t is one
+        // half of the pair (t & ~1, t | 1) of its 16-token block's row j; the
+        // other token's nibble is kept.
+        const int i = threadIdx.x;
+        const uint32_t c0 = codes[2 * i], c1 = codes[2 * i + 1];
+        uint8_t* pk = kc + t * W + 3 * i;
+        pk[0] = (uint8_t)(c0 & 0xff);
+        pk[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
+        pk[2] = (uint8_t)(c1 >> 4);
+        for (int j = 2 * i; j < 2 * i + 2; ++j) {
+            const uint32_t c = codes[J + j];
+            uint8_t* pv = vc + (t / 16) * 384 + j * 24 + 3 * ((t % 16) / 2);
+            if (!(t & 1)) {
+                pv[0] = (uint8_t)(c & 0xff);
+                pv[1] = (uint8_t)((pv[1] & 0xf0) | (c >> 8));
+            } else {
+                pv[1] = (uint8_t)((pv[1] & 0x0f) | ((c & 0xf) << 4));
+                pv[2] = (uint8_t)(c >> 4);
+            }
+        }
+    }
+}
+
 // --------------------------------------------------------- smoothing scales
 
 // s[h][c] = fp32 nearest sqrt(max_t |k[h][t][c]|).  The fp64 root is checked
@@ -375,6 +492,12 @@ hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
     const int TT = a.fmt == 0 ? AppendTile<0>::TT : AppendTile<1>::TT;
     const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
     const dim3 grid(last - first + 1, a.hkv, a.batch);
+    if (a.n_new == 1) {
+        const dim3 g1(1, a.hkv, a.batch);
+        if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.fmt == 0) hipLaunchKernelGGL(quantize_append_kernel<0>, grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(quantize_append_kernel<1>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
