@@ -45,10 +45,10 @@
  *   blocks of 64 tokens, 2048 bytes each, cut into 64 chunks of 32 bytes;
  *   the code of token t (u = t % 64) and sub-vector j sits in chunk
  *   16*((j%16)/4) + 4*(u%4) + j%4, at byte 2*(u/4) + j/16 of the chunk.
- *   1.5-bit: blocks of 16
- *   tokens, 384 bytes each; the 24 bytes at offset 24*j hold the 16 codes of
- *   sub-vector j, tokens (2i, 2i+1) of the block packed in bytes 3i..3i+2 by
- *   the 12-bit rule above.
+ *   1.5-bit: blocks of 64 tokens, 1536 bytes each, cut into 32 streams of 48
+ *   bytes; the codes of sub-vectors j and j + 8 (j < 8) of token t form one
+ *   12-bit pair (c0 = sub-vector j, packed by the rule above) in stream
+ *   8*(j/2) + 2*(u%4) + j%2, bytes 3*(u/4)..3*(u/4)+2.
  * - Codebooks: fp16 [Hkv][E][dsub], one for keys and one for values per KV
  *   head, shared by every sub-vector position.  Key codebooks live in the
  *   rotated space.

@@ -362,11 +362,10 @@ int vqo_attention_fp(int B, int Hq, int Hkv, int64_t T, const double* q, const d
  * (2i, 2i+1) share bytes 3i..3i+2 as b0 = c0 & 0xFF, b1 = (c0 >> 8) | ((c1 & 0xF) << 4),
  * b2 = c1 >> 4 (12-bit codes, 3 bytes per 2 sub-vectors).
  *
- * Values, blocked by sub-vector: 2-bit uses blocks of 32 tokens, 1 KB each;
- * within a block, row j (32 bytes) holds the code of sub-vector j for the 32
- * tokens in order.  1.5-bit uses blocks of 16 tokens, 384 bytes each; row j
- * (24 bytes) holds the 16 codes of sub-vector j, tokens (2i, 2i+1) packed in
- * bytes 3i..3i+2 by the same 12-bit rule.
+ * Values, in blocks of 64 tokens (see v_offset): 2-bit blocks of 2048 bytes
+ * (64 chunks of 32 bytes), 1.5-bit blocks of 1536 bytes (32 streams of 48
+ * bytes, each holding 16 pairs of 12-bit codes by the same rule; a pair is
+ * sub-vectors j and j + 8 of one token).
  *
  * codes: [T][J]; out: cap * W bytes.  Bytes of tokens >= T are left as they are. */
 static void put12(uint8_t* p, int which, uint16_t c)
@@ -422,9 +421,16 @@ static int64_t v_offset(int fmt, int64_t t, int j, int* which)
         *which = 0;
         return (t / 64) * 2048 + 32 * chunk + 2 * (u / 4) + j / 16;
     }
-    int64_t r = t % 16;
-    *which = (int)(r & 1);
-    return (t / 16) * 384 + j * 24 + 3 * (r / 2);
+    {
+        /* 64-token blocks of 1536 bytes, 32 streams of 48 bytes.  Stream
+           8*((j%8)/2) + 2*(u%4) + j%2 (u = t % 64) holds, in bytes
+           3*(u/4)..3*(u/4)+2, the pair (sub-vector j%8, sub-vector j%8 + 8)
+           of token t; sub-vector j is element j/8 of the pair. */
+        int64_t u = t % 64;
+        int64_t stream = 8 * ((j % 8) / 2) + 2 * (u % 4) + (j % 2);
+        *which = j / 8;
+        return (t / 64) * 1536 + 48 * stream + 3 * (u / 4);
+    }
 }
 
 int vqo_pack_v(int fmt, int64_t T, const uint16_t* codes, uint8_t* out)

@@ -388,11 +388,12 @@ def test_pack12_golden_examples():
         codes[0, 0], codes[0, 1] = int(c0, 16), int(c1, 16)
         kb = oracle.pack_k(1, codes, 64)
         assert list(kb[:3]) == [int(b0, 16), int(b1, 16), int(b2, 16)]
-        # Values pair consecutive tokens of one sub-vector row.
-        vcodes = np.zeros((2, 16), dtype=np.uint16)
-        vcodes[0, 5], vcodes[1, 5] = int(c0, 16), int(c1, 16)
+        # Values pair sub-vectors j and j + 8 of one token: (5, 13) of token 0
+        # is stream 8 * 2 + 0 + 1 = 17, bytes 17 * 48 ..
+        vcodes = np.zeros((1, 16), dtype=np.uint16)
+        vcodes[0, 5], vcodes[0, 13] = int(c0, 16), int(c1, 16)
         vb = oracle.pack_v(1, vcodes, 64)
-        assert list(vb[5 * 24:5 * 24 + 3]) == [int(b0, 16), int(b1, 16), int(b2, 16)]
+        assert list(vb[17 * 48:17 * 48 + 3]) == [int(b0, 16), int(b1, 16), int(b2, 16)]
 
 
 def test_pack12_round_trip_exhaustive():
@@ -404,6 +405,26 @@ def test_pack12_round_trip_exhaustive():
     assert kb.size == T * 24
     assert np.array_equal(oracle.unpack_k(1, kb, T), c)
     vb = oracle.pack_v(1, c, T)
+    assert np.array_equal(oracle.unpack_v(1, vb, T), c)
+
+
+def test_pack_1p5bit_value_positions():
+    """Hand-computed positions of the 1.5-bit value layout: token t (u = t % 64),
+    sub-vector j -> block t // 64 of 1536 bytes, stream 8*((j%8)//2) + 2*(u%4) + j%2,
+    bytes 3*(u//4)..+2, element j // 8 of the pair."""
+    T = 130
+    c = synth.random_codes(2, (T, 16), 4096)
+    vb = oracle.pack_v(1, c, 192)
+
+    def pair(off):
+        b0, b1, b2 = (int(x) for x in vb[off:off + 3])
+        return b0 | ((b1 & 0xF) << 8), (b1 >> 4) | (b2 << 4)
+    assert pair(0) == (c[0, 0], c[0, 8])                        # stream 0
+    assert pair(48 * 1 + 0) == (c[0, 1], c[0, 9])               # j = 1 -> stream 1
+    assert pair(48 * 3 + 0) == (c[1, 1], c[1, 9])               # t = 1, j = 1 -> 2 + 1
+    assert pair(48 * 28 + 3 * 15) == (c[62, 6], c[62, 14])      # u = 62: 8*3 + 2*2 + 0, byte 45
+    assert pair(1536 + 48 * 31 + 3 * 0) == (c[67, 7], c[67, 15])  # block 1, u = 3: 24 + 6 + 1
+    assert pair(2 * 1536 + 48 * 8 + 0) == (c[128, 2], c[128, 10])  # block 2, u = 0: 8*1 + 0 + 0
     assert np.array_equal(oracle.unpack_v(1, vb, T), c)
 
 

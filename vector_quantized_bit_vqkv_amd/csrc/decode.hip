@@ -360,13 +360,33 @@ __device__ __forceinline__ float4_t mfma_bcast(half4_t a, half4_t b, float4_t c)
 template <int K>
 constexpr uint32_t lookup_sel() { return 0x0c020000u | ((4u + K) << 8); }
 
-template <int G, int NW>
+// 24-bit little-endian value of bytes B..B+2 of a dword array (one v_perm_b32).
+template <int B, int N>
+__device__ __forceinline__ uint32_t bytes3_at(const uint32_t (&w)[N]) {
+    constexpr int d = B >> 2;
+    constexpr int d1 = (B + 2) >> 2;
+    constexpr uint32_t s0 = ((B + 0) >> 2) == d ? ((B + 0) & 3) : 4 + ((B + 0) & 3);
+    constexpr uint32_t s1 = ((B + 1) >> 2) == d ? ((B + 1) & 3) : 4 + ((B + 1) & 3);
+    constexpr uint32_t s2 = ((B + 2) >> 2) == d ? ((B + 2) & 3) : 4 + ((B + 2) & 3);
+    return __builtin_amdgcn_perm(w[d1], w[d], s0 | (s1 << 8) | (s2 << 16) | (0x0cu << 24));
+}
+
+// 1.5-bit: an 8-dim centroid is two 4-dim halves, so the same products run on
+// 32 "virtual" sub-vectors j' = 2j + e of 4 dims (e = half).  A score lookup
+// reads the whole 16-byte entry and feeds two products; a value lookup reads
+// one 8-byte half (e = lane % 2 with the lane mapping above).  Books are single
+// copies (2 x 64 KB).  Key codes are 24 bytes per token; value codes come in
+// 48-byte streams, one per lane pair, 16 pairs (sub-vectors j, j + 8) in step
+// order.
+template <int FMT, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int HB = (G + 3) / 4;
     constexpr int PT_BYTES = NW * HB * 512;
     constexpr int MERGE_BYTES = NW * G * (kHeadDim + 2) * 4;
     constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES;
     constexpr int SMEM = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
+    constexpr int W = FMT == 0 ? 32 : 24;
+    static_assert(FMT == 0 || 4096 * 16 == kBookBytes, "a 1.5-bit book fills one book region");
     __shared__ __align__(16) unsigned char smem[SMEM];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -374,16 +394,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int t_begin = s * a.chunk;
     const int t_end = min(a.seq_len, t_begin + a.chunk);
 
-    {
+    if constexpr (FMT == 0) {
         const uint2* kb = (const uint2*)(a.k_book + (int64_t)h * 256 * 4);
         const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * 256 * 4);
         for (int i = threadIdx.x; i < 256 * 32; i += NW * 64) {
             ((uint2*)smem)[i] = kb[i >> 5];
             ((uint2*)(smem + kBookBytes))[i] = vb[i >> 5];
         }
+    } else {
+        const uint4* kb = (const uint4*)(a.k_book + (int64_t)h * 4096 * 8);
+        const uint4* vb = (const uint4*)(a.v_book + (int64_t)h * 4096 * 8);
+        for (int i = threadIdx.x; i < 4096; i += NW * 64) {
+            ((uint4*)smem)[i] = kb[i];
+            ((uint4*)(smem + kBookBytes))[i] = vb[i];
+        }
     }
-    // Query operands: lane 4c + i holds head 4hb + i's dims of sub-vector
-    // 16r + c, times sm_scale * log2(e), rounded to fp16.
+    // Query operands: lane 4c + i holds head 4hb + i's dims of (virtual)
+    // sub-vector 16r + c, times sm_scale * log2(e), rounded to fp16.
     half4_t qa[HB][2];
     {
         const float* qp = a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim;
@@ -412,10 +439,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         o[hb][0] = o[hb][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
     const int64_t stream = (int64_t)b * a.hkv + h;
-    const uint8_t* kbase = a.k_codes + stream * (int64_t)a.cap * 32;
-    const uint8_t* vbase = a.v_codes + stream * (int64_t)a.cap * 32;
-    const uint32_t kofs = (uint32_t)(lane & 31) * 8;
-    const uint32_t vofs = kofs | (1u << 16);                // the value book starts at 64 KB
+    const uint8_t* kbase = a.k_codes + stream * (int64_t)a.cap * W;
+    const uint8_t* vbase = a.v_codes + stream * (int64_t)a.cap * W;
+    // 2-bit: 32 copies, lane l reads copy l % 32; the value book starts at 64 KB.
+    // 1.5-bit: value lookups read half e = lane % 2 of the entry.
+    const uint32_t kofs = FMT == 0 ? (uint32_t)(lane & 31) * 8 : 0u;
+    const uint32_t vofs = FMT == 0 ? (kofs | (1u << 16)) : (((uint32_t)(lane & 1) << 3) | (1u << 16));
     unsigned char* pt = smem + 2 * kBookBytes + wave * (HB * 512);
     const int row_w = lane * 8;
     const int row_r = ((lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3)) * 8;
@@ -427,37 +456,91 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // index is clamped to a valid tile so the loads stay in bounds.
     constexpr int kStride = NW * 64;
     const int first = t_begin + wave * 64;
+    // 2-bit: 32 bytes per lane per tile for keys and values.  1.5-bit: 24
+    // bytes (3 x 8) of keys, 48 bytes (3 x 16) of values from stream
+    // 8 (lane / 16) + 2 ((lane / 4) % 4) + (lane / 2) % 2 of the block.
+    const int vstream = 8 * (lane >> 4) + 2 * ((lane >> 2) & 3) + ((lane >> 1) & 1);
     const uint4* kc0 = (const uint4*)(kbase + (int64_t)lane * 32);
     const uint4* vc0 = (const uint4*)(vbase + (int64_t)lane * 32);
-    uint4 ck0, ck1, cv0, cv1;
+    const uint2* kc1 = (const uint2*)(kbase + (int64_t)lane * 24);
+    const uint4* vc1 = (const uint4*)(vbase + (int64_t)vstream * 48);
+    uint4 ck0, ck1, cv0, cv1;                               // 2-bit
+    uint2 dk[3];                                            // 1.5-bit
+    uint4 dv[3];
+    auto load_k = [&](int tl) {
+        if constexpr (FMT == 0) {
+            ck0 = kc0[(int64_t)tl * 2];
+            ck1 = kc0[(int64_t)tl * 2 + 1];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) dk[i] = kc1[(int64_t)tl * 3 + i];
+        }
+    };
+    auto load_v = [&](int tl) {
+        if constexpr (FMT == 0) {
+            cv0 = vc0[(int64_t)tl * 2];
+            cv1 = vc0[(int64_t)tl * 2 + 1];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) dv[i] = vc1[(int64_t)tl * 3 / 2 + i];   // tl * 24 bytes
+        }
+    };
     if (first < t_end) {
-        ck0 = kc0[(int64_t)first * 2];
-        ck1 = kc0[(int64_t)first * 2 + 1];
-        cv0 = vc0[(int64_t)first * 2];
-        cv1 = vc0[(int64_t)first * 2 + 1];
+        load_k(first);
+        load_v(first);
     }
 
     for (int tile = first; tile < t_end; tile += kStride) {
         const int t = tile + lane;
         const int nxt = tile + kStride < t_end ? tile + kStride : tile;
-        // Scores: 32 sub-vectors, 16 per code half.
         float4_t sacc[HB];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) sacc[hb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (FMT == 0) {
+            // Scores: 32 sub-vectors, 16 per code half.
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint4 ck = half == 0 ? ck0 : ck1;
-            const uint32_t kw[4] = {ck.x, ck.y, ck.z, ck.w};
-            static_for<0, 16>([&](auto jc) {
-                constexpr int jj = decltype(jc)::value;     // sub-vector 16 * half + jj
-                const uint32_t addr = __builtin_amdgcn_perm(kw[jj >> 2], kofs, lookup_sel<jj & 3>());
-                const half4_t kv = *(const half4_t*)(smem + addr);
+            for (int half = 0; half < 2; ++half) {
+                const uint4 ck = half == 0 ? ck0 : ck1;
+                const uint32_t kw[4] = {ck.x, ck.y, ck.z, ck.w};
+                static_for<0, 16>([&](auto jc) {
+                    constexpr int jj = decltype(jc)::value;     // sub-vector 16 * half + jj
+                    const uint32_t addr = __builtin_amdgcn_perm(kw[jj >> 2], kofs, lookup_sel<jj & 3>());
+                    const half4_t kv = *(const half4_t*)(smem + addr);
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) sacc[hb] = mfma_bcast<jj>(qa[hb][half], kv, sacc[hb]);
+                    for (int hb = 0; hb < HB; ++hb) sacc[hb] = mfma_bcast<jj>(qa[hb][half], kv, sacc[hb]);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+                if (half == 0) ck0 = kc0[(int64_t)nxt * 2];
+                else ck1 = kc0[(int64_t)nxt * 2 + 1];
+            }
+        } else {
+            // Scores: 16 sub-vectors in 8 pairs; each 16-byte entry feeds the
+            // products of virtual sub-vectors 2j and 2j + 1.
+            const uint32_t kw[6] = {dk[0].x, dk[0].y, dk[1].x, dk[1].y, dk[2].x, dk[2].y};
+            static_for<0, 8>([&](auto mc) {
+                constexpr int mp = decltype(mc)::value;
+                const uint32_t x = bytes3_at<3 * mp>(kw);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint32_t addr = u == 0 ? ((x << 4) & 0xfff0u) : ((x >> 8) & 0xfff0u);
+                    const uint4 ent = *(const uint4*)(smem + addr);
+                    const half4_t lo = __builtin_bit_cast(half4_t, make_uint2(ent.x, ent.y));
+                    const half4_t hi = __builtin_bit_cast(half4_t, make_uint2(ent.z, ent.w));
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) {
+                        // virtual sub-vectors 4 mp + 2u and 4 mp + 2u + 1, both in register pair mp / 4
+                        if (u == 0) {
+                            sacc[hb] = mfma_bcast<(4 * mp) & 15>(qa[hb][mp >> 2], lo, sacc[hb]);
+                            sacc[hb] = mfma_bcast<(4 * mp + 1) & 15>(qa[hb][mp >> 2], hi, sacc[hb]);
+                        } else {
+                            sacc[hb] = mfma_bcast<(4 * mp + 2) & 15>(qa[hb][mp >> 2], lo, sacc[hb]);
+                            sacc[hb] = mfma_bcast<(4 * mp + 3) & 15>(qa[hb][mp >> 2], hi, sacc[hb]);
+                        }
+                    }
+                }
             });
             __builtin_amdgcn_sched_barrier(0);
-            if (half == 0) ck0 = kc0[(int64_t)nxt * 2];
-            else ck1 = kc0[(int64_t)nxt * 2 + 1];
+            load_k(nxt);
         }
         float sc[G];
 #pragma unroll
@@ -484,28 +567,47 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             const uint2 pw = __builtin_bit_cast(uint2, pt_op[hb]);
             lsum[hb] = dot2(pw.x, kOnes, dot2(pw.y, kOnes, lsum[hb]));
         }
-        // Values: step st takes byte 2 st + half of the lane's code chunk.
+        if constexpr (FMT == 0) {
+            // Values: step st takes byte 2 st + half of the lane's code chunk.
 #pragma unroll
-        for (int hv = 0; hv < 2; ++hv) {
-            const uint4 cv = hv == 0 ? cv0 : cv1;
-            const uint32_t vw[4] = {cv.x, cv.y, cv.z, cv.w};
-            static_for<0, 8>([&](auto sc8) {
-                constexpr int st8 = decltype(sc8)::value;   // step 8 * hv + st8
+            for (int hv = 0; hv < 2; ++hv) {
+                const uint4 cv = hv == 0 ? cv0 : cv1;
+                const uint32_t vw[4] = {cv.x, cv.y, cv.z, cv.w};
+                static_for<0, 8>([&](auto sc8) {
+                    constexpr int st8 = decltype(sc8)::value;   // step 8 * hv + st8
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const uint32_t sel = hh == 0 ? lookup_sel<2 * (st8 & 1)>() : lookup_sel<2 * (st8 & 1) + 1>();
+                        const uint32_t addr = __builtin_amdgcn_perm(vw[st8 >> 1], vofs, sel);
+                        const half4_t vv = lds_read_tr16((const lds_char*)(smem + addr));
+#pragma unroll
+                        for (int hb = 0; hb < HB; ++hb) {
+                            if (hv == 0) o[hb][hh] = mfma_bcast<st8>(pt_op[hb], vv, o[hb][hh]);
+                            else o[hb][hh] = mfma_bcast<8 + st8>(pt_op[hb], vv, o[hb][hh]);
+                        }
+                    }
+                });
+                __builtin_amdgcn_sched_barrier(0);
+                if (hv == 0) cv0 = vc0[(int64_t)nxt * 2];
+                else cv1 = vc0[(int64_t)nxt * 2 + 1];
+            }
+        } else {
+            // Values: step st takes pair st of the lane's stream (bytes 3 st..).
+            const uint32_t vw[12] = {dv[0].x, dv[0].y, dv[0].z, dv[0].w, dv[1].x, dv[1].y,
+                                     dv[1].z, dv[1].w, dv[2].x, dv[2].y, dv[2].z, dv[2].w};
+            static_for<0, 16>([&](auto sc16) {
+                constexpr int st = decltype(sc16)::value;
+                const uint32_t x = bytes3_at<3 * st>(vw);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const uint32_t sel = hh == 0 ? lookup_sel<2 * (st8 & 1)>() : lookup_sel<2 * (st8 & 1) + 1>();
-                    const uint32_t addr = __builtin_amdgcn_perm(vw[st8 >> 1], vofs, sel);
+                    const uint32_t addr = hh == 0 ? (((x << 4) & 0xfff0u) | vofs) : (((x >> 8) & 0xfff0u) | vofs);
                     const half4_t vv = lds_read_tr16((const lds_char*)(smem + addr));
 #pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) {
-                        if (hv == 0) o[hb][hh] = mfma_bcast<st8>(pt_op[hb], vv, o[hb][hh]);
-                        else o[hb][hh] = mfma_bcast<8 + st8>(pt_op[hb], vv, o[hb][hh]);
-                    }
+                    for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_bcast<st>(pt_op[hb], vv, o[hb][hh]);
                 }
             });
             __builtin_amdgcn_sched_barrier(0);
-            if (hv == 0) cv0 = vc0[(int64_t)nxt * 2];
-            else cv1 = vc0[(int64_t)nxt * 2 + 1];
+            load_v(nxt);
         }
         wave_lds_sync();
     }
@@ -540,19 +642,14 @@ template <int FMT, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
     using F = DFmt<FMT>;
     constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
-    constexpr int NG = 64 / J;                              // token groups in the value mapping
-    constexpr int TPG = 64 / NG;                            // tokens per group
     constexpr int BOOK_BYTES = E * DS * 2;
     constexpr int MERGE_BYTES = NW * G * (kHeadDim + 2) * 4;
     constexpr int A_BYTES = BOOK_BYTES > MERGE_BYTES ? BOOK_BYTES : MERGE_BYTES;
+    constexpr int HB = (G + 3) / 4;
     __shared__ __align__(16) unsigned char region_a[A_BYTES];      // K book, then merge scratch
     __shared__ __align__(16) uint16_t vbook[E * DS];
     __shared__ __align__(16) float qs[G * kHeadDim];
-    // Probabilities: fp32 [token][head] (1.5-bit), or the fp16 A-operand
-    // buffer of the matrix-core value product (2-bit, HB blocks of 4 heads).
-    constexpr int HB = (G + 3) / 4;
-    constexpr int PB = FMT == 0 ? 16 * 8 * HB : 64 * G;
-    __shared__ __align__(16) float pbuf[NW][PB];
+    __shared__ __align__(16) uint32_t pbuf[NW][16 * 8 * HB];       // fp16 A operands of the value product
     uint16_t* kbook = (uint16_t*)region_a;
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -569,33 +666,33 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
         }
         const float* qp = a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim;
         for (int i = threadIdx.x; i < G * kHeadDim; i += NW * 64) qs[i] = qp[i] * a.qscale;
-        if (FMT == 0 && G % 4 != 0)                          // padding heads stay zero
-            for (int i = threadIdx.x; i < NW * PB; i += NW * 64) (&pbuf[0][0])[i] = 0.0f;
+        if (G % 4 != 0)                                      // padding heads stay zero
+            for (int i = threadIdx.x; i < NW * 16 * 8 * HB; i += NW * 64) (&pbuf[0][0])[i] = 0u;
     }
     __syncthreads();
 
-    float m[G], l[G], acc[G][DS];
+    float m[G], l[G];
     float4_t o[HB][2];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = kNegInf;
         l[g] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < DS; ++i) acc[g][i] = 0.0f;
     }
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) o[hb][0] = o[hb][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    constexpr int P_LOG2 = 15;                               // 2-bit: p and l carry 2^15
+    constexpr int P_LOG2 = 15;                               // p and l carry 2^15
     const int64_t stream = (int64_t)b * a.hkv + h;
     const uint8_t* kbase = a.k_codes + stream * (int64_t)a.cap * W;
     const uint8_t* vbase = a.v_codes + stream * (int64_t)a.cap * W;
-    const int jv = lane % J, grp = lane / J;
-    float* pw = pbuf[wave];
+    uint32_t* pw = pbuf[wave];
+    const lds_char* vt = (const lds_char*)vbook;
+    const uint32_t eofs = FMT == 0 ? 0u : (uint32_t)(lane & 1) * 8;   // 1.5-bit: half of the entry
+    const int vstream = 8 * (lane >> 4) + 2 * ((lane >> 2) & 3) + ((lane >> 1) & 1);
 
     for (int tile = t_begin + wave * 64; tile < t_end; tile += NW * 64) {
         const int t = tile + lane;
-        // Key codes of this lane's token, value codes of row jv of this lane's group.
-        uint32_t kw[W / 4], vw[TPG * (FMT == 0 ? 1 : 3) / (FMT == 0 ? 1 : 2) / 4];
+        // Key codes of this lane's token; value codes of its chunk or stream.
+        uint32_t kw[W / 4], vw[FMT == 0 ? 8 : 12];
         if constexpr (FMT == 0) {
             const uint4* kc = (const uint4*)(kbase + (int64_t)t * 32);
             const uint4 k0 = kc[0], k1 = kc[1];
@@ -609,13 +706,17 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
             const uint2* kc = (const uint2*)(kbase + (int64_t)t * 24);
             const uint2 k0 = kc[0], k1 = kc[1], k2 = kc[2];
             kw[0] = k0.x; kw[1] = k0.y; kw[2] = k1.x; kw[3] = k1.y; kw[4] = k2.x; kw[5] = k2.y;
-            const uint2* vc = (const uint2*)(vbase + (int64_t)(tile + grp * 16) * 24 + jv * 24);
-            const uint2 v0 = vc[0], v1 = vc[1], v2 = vc[2];
-            vw[0] = v0.x; vw[1] = v0.y; vw[2] = v1.x; vw[3] = v1.y; vw[4] = v2.x; vw[5] = v2.y;
+            const uint4* vc = (const uint4*)(vbase + (int64_t)tile * 24 + vstream * 48);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const uint4 v = vc[i];
+                vw[4 * i] = v.x; vw[4 * i + 1] = v.y; vw[4 * i + 2] = v.z; vw[4 * i + 3] = v.w;
+            }
         }
         float sc[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) sc[g] = 0.0f;
+        // Scores: gather the token's centroids, fp32 dot products with q'.
         // Codes are consumed RW dwords (SUB sub-vectors) per step from the front
         // of a rotating window: static register indexing, bounded loads in flight.
         constexpr int RW = FMT == 0 ? 1 : 3, SUB = FMT == 0 ? 4 : 8;
@@ -627,116 +728,72 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < W / 4 - RW; ++i) kw[i] = kw[i + RW];
 #pragma unroll
-          for (int jj = 0; jj < SUB; ++jj) {
-            const int j = j0 + jj;
-            const uint32_t code = FMT == 0 ? byte_at(cw, jj) : code12_at(cw, jj);
-            float c[DS];
-            if constexpr (DS == 4) {
-                const uint2 w = *(const uint2*)(kbook + code * 4);
-                c[0] = lo_half(w.x); c[1] = hi_half(w.x); c[2] = lo_half(w.y); c[3] = hi_half(w.y);
-            } else {
-                const uint4 w = *(const uint4*)(kbook + code * 8);
-                c[0] = lo_half(w.x); c[1] = hi_half(w.x); c[2] = lo_half(w.y); c[3] = hi_half(w.y);
-                c[4] = lo_half(w.z); c[5] = hi_half(w.z); c[6] = lo_half(w.w); c[7] = hi_half(w.w);
-            }
+            for (int jj = 0; jj < SUB; ++jj) {
+                const int j = j0 + jj;
+                const uint32_t code = FMT == 0 ? byte_at(cw, jj) : code12_at(cw, jj);
+                float c[DS];
+                if constexpr (DS == 4) {
+                    const uint2 w = *(const uint2*)(kbook + code * 4);
+                    c[0] = lo_half(w.x); c[1] = hi_half(w.x); c[2] = lo_half(w.y); c[3] = hi_half(w.y);
+                } else {
+                    const uint4 w = *(const uint4*)(kbook + code * 8);
+                    c[0] = lo_half(w.x); c[1] = hi_half(w.x); c[2] = lo_half(w.y); c[3] = hi_half(w.y);
+                    c[4] = lo_half(w.z); c[5] = hi_half(w.z); c[6] = lo_half(w.w); c[7] = hi_half(w.w);
+                }
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float* q = qs + g * kHeadDim + j * DS;
+                for (int g = 0; g < G; ++g) {
+                    const float* q = qs + g * kHeadDim + j * DS;
 #pragma unroll
-                for (int i = 0; i < DS; ++i) sc[g] += q[i] * c[i];
+                    for (int i = 0; i < DS; ++i) sc[g] += q[i] * c[i];
+                }
             }
-          }
         }
         if (t >= t_end) {
 #pragma unroll
             for (int g = 0; g < G; ++g) sc[g] = kNegInf;
         }
         float p[G];
-        if constexpr (FMT == 0) {
-            softmax_tile_lazy<G, P_LOG2>(sc, m, p, [&](int g, float alpha) {
-                l[g] *= alpha;
-                o[g >> 2][0][g & 3] *= alpha;
-                o[g >> 2][1][g & 3] *= alpha;
-            });
-            uint32_t* pw32 = (uint32_t*)pw;
-            store_probs<G, HB>(pw32, p, l, lane);
-            wave_lds_sync();
-            const lds_char* vt = (const lds_char*)vbook;
+        softmax_tile_lazy<G, P_LOG2>(sc, m, p, [&](int g, float alpha) {
+            l[g] *= alpha;
+            o[g >> 2][0][g & 3] *= alpha;
+            o[g >> 2][1][g & 3] *= alpha;
+        });
+        store_probs<G, HB>(pw, p, l, lane);
+        wave_lds_sync();
+        // Values on the matrix cores (same lane mapping as the matrix-core kernel).
+        static_for<0, 16>([&](auto sc16) {
+            constexpr int st = decltype(sc16)::value;
+            half4_t pa[HB];
 #pragma unroll
-            for (int st = 0; st < 16; ++st) {
-                half4_t pa[HB];
+            for (int hb = 0; hb < HB; ++hb)
+                pa[hb] = *(const half4_t*)((const char*)pw + st * 32 * HB + (4 * hb + (lane & 3)) * 8);
+            uint32_t x = 0;
+            if constexpr (FMT == 1) x = bytes3_at<3 * st>(vw);
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-                    pa[hb] = *(const half4_t*)((const char*)pw32 + st * 32 * HB + (4 * hb + (lane & 3)) * 8);
+            for (int hh = 0; hh < 2; ++hh) {
+                uint32_t addr;
+                if constexpr (FMT == 0) addr = byte_at(vw, 2 * st + hh) * 8;
+                else addr = (hh == 0 ? ((x << 4) & 0xfff0u) : ((x >> 8) & 0xfff0u)) | eofs;
+                const half4_t vb = lds_read_tr16(vt + addr);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const uint32_t code = byte_at(vw, 2 * st + hh);
-                    const half4_t vb = lds_read_tr16(vt + code * 8);
-#pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_4x4x4(pa[hb], vb, o[hb][hh]);
-                }
+                for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_4x4x4(pa[hb], vb, o[hb][hh]);
             }
-            wave_lds_sync();
-        } else {
-            softmax_tile<G, DS>(sc, m, l, acc, p);
-#pragma unroll
-            for (int g = 0; g < G; ++g) pw[lane * G + g] = p[g];
-            wave_lds_sync();
-            constexpr int VW = TPG * 3 / 2 / 4;
-#pragma unroll 1
-            for (int t0 = 0; t0 < TPG; t0 += SUB) {
-                uint32_t cw[RW];
-#pragma unroll
-                for (int i = 0; i < RW; ++i) cw[i] = vw[i];
-#pragma unroll
-                for (int i = 0; i < VW - RW; ++i) vw[i] = vw[i + RW];
-#pragma unroll
-                for (int ti = 0; ti < SUB; ++ti) {
-                    const int tt = t0 + ti;
-                    const float* pp = pw + (grp * TPG + tt) * G;
-                    const uint32_t code = code12_at(cw, ti);
-                    const uint4 w = *(const uint4*)(vbook + code * 8);
-                    float c[8];
-                    c[0] = lo_half(w.x); c[1] = hi_half(w.x); c[2] = lo_half(w.y); c[3] = hi_half(w.y);
-                    c[4] = lo_half(w.z); c[5] = hi_half(w.z); c[6] = lo_half(w.w); c[7] = hi_half(w.w);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float pv = pp[g];
-#pragma unroll
-                        for (int i = 0; i < DS; ++i) acc[g][i] += pv * c[i];
-                    }
-                }
-            }
-            wave_lds_sync();
-        }
+        });
+        wave_lds_sync();
     }
 
-    if constexpr (FMT == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) l[g] = 0.5f * wave_sum(l[g]);
-        __syncthreads();
-        float* scratch = (float*)region_a;
+    for (int g = 0; g < G; ++g) l[g] = 0.5f * wave_sum(l[g]);
+    __syncthreads();
+    float* scratch = (float*)region_a;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            scratch[(wave * G + g) * kHeadDim + lane] = o[g >> 2][0][g & 3];
-            scratch[(wave * G + g) * kHeadDim + 64 + lane] = o[g >> 2][1][g & 3];
-        }
-        stash_ml<G, NW>(scratch, m, l);
-        __syncthreads();
-        merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2);
-    } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            l[g] = wave_sum(l[g]);
-#pragma unroll
-            for (int i = 0; i < DS; ++i) {
-                if (NG >= 4) acc[g][i] += xor_lane(acc[g][i], 16);
-                acc[g][i] += xor_lane(acc[g][i], 32);
-            }
-        }
-        __syncthreads();
-        merge_and_store<G, DS, NW>((float*)region_a, m, l, acc, a, b, h, s);
+    for (int g = 0; g < G; ++g) {
+        scratch[(wave * G + g) * kHeadDim + lane] = o[g >> 2][0][g & 3];
+        scratch[(wave * G + g) * kHeadDim + 64 + lane] = o[g >> 2][1][g & 3];
     }
+    stash_ml<G, NW>(scratch, m, l);
+    __syncthreads();
+    merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2);
 }
 
 // ----------------------------------------------------------------------- combine
@@ -795,8 +852,8 @@ hipError_t launch_gather(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid(a.splits, a.hkv, a.batch);
     const int G = a.hq / a.hkv;
-    // 2-bit: the matrix-core kernel unless a measurement override asks for
-    // the score-table (G <= 4) or gather kernel.  1.5-bit: gather.
+    // The matrix-core kernel unless a measurement override asks for the
+    // score-table (2-bit, G <= 4) or gather kernel.
     if (a.fmt == 0 && a.path == 1) {
         constexpr int NW = 16;
         switch (G) {
@@ -808,17 +865,25 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         }
         return hipGetLastError();
     }
-    if (a.fmt == 0 && a.path != 2) {
+    if (a.path != 2) {
         constexpr int NW = 16;
-        switch (G) {
-#define VQKV_G(GV) case GV: hipLaunchKernelGGL((decode_mfma_kernel<GV, NW>), grid, dim3(NW * 64), 0, stream, a); break;
-            VQKV_G(1) VQKV_G(2) VQKV_G(3) VQKV_G(4) VQKV_G(5) VQKV_G(6) VQKV_G(7) VQKV_G(8)
+        if (a.fmt == 0) {
+            switch (G) {
+#define VQKV_G(GV) case GV: hipLaunchKernelGGL((decode_mfma_kernel<0, GV, NW>), grid, dim3(NW * 64), 0, stream, a); break;
+                VQKV_G(1) VQKV_G(2) VQKV_G(3) VQKV_G(4) VQKV_G(5) VQKV_G(6) VQKV_G(7) VQKV_G(8)
 #undef VQKV_G
-            default: return hipErrorInvalidValue;
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (G) {
+#define VQKV_G(GV) case GV: hipLaunchKernelGGL((decode_mfma_kernel<1, GV, NW>), grid, dim3(NW * 64), 0, stream, a); break;
+                VQKV_G(1) VQKV_G(2) VQKV_G(3) VQKV_G(4) VQKV_G(5) VQKV_G(6) VQKV_G(7) VQKV_G(8)
+#undef VQKV_G
+                default: return hipErrorInvalidValue;
+            }
         }
         return hipGetLastError();
     }
-    if (a.path == 1) return hipErrorInvalidValue;
     if (a.fmt == 0) return launch_gather<0, 8>(a, grid, stream);
     return launch_gather<1, 8>(a, grid, stream);
 }

@@ -18,6 +18,17 @@ __host__ __device__ __forceinline__ int64_t v_code_offset_2bit(int64_t t, int j)
     return (t >> 6) * 2048 + 32 * chunk + 2 * (u >> 2) + (j >> 4);
 }
 
+// Byte offset of the 3-byte pair holding the value codes of sub-vectors
+// (j, j + 8), j < 8, of token t in a 1.5-bit stream.  Blocks of 64 tokens x 16
+// sub-vectors = 1536 bytes, cut into 32 streams of 48 bytes, stream
+// 8*(j/2) + 2*(t%4) + j%2 holding the pair at bytes 3*((t%64)/4)..+2.  A stream
+// is what lanes 2m and 2m+1 of the decode wave read for the block.
+__host__ __device__ __forceinline__ int64_t v_pair_offset_1p5(int64_t t, int j) {
+    const int u = (int)(t & 63);
+    const int stream = 8 * (j >> 1) + 2 * (u & 3) + (j & 1);
+    return (t >> 6) * 1536 + 48 * stream + 3 * (u >> 2);
+}
+
 struct TransformQueryArgs {
     const void* q;          // [B][Hq][128], bf16 or fp32
     int dtype;              // 0 bf16, 1 fp32

@@ -188,28 +188,15 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
             p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
             p[2] = (uint8_t)(c1 >> 4);
         }
-        // Values: tokens (2i, 2i+1) of a 16-token block share 3 bytes of row j.
-        // Tiles are aligned to even positions, so both tokens of a pair belong
-        // to this block; a pair with only one token in range keeps the other
-        // token's nibble.
-        const int pr0 = lo / 2, pr1 = (hi - 1) / 2;     // absolute pair indices
-        const int npr = pr1 - pr0 + 1;
-        for (int idx = threadIdx.x; idx < npr * J; idx += blockDim.x) {
-            const int pr = pr0 + idx / J, j = idx % J;
-            const int64_t t0 = 2 * (int64_t)pr;
-            uint8_t* p = vc + (t0 / 16) * 384 + j * 24 + 3 * ((t0 % 16) / 2);
-            const bool has0 = t0 >= lo, has1 = t0 + 1 < hi;
-            if (has0) {
-                const uint32_t c0 = codes[1][(int)(t0 - tile_base) * J + j];
-                p[0] = (uint8_t)(c0 & 0xff);
-                p[1] = has1 ? (uint8_t)((c0 >> 8) | ((codes[1][(int)(t0 + 1 - tile_base) * J + j] & 0xf) << 4))
-                            : (uint8_t)((p[1] & 0xf0) | (c0 >> 8));
-            }
-            if (has1) {
-                const uint32_t c1 = codes[1][(int)(t0 + 1 - tile_base) * J + j];
-                if (!has0) p[1] = (uint8_t)((p[1] & 0x0f) | ((c1 & 0xf) << 4));
-                p[2] = (uint8_t)(c1 >> 4);
-            }
+        // Values: sub-vectors (j, j + 8) of a token share 3 bytes.
+        for (int idx = threadIdx.x; idx < nt * (J / 2); idx += blockDim.x) {
+            const int r = off + idx / (J / 2), j = idx % (J / 2);
+            const int64_t t = tile_base + r;
+            const uint32_t c0 = codes[1][r * J + j], c1 = codes[1][r * J + j + 8];
+            uint8_t* p = vc + v_pair_offset_1p5(t, j);
+            p[0] = (uint8_t)(c0 & 0xff);
+            p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
+            p[2] = (uint8_t)(c1 >> 4);
         }
     }
 }
@@ -308,26 +295,18 @@ __global__ __launch_bounds__(512) void quantize_token_kernel(AppendArgs a) {
             vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[J + j];
         }
     } else if (threadIdx.x < J / 2) {
-        // Keys: sub-vectors (2i, 2i+1) share 3 bytes.  Values: token t is one
-        // half of the pair (t & ~1, t | 1) of its 16-token block's row j; the
-        // other token's nibble is kept.
+        // Keys: sub-vectors (2i, 2i+1) share 3 bytes; values: (i, i + 8).
         const int i = threadIdx.x;
         const uint32_t c0 = codes[2 * i], c1 = codes[2 * i + 1];
         uint8_t* pk = kc + t * W + 3 * i;
         pk[0] = (uint8_t)(c0 & 0xff);
         pk[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
         pk[2] = (uint8_t)(c1 >> 4);
-        for (int j = 2 * i; j < 2 * i + 2; ++j) {
-            const uint32_t c = codes[J + j];
-            uint8_t* pv = vc + (t / 16) * 384 + j * 24 + 3 * ((t % 16) / 2);
-            if (!(t & 1)) {
-                pv[0] = (uint8_t)(c & 0xff);
-                pv[1] = (uint8_t)((pv[1] & 0xf0) | (c >> 8));
-            } else {
-                pv[1] = (uint8_t)((pv[1] & 0x0f) | ((c & 0xf) << 4));
-                pv[2] = (uint8_t)(c >> 4);
-            }
-        }
+        const uint32_t v0 = codes[J + i], v1 = codes[J + i + 8];
+        uint8_t* pv = vc + v_pair_offset_1p5(t, i);
+        pv[0] = (uint8_t)(v0 & 0xff);
+        pv[1] = (uint8_t)((v0 >> 8) | ((v1 & 0xf) << 4));
+        pv[2] = (uint8_t)(v1 >> 4);
     }
 }
 
