@@ -293,13 +293,13 @@ def read_stream_peak(dev):
     buf.fill_(1)
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
     for _ in range(3):
-        vq.baseline_read_stream(buf, sink, 8192)
+        vq.baseline_read_stream(buf, sink, 2048)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     n = 10
     for _ in range(n):
-        vq.baseline_read_stream(buf, sink, 8192)
+        vq.baseline_read_stream(buf, sink, 2048)
     b.record()
     torch.cuda.synchronize()
     gbps = buf.numel() * n / (a.elapsed_time(b) * 1e-3) / 1e9

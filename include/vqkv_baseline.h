@@ -38,9 +38,9 @@ vqkv_status vqkv_baseline_bf16_decode(const vqkv_shape* shape, const void* q, co
                                       void* stream);
 
 /* Reads `bytes` (rounded down to 16) of device memory once with 16-byte
- * loads on a grid of `blocks` x 256 threads; XOR-folds into sink[1024]
- * (device) so the loads cannot be dropped.  Measures achievable HBM read
- * bandwidth. */
+ * loads: `blocks` work-groups of 1024 threads, each reading one contiguous
+ * chunk; XOR-folds into sink[1024] (device) so the loads cannot be dropped.
+ * Measures achievable HBM read bandwidth. */
 vqkv_status vqkv_baseline_read_stream(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
                                       void* stream);
 

@@ -122,16 +122,22 @@ __global__ __launch_bounds__(NW * 64) void bf16_decode_kernel(Bf16Args in, Decod
 }
 
 // Grid-stride read of `n16` 16-byte words; one xor per block keeps the loads live.
-__global__ __launch_bounds__(256) void read_stream_kernel(const uint4* buf, int64_t n16, uint32_t* sink) {
+// Each block reads one contiguous chunk of the buffer, 1024 threads with four
+// 16-byte loads in flight each (the pattern that reached the highest read rate
+// in a sweep of grid-stride and chunked variants on MI355X).
+__global__ __launch_bounds__(1024) void read_stream_kernel(const uint4* buf, int64_t n16, int64_t chunk,
+                                                           uint32_t* sink) {
     uint32_t x = 0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a0 = buf[i], a1 = buf[i + stride], a2 = buf[i + 2 * stride], a3 = buf[i + 3 * stride];
+    const int64_t begin = (int64_t)blockIdx.x * chunk;
+    const int64_t end = begin + chunk < n16 ? begin + chunk : n16;
+    const int B = blockDim.x;
+    int64_t i = begin + threadIdx.x;
+    for (; i + 3 * B < end; i += 4 * B) {
+        const uint4 a0 = buf[i], a1 = buf[i + B], a2 = buf[i + 2 * B], a3 = buf[i + 3 * B];
         x ^= a0.x ^ a0.y ^ a0.z ^ a0.w ^ a1.x ^ a1.y ^ a1.z ^ a1.w;
         x ^= a2.x ^ a2.y ^ a2.z ^ a2.w ^ a3.x ^ a3.y ^ a3.z ^ a3.w;
     }
-    for (; i < n16; i += stride) {
+    for (; i < end; i += B) {
         const uint4 a0 = buf[i];
         x ^= a0.x ^ a0.y ^ a0.z ^ a0.w;
     }
@@ -194,8 +200,10 @@ vqkv_status vqkv_baseline_read_stream(const void* buf, size_t bytes, uint32_t* s
     using namespace vqkv;
     if (!buf || !sink || ((uintptr_t)buf & 15) || bytes < 16 || blocks < 1)
         return fail(VQKV_ERR_INVALID_ARG, "bad read-stream arguments");
-    hipLaunchKernelGGL(read_stream_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)buf,
-                       (int64_t)(bytes / 16), sink);
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int64_t chunk = (n16 + blocks - 1) / blocks;
+    hipLaunchKernelGGL(read_stream_kernel, dim3(blocks), dim3(1024), 0, (hipStream_t)stream, (const uint4*)buf,
+                       n16, chunk, sink);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? VQKV_OK : fail(VQKV_ERR_HIP, hipGetErrorString(e));
 }

@@ -203,71 +203,65 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
 // ------------------------------------------------- append of a single token
 
-// The per-step append (one new token per sequence), latency-bound: one block
-// per (b, KV head); both codebooks, the key and the value row are staged in
-// LDS at once, one wave rotates the key (the same butterflies as block_fwht,
-// stage h exchanged between lanes l and l ^ h, so the result is identical),
-// and the K and V nearest-centroid searches run in one pass over slices of
-// the codebooks, merged in slice order (ties keep the lowest index).
+// The per-step append (one new token per sequence), latency-bound: grid
+// (2, Hkv, B), block x = 0 codes the key, x = 1 the value.  The codebook and
+// the row are staged in LDS at once; the key block rotates the key with one
+// wave (the same butterflies as block_fwht, stage h exchanged between lanes l
+// and l ^ h, so the result is identical); the nearest-centroid searches run
+// over slices of the codebook, merged in slice order (ties keep the lowest
+// index).
 template <int FMT>
-__global__ __launch_bounds__(512) void quantize_token_kernel(AppendArgs a) {
+__global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
     using F = Fmt<FMT>;
     constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
-    constexpr int NT = 512;
-    constexpr int P = 2 * J;                    // points: K sub-vectors, then V
-    constexpr int ES = NT / P;                  // slices per point
+    constexpr int NT = 1024;
+    constexpr int ES = NT / J;                  // slices per sub-vector
     constexpr int EPS = E / ES;                 // centroids per slice
-    __shared__ __align__(16) uint16_t books[2][E * DS];
-    __shared__ double x[2][kHeadDim];
+    __shared__ __align__(16) uint16_t book[E * DS];
+    __shared__ double x[kHeadDim];
     __shared__ double red_d[NT];
     __shared__ int red_i[NT];
-    __shared__ uint16_t codes[P];
+    __shared__ uint16_t codes[J];
 
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int ph = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t stream = (int64_t)b * a.hkv + h;
     {
-        const uint4* kb = (const uint4*)(a.k_book + (int64_t)h * E * DS);
-        const uint4* vb = (const uint4*)(a.v_book + (int64_t)h * E * DS);
-        for (int i = threadIdx.x; i < E * DS / 8; i += NT) {
-            ((uint4*)books[0])[i] = kb[i];
-            ((uint4*)books[1])[i] = vb[i];
-        }
-        const float* sm = a.smooth + (int64_t)h * kHeadDim;
+        const uint4* src = (const uint4*)((ph == 0 ? a.k_book : a.v_book) + (int64_t)h * E * DS);
+        for (int i = threadIdx.x; i < E * DS / 8; i += NT) ((uint4*)book)[i] = src[i];
         if (threadIdx.x < kHeadDim) {
             const int c = threadIdx.x;
-            x[0][c] = load_elem_d(a.k_new, stream * kHeadDim + c, a.dtype) / (double)sm[c];
-            x[1][c] = load_elem_d(a.v_new, stream * kHeadDim + c, a.dtype);
+            x[c] = ph == 0 ? load_elem_d(a.k_new, stream * kHeadDim + c, a.dtype) /
+                                 (double)a.smooth[(int64_t)h * kHeadDim + c]
+                           : load_elem_d(a.v_new, stream * kHeadDim + c, a.dtype);
         }
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
+    if (ph == 0 && threadIdx.x < 64) {
         const int l = threadIdx.x;
-        double lo = x[0][l], hi = x[0][l + 64];
+        double lo = x[l], hi = x[l + 64];
         for (int st = 1; st < 64; st <<= 1) {
             const double olo = __shfl_xor(lo, st, 64), ohi = __shfl_xor(hi, st, 64);
             if (l & st) { lo = olo - lo; hi = ohi - hi; }
             else { lo = lo + olo; hi = hi + ohi; }
         }
         const double a0 = lo + hi, a1 = lo - hi;     // stage 64, within the lane
-        x[0][l] = a0 * kInvSqrtHeadDimD;
-        x[0][l + 64] = a1 * kInvSqrtHeadDimD;
+        x[l] = a0 * kInvSqrtHeadDimD;
+        x[l + 64] = a1 * kInvSqrtHeadDimD;
     }
     __syncthreads();
     {
-        const int pt = threadIdx.x / ES, sl = threadIdx.x % ES;
-        const int ph = pt / J, j = pt % J;
+        const int j = threadIdx.x / ES, sl = threadIdx.x % ES;
         double xs[DS];
 #pragma unroll
-        for (int i = 0; i < DS; ++i) xs[i] = x[ph][j * DS + i];
-        const uint16_t* bk = books[ph];
+        for (int i = 0; i < DS; ++i) xs[i] = x[j * DS + i];
         double best = __builtin_inf();
         int idx = sl * EPS;
         for (int e = sl * EPS; e < (sl + 1) * EPS; ++e) {
-            double t = xs[0] - (double)half_bits_to_float(bk[e * DS]);
+            double t = xs[0] - (double)half_bits_to_float(book[e * DS]);
             double d = t * t;
 #pragma unroll
             for (int i = 1; i < DS; ++i) {
-                t = xs[i] - (double)half_bits_to_float(bk[e * DS + i]);
+                t = xs[i] - (double)half_bits_to_float(book[e * DS + i]);
                 d = d + t * t;
             }
             if (d < best) { best = d; idx = e; }
@@ -276,37 +270,32 @@ __global__ __launch_bounds__(512) void quantize_token_kernel(AppendArgs a) {
         red_i[threadIdx.x] = idx;
     }
     __syncthreads();
-    if (threadIdx.x < P) {
-        const int pt = threadIdx.x;
-        double best = red_d[pt * ES];
-        int idx = red_i[pt * ES];
+    if (threadIdx.x < J) {
+        const int j = threadIdx.x;
+        double best = red_d[j * ES];
+        int idx = red_i[j * ES];
         for (int sl = 1; sl < ES; ++sl)
-            if (red_d[pt * ES + sl] < best) { best = red_d[pt * ES + sl]; idx = red_i[pt * ES + sl]; }
-        codes[pt] = (uint16_t)idx;
+            if (red_d[j * ES + sl] < best) { best = red_d[j * ES + sl]; idx = red_i[j * ES + sl]; }
+        codes[j] = (uint16_t)idx;
     }
     __syncthreads();
     const int64_t t = a.start_pos;
-    uint8_t* kc = a.k_codes + stream * (int64_t)a.cap * W;
-    uint8_t* vc = a.v_codes + stream * (int64_t)a.cap * W;
     if (FMT == 0) {
         if (threadIdx.x < J) {
             const int j = threadIdx.x;
-            kc[t * W + j] = (uint8_t)codes[j];
-            vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[J + j];
+            if (ph == 0) a.k_codes[stream * (int64_t)a.cap * W + t * W + j] = (uint8_t)codes[j];
+            else a.v_codes[stream * (int64_t)a.cap * W + v_code_offset_2bit(t, j)] = (uint8_t)codes[j];
         }
     } else if (threadIdx.x < J / 2) {
         // Keys: sub-vectors (2i, 2i+1) share 3 bytes; values: (i, i + 8).
         const int i = threadIdx.x;
-        const uint32_t c0 = codes[2 * i], c1 = codes[2 * i + 1];
-        uint8_t* pk = kc + t * W + 3 * i;
-        pk[0] = (uint8_t)(c0 & 0xff);
-        pk[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
-        pk[2] = (uint8_t)(c1 >> 4);
-        const uint32_t v0 = codes[J + i], v1 = codes[J + i + 8];
-        uint8_t* pv = vc + v_pair_offset_1p5(t, i);
-        pv[0] = (uint8_t)(v0 & 0xff);
-        pv[1] = (uint8_t)((v0 >> 8) | ((v1 & 0xf) << 4));
-        pv[2] = (uint8_t)(v1 >> 4);
+        const uint32_t c0 = ph == 0 ? codes[2 * i] : codes[i];
+        const uint32_t c1 = ph == 0 ? codes[2 * i + 1] : codes[i + 8];
+        uint8_t* p = ph == 0 ? a.k_codes + stream * (int64_t)a.cap * W + t * W + 3 * i
+                             : a.v_codes + stream * (int64_t)a.cap * W + v_pair_offset_1p5(t, i);
+        p[0] = (uint8_t)(c0 & 0xff);
+        p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
+        p[2] = (uint8_t)(c1 >> 4);
     }
 }
 
@@ -472,9 +461,9 @@ hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
     const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
     const dim3 grid(last - first + 1, a.hkv, a.batch);
     if (a.n_new == 1) {
-        const dim3 g1(1, a.hkv, a.batch);
-        if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(512), 0, stream, a);
-        else hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(512), 0, stream, a);
+        const dim3 g1(2, a.hkv, a.batch);
+        if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     if (a.fmt == 0) hipLaunchKernelGGL(quantize_append_kernel<0>, grid, dim3(256), 0, stream, a);
