@@ -451,9 +451,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int P_LOG2 = 15;
     constexpr uint32_t kOnes = 0x3c003c00u;
 
-    // Each code register is reloaded with the next tile's codes right after
-    // its last use (a whole phase of work hides the load); the next tile
-    // index is clamped to a valid tile so the loads stay in bounds.
+    // Each code register is reloaded with a later tile's codes right after
+    // its last use (at least a whole phase of work hides the load); the
+    // tile index is clamped to a valid tile so the loads stay in bounds.
     constexpr int kStride = NW * 64;
     const int first = t_begin + wave * 64;
     // 2-bit: 32 bytes per lane per tile for keys and values.  1.5-bit: 24
@@ -490,9 +490,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         load_v(first);
     }
 
-    for (int tile = first; tile < t_end; tile += kStride) {
+    // One tile; the 2-bit code registers are parameters so that two sets can
+    // alternate (codes loaded two tiles ahead).
+    auto step = [&](int tile, int nxt, uint4& ck0, uint4& ck1, uint4& cv0, uint4& cv1) {
         const int t = tile + lane;
-        const int nxt = tile + kStride < t_end ? tile + kStride : tile;
         float4_t sacc[HB];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) sacc[hb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -610,6 +611,26 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             load_v(nxt);
         }
         wave_lds_sync();
+    };
+    if constexpr (FMT == 0) {
+        // Two code sets: each tile's codes arrive two tiles ahead, which
+        // matters when a wave has few tiles (batch 1: six per wave).
+        uint4 bk0, bk1, bv0, bv1;
+        if (first < t_end) {
+            const int second = first + kStride < t_end ? first + kStride : first;
+            bk0 = kc0[(int64_t)second * 2];
+            bk1 = kc0[(int64_t)second * 2 + 1];
+            bv0 = vc0[(int64_t)second * 2];
+            bv1 = vc0[(int64_t)second * 2 + 1];
+        }
+        for (int tile = first; tile < t_end; tile += 2 * kStride) {
+            step(tile, tile + 2 * kStride < t_end ? tile + 2 * kStride : tile, ck0, ck1, cv0, cv1);
+            const int t2 = tile + kStride;
+            if (t2 < t_end) step(t2, t2 + 2 * kStride < t_end ? t2 + 2 * kStride : t2, bk0, bk1, bv0, bv1);
+        }
+    } else {
+        for (int tile = first; tile < t_end; tile += kStride)
+            step(tile, tile + kStride < t_end ? tile + kStride : tile, ck0, ck1, cv0, cv1);
     }
 
     float l[G];
