@@ -227,6 +227,45 @@ def test_quantize_ties_go_to_lowest_index(fmt):
     assert np.array_equal(oracle.unpack_v(fmt, vcodes1[0, 0].cpu().numpy(), 9), vc_ref[:9])
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_fallbacks_match_oracle(fmt):
+    """Points the distance screen cannot take (coordinates beyond the fp16 range,
+    NaN) go through the exact scan: codes still equal the oracle's, in the bulk
+    and in the one-token path.  A NaN makes every distance NaN, so the lowest
+    index, 0, is the code (the oracle's rule)."""
+    say(f"quantize fallbacks fmt{fmt}")
+    E, dsub = oracle.FORMATS[fmt]
+    rng = np.random.default_rng(11 + fmt)
+    n = 40
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    k[3] *= 3.0e5                     # |x| far beyond 2^15 after the transform
+    v[5] *= 1.0e5
+    v[7, 9] = np.nan                  # one value sub-vector
+    k[11, 4] = np.nan                 # spreads over the whole rotated key
+    v[13, :dsub] = 40000.0            # just past the fp16-safe range
+    s = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    kb = synth.random_fp16_book(21, (1, E, dsub), 0.8)
+    vb = synth.random_fp16_book(22, (1, E, dsub), 1.0)
+    kc_ref, vc_ref = oracle.quantize(fmt, k, v, s, kb[0], vb[0])
+    assert np.all(kc_ref[11] == 0) and vc_ref[7, 9 // dsub] == 0
+    shape = vq.make_shape(1, 1, 1, 64, fmt)
+    W = vq.code_bytes_per_token(fmt)
+    for mode in ("bulk", "one-token"):
+        kcodes = torch.zeros((1, 1, 64 * W), dtype=torch.uint8, device=DEV)
+        vcodes = torch.zeros_like(kcodes)
+        if mode == "bulk":
+            vq.quantize_append(shape, dev(k[None, None]), dev(v[None, None]), 0, dev(s[None]), book_dev(kb),
+                               book_dev(vb), kcodes, vcodes)
+        else:
+            for t in range(n):
+                vq.quantize_append(shape, dev(k[None, None, t:t + 1]), dev(v[None, None, t:t + 1]), t, dev(s[None]),
+                                   book_dev(kb), book_dev(vb), kcodes, vcodes)
+        torch.cuda.synchronize()
+        assert np.array_equal(oracle.unpack_k(fmt, kcodes[0, 0].cpu().numpy(), n), kc_ref), mode
+        assert np.array_equal(oracle.unpack_v(fmt, vcodes[0, 0].cpu().numpy(), n), vc_ref), mode
+
+
 # ---------------------------------------------------------------------- attention
 
 def _attn_inputs(fmt, B, Hq, Hkv, T, seed, cap=None):

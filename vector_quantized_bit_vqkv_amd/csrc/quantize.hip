@@ -91,12 +91,326 @@ __device__ __forceinline__ void argmin_range(const double* x, const float* book,
     }
 }
 
+// ------------------------------------------------- matrix-core distance screen
+//
+// Nearest centroid by a screen and an exact refinement, a set of points at a time:
+// s~_e = |c_e|^2 - 2 x.c_e on v_mfma_f32_4x4x4f16, with x split into fp16
+// hi + lo parts (products exact, fp32 sums) and broadcast to all 16 blocks
+// (CBSZ = 4, ABID = group of 4 points), each lane holding one centroid of a
+// 64-centroid group.  |s~_e - s_e| <= tau, with s_e = |c_e|^2 - 2 x.c_e exact
+// and tau = 2^-18 (|x| + max|c|)^2 + 2^-22 max|c|_1 (twice the worst case of
+// the x split, 18 fp32 accumulations, the fp32 |c|^2 and the final rounding).
+// Every centroid with s~ <= min s~ + 3 tau is a candidate; candidates get the
+// exact fp64 distance in the pinned order and the lowest index among the
+// smallest wins, so the code equals the brute-force one.  Each lane keeps its
+// best and second-best screened value: when a lane's second value is also a
+// candidate, or a coordinate is outside the fp16 range (|x| >= 2^15, NaN),
+// the point falls back to the exact scan of the whole book.
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+template <int V> struct IntC { static constexpr int value = V; };
+template <int I, int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+template <int ABID>
+__device__ __forceinline__ float4_t mfma_bcast(half4_t a, half4_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, ABID, 0);
+}
+
+// Exact distance to an fp16 book entry, pinned order.
+template <int DS>
+__device__ __forceinline__ double dist_h(const double* x, const uint16_t* c) {
+    double t = x[0] - (double)half_bits_to_float(c[0]);
+    double d = t * t;
+#pragma unroll
+    for (int i = 1; i < DS; ++i) {
+        t = x[i] - (double)half_bits_to_float(c[i]);
+        d = d + t * t;
+    }
+    return d;
+}
+
+// Lexicographic (distance, index) minimum over the wave; every lane gets it.
+__device__ __forceinline__ void wave_argmin(double& d, int& idx) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const double od = __shfl_xor(d, m, 64);
+        const int oi = __shfl_xor(idx, m, 64);
+        if (od < d || (od == d && oi < idx)) { d = od; idx = oi; }
+    }
+}
+
+__device__ __forceinline__ float wave_minf(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = fminf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// Per-book constants of the bound, and |c_e|^2 in fp32 (exact products,
+// DS - 1 additions): written by the whole block.
+template <int DS, int E>
+__device__ void book_norms(const uint16_t* book, float* cc, float* cmax2) {
+    __shared__ float red[2][32];
+    float m2 = 0.0f, m1 = 0.0f;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        float n2 = 0.0f, n1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < DS; ++i) {
+            const float c = half_bits_to_float(book[e * DS + i]);
+            n2 = n2 + c * c;
+            n1 = n1 + fabsf(c);
+        }
+        cc[e] = n2;
+        m2 = fmaxf(m2, n2);
+        m1 = fmaxf(m1, n1);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        m2 = fmaxf(m2, __shfl_xor(m2, m, 64));
+        m1 = fmaxf(m1, __shfl_xor(m1, m, 64));
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { red[0][w] = m2; red[1][w] = m1; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a2 = 0.0f, a1 = 0.0f;
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) { a2 = fmaxf(a2, red[0][i]); a1 = fmaxf(a1, red[1][i]); }
+        // fp32 rounding of the norms is far inside the bound's margin; round up anyway.
+        cmax2[0] = a2 * (1.0f + 0x1p-20f);
+        cmax2[1] = a1 * (1.0f + 0x1p-20f);
+    }
+    __syncthreads();
+}
+
+// The screen for one wave's set of 4 * NG points (A operands in lanes
+// 0 .. 4 NG - 1: lane p holds point p) over centroid groups cg = cg0,
+// cg0 + cgs, ...; per lane and point: best value m1 at centroid a1 (first
+// index on ties), second value m2.
+template <int DS, int E, int NG>
+__device__ __forceinline__ void screen_set(const half4_t (&ahi)[DS / 4], const half4_t (&alo)[DS / 4],
+                                           const uint16_t* book, const float* cc, int cg0, int cgs,
+                                           float (&m1)[4 * NG], float (&m2)[4 * NG], int (&a1)[4 * NG]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll 1
+    for (int cg = cg0; cg < E / 64; cg += cgs) {
+        const int e = cg * 64 + lane;
+        half4_t bq[DS / 4];
+#pragma unroll
+        for (int q = 0; q < DS / 4; ++q) bq[q] = *(const half4_t*)(book + e * DS + 4 * q);
+        const float c2 = cc[e];
+        static_for<0, NG>([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int q = 0; q < DS / 4; ++q) {
+                d = mfma_bcast<g>(ahi[q], bq[q], d);
+                d = mfma_bcast<g>(alo[q], bq[q], d);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pt = 4 * g + i;
+                const float v = __builtin_fmaf(-2.0f, d[i], c2);
+                if (v < m1[pt]) { m2[pt] = m1[pt]; m1[pt] = v; a1[pt] = e; }
+                else if (v < m2[pt]) m2[pt] = v;
+            }
+        });
+    }
+}
+
+// Builds the A operands of up to NP points (point p of x, DS doubles each,
+// for p < np) in lanes 0 .. NP - 1; flags points outside the fp16 range;
+// returns |x| of point (lane % NP).
+template <int DS, int NP>
+__device__ __forceinline__ double screen_operands(const double* x, int np, half4_t (&ahi)[DS / 4],
+                                                  half4_t (&alo)[DS / 4], bool& out_of_range) {
+    const int p = threadIdx.x & (NP - 1);
+    double n2 = 0.0;
+    out_of_range = false;
+#pragma unroll
+    for (int q = 0; q < DS / 4; ++q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double v = p < np ? x[p * DS + 4 * q + i] : 0.0;
+            n2 = n2 + v * v;
+            if (!(__builtin_fabs(v) < 32768.0)) out_of_range = true;
+            const _Float16 h = (_Float16)v;
+            ahi[q][i] = h;
+            alo[q][i] = (_Float16)(v - (double)h);
+        }
+    }
+    return __builtin_sqrt(n2);
+}
+
 // -------------------------------------------------------------- append kernel
 
 template <int FMT> struct AppendTile { static constexpr int TT = FMT == 0 ? 32 : 16; };
 
+// The screen's bound for a point of norm xn against a book with
+// (max |c|^2, max |c|_1) = cb.
+__device__ __forceinline__ double screen_tau(double xn, const float* cb) {
+    const double r = xn + __builtin_sqrt((double)cb[0]);
+    return 0x1p-18 * r * r + 0x1p-22 * (double)cb[1];
+}
+
+// Final code of point p of a wave's screened set (see the screen): the
+// candidates' exact distances, or the exact scan of the book on fallback.
+template <int DS, int E>
+__device__ __forceinline__ int refine_point(const double* xp, const uint16_t* book, double thr, bool fallback,
+                                            float m1, int a1) {
+    const int lane = threadIdx.x & 63;
+    double d;
+    int idx;
+    if (!fallback) {
+        const bool cand = (double)m1 <= thr;
+        d = cand ? dist_h<DS>(xp, book + a1 * DS) : __builtin_inf();
+        idx = cand ? a1 : 0x7fffffff;
+    } else {
+        d = __builtin_inf();
+        idx = lane;                                   // lowest index when nothing compares smaller
+        for (int e = lane; e < E; e += 64) {
+            const double dd = dist_h<DS>(xp, book + e * DS);
+            if (dd < d) { d = dd; idx = e; }
+        }
+    }
+    wave_argmin(d, idx);
+    return idx;
+}
+
+// Bulk quantization of a tile of TT positions of one (b, KV head) by the
+// screen: block of 1024 threads; the key rows are rotated in LDS, then for
+// keys and then values each wave screens sets of 4 points (token, sub-vector)
+// against the whole codebook and refines.  Used for the 1.5-bit format
+// (4096 entries), where it is 3x faster than the exact scan.
 template <int FMT>
-__global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(1024) void quantize_screen_kernel(AppendArgs a) {
+    using F = Fmt<FMT>;
+    constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
+    constexpr int TT = AppendTile<FMT>::TT;
+    constexpr int NWV = 16;
+    __shared__ __align__(16) uint16_t book[E * DS];   // one codebook at a time (K, then V)
+    __shared__ float cc[E];
+    __shared__ float cb[2];
+    __shared__ double x[TT * kHeadDim];
+    __shared__ uint16_t codes[2][TT * J];
+
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tile_base = (a.start_pos / TT + blockIdx.x) * TT;
+    const int lo = max(tile_base, a.start_pos);
+    const int hi = min(tile_base + TT, a.start_pos + a.n_new);
+    const int off = lo - tile_base;             // first valid row of the tile
+    const int nt = hi - lo;                     // >= 1
+    const int64_t stream = (int64_t)b * a.hkv + h;
+    const int64_t row0 = stream * a.n_new + (lo - a.start_pos);   // input row of position lo
+
+    // Keys: x = k / s, into LDS rows [off, off + nt), then the rotation.
+    const float* s = a.smooth + (int64_t)h * kHeadDim;
+    for (int idx = threadIdx.x; idx < nt * kHeadDim; idx += blockDim.x) {
+        const int r = idx / kHeadDim, c = idx % kHeadDim;
+        x[(off + r) * kHeadDim + c] = load_elem_d(a.k_new, (row0 + r) * kHeadDim + c, a.dtype) / (double)s[c];
+    }
+    __syncthreads();
+    block_fwht(x + off * kHeadDim, nt);
+
+    const int P = nt * J;                       // points per phase, contiguous from row off
+    for (int phase = 0; phase < 2; ++phase) {
+        if (phase == 1) {
+            for (int idx = threadIdx.x; idx < nt * kHeadDim; idx += blockDim.x) {
+                const int r = idx / kHeadDim, c = idx % kHeadDim;
+                x[(off + r) * kHeadDim + c] = load_elem_d(a.v_new, (row0 + r) * kHeadDim + c, a.dtype);
+            }
+        }
+        const uint4* src = (const uint4*)((phase == 0 ? a.k_book : a.v_book) + (int64_t)h * E * DS);
+        for (int i = threadIdx.x; i < E * DS / 8; i += blockDim.x) ((uint4*)book)[i] = src[i];
+        __syncthreads();
+        book_norms<DS, E>(book, cc, cb);
+        const double* xs = x + off * kHeadDim;
+        constexpr int NP = 4;                     // points per screened set
+        for (int base = wave * NP; base < P; base += NWV * NP) {
+            const int np = min(NP, P - base);
+            half4_t ahi[DS / 4], alo[DS / 4];
+            bool oor;
+            const double xn = screen_operands<DS, NP>(xs + base * DS, np, ahi, alo, oor);
+            float m1[NP], m2[NP];
+            int a1[NP];
+#pragma unroll
+            for (int q = 0; q < NP; ++q) { m1[q] = __builtin_inff(); m2[q] = __builtin_inff(); a1[q] = 0; }
+            screen_set<DS, E, NP / 4>(ahi, alo, book, cc, 0, 1, m1, m2, a1);
+            uint32_t fbmask = 0;
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+                if (q < np) {
+                    const float smin = wave_minf(m1[q]);
+                    const double xq = __shfl(xn, q, 64);
+                    const bool oq = __shfl((int)oor, q, 64) != 0;
+                    const double thr = (double)smin + 3.0 * screen_tau(xq, cb);
+                    const bool fb = oq || !(smin < __builtin_inff()) || __ballot((double)m2[q] <= thr) != 0;
+                    if (fb) {
+                        fbmask |= 1u << q;
+                    } else {
+                        const int code = refine_point<DS, E>(xs + (base + q) * DS, book, thr, false, m1[q], a1[q]);
+                        if (lane == 0) codes[phase][off * J + base + q] = (uint16_t)code;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);      // one point at a time: bounded registers
+            }
+            while (fbmask) {                         // wave-uniform
+                const int q = __builtin_ctz(fbmask);
+                fbmask &= fbmask - 1;
+                const int code = refine_point<DS, E>(xs + (base + q) * DS, book, 0.0, true, 0.0f, 0);
+                if (lane == 0) codes[phase][off * J + base + q] = (uint16_t)code;
+            }
+        }
+        __syncthreads();
+    }
+
+    // Write the codes of positions [lo, hi) in the cache layout.
+    uint8_t* kc = a.k_codes + stream * (int64_t)a.cap * W;
+    uint8_t* vc = a.v_codes + stream * (int64_t)a.cap * W;
+    if (FMT == 0) {
+        for (int idx = threadIdx.x; idx < nt * J; idx += blockDim.x) {
+            const int r = off + idx / J, j = idx % J;
+            const int64_t t = tile_base + r;
+            kc[t * W + j] = (uint8_t)codes[0][r * J + j];
+            vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[1][r * J + j];
+        }
+    } else {
+        // Keys: sub-vectors (2i, 2i+1) of a token share 3 bytes.
+        for (int idx = threadIdx.x; idx < nt * (J / 2); idx += blockDim.x) {
+            const int r = off + idx / (J / 2), i = idx % (J / 2);
+            const int64_t t = tile_base + r;
+            const uint32_t c0 = codes[0][r * J + 2 * i], c1 = codes[0][r * J + 2 * i + 1];
+            uint8_t* p = kc + t * W + 3 * i;
+            p[0] = (uint8_t)(c0 & 0xff);
+            p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
+            p[2] = (uint8_t)(c1 >> 4);
+        }
+        // Values: sub-vectors (j, j + 8) of a token share 3 bytes.
+        for (int idx = threadIdx.x; idx < nt * (J / 2); idx += blockDim.x) {
+            const int r = off + idx / (J / 2), j = idx % (J / 2);
+            const int64_t t = tile_base + r;
+            const uint32_t c0 = codes[1][r * J + j], c1 = codes[1][r * J + j + 8];
+            uint8_t* p = vc + v_pair_offset_1p5(t, j);
+            p[0] = (uint8_t)(c0 & 0xff);
+            p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
+            p[2] = (uint8_t)(c1 >> 4);
+        }
+    }
+}
+
+// Bulk quantization by the exact scan (fp64 distances to every entry, over
+// slices of the codebook): block of 256 threads per tile of TT positions.
+// Used for the 2-bit format, where 256 entries make the scan cheaper than
+// the screen's per-point reductions.
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
     using F = Fmt<FMT>;
     constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
     constexpr int TT = AppendTile<FMT>::TT;
@@ -257,13 +571,7 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
         double best = __builtin_inf();
         int idx = sl * EPS;
         for (int e = sl * EPS; e < (sl + 1) * EPS; ++e) {
-            double t = xs[0] - (double)half_bits_to_float(book[e * DS]);
-            double d = t * t;
-#pragma unroll
-            for (int i = 1; i < DS; ++i) {
-                t = xs[i] - (double)half_bits_to_float(book[e * DS + i]);
-                d = d + t * t;
-            }
+            const double d = dist_h<DS>(xs, book + e * DS);
             if (d < best) { best = d; idx = e; }
         }
         red_d[threadIdx.x] = best;
@@ -466,8 +774,8 @@ hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
         else hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
-    if (a.fmt == 0) hipLaunchKernelGGL(quantize_append_kernel<0>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(quantize_append_kernel<1>, grid, dim3(256), 0, stream, a);
+    if (a.fmt == 0) hipLaunchKernelGGL(quantize_exact_kernel<0>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(quantize_screen_kernel<1>, grid, dim3(1024), 0, stream, a);
     return hipGetLastError();
 }
 
