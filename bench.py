@@ -190,6 +190,8 @@ class Workload:
         torch.cuda.synchronize()
         step_ms = start.elapsed_time(end) / steps
         dec = sorted(a.elapsed_time(b) for a, b in evs)
+        self.decode_p10 = dec[int(0.1 * (len(dec) - 1))]
+        self.decode_p90 = dec[int(0.9 * (len(dec) - 1))]
         return step_ms, sum(dec) / len(dec), dec[len(dec) // 2]
 
     def time_attention_only(self, steps, warmup):
@@ -319,6 +321,8 @@ def measure(name, args, dev, with_bf16, with_cpu):
         "pct_hbm_peak": round(100 * wk.step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
         "decode_us": round(dec_ms * 1e3, 2),
         "decode_us_median": round(dec_med * 1e3, 2),
+        "decode_us_p10": round(wk.decode_p10 * 1e3, 2),
+        "decode_us_p90": round(wk.decode_p90 * 1e3, 2),
         "decode_GBps": round(wk.decode_bytes / (dec_ms * 1e-3) / 1e9, 1),
         "attention_us": round(attn_ms * 1e3, 2),
         "num_splits": wk.S,
