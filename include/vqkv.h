@@ -151,6 +151,17 @@ vqkv_status vqkv_quantize_append(const vqkv_shape* shape, const void* k_new, con
                                  const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes,
                                  void* stream);
 
+/* Ragged batches: one new token per sequence, sequence b's at position
+ * positions[b] (the codes it computes are those of vqkv_quantize_append).
+ *   k_new, v_new  device, [B][Hkv][1][128], dtype
+ *   positions     device, int32 [B], 4-byte aligned; a position outside
+ *                 [0, max_tokens) leaves that sequence's cache untouched
+ *   other arguments as for vqkv_quantize_append. */
+vqkv_status vqkv_quantize_append_varlen(const vqkv_shape* shape, const void* k_new, const void* v_new,
+                                        int32_t dtype, const int32_t* positions, const float* smooth,
+                                        const uint16_t* k_book, const uint16_t* v_book, uint8_t* k_codes,
+                                        uint8_t* v_codes, void* stream);
+
 /* Split-context decode attention over the codes.  VecInfer abstract: a kernel
  * that fuses dequantization into the attention computation to minimize memory
  * access.  For each (b, g) and split i of `num_splits` equal 64-aligned token
@@ -171,6 +182,25 @@ vqkv_status vqkv_decode_attention(const vqkv_shape* shape, const float* q_prime,
                                   const uint8_t* k_codes, const uint8_t* v_codes,
                                   int32_t seq_len, float sm_scale, int32_t num_splits,
                                   void* workspace, void* stream);
+
+/* Ragged batches: sequence b holds seq_lens[b] tokens.  The same computation
+ * as vqkv_decode_attention per sequence; every sequence is cut into the same
+ * num_splits ranges of ceil(max_seq_len / num_splits) tokens (64-aligned), so
+ * splits past a short sequence's end are empty (their lse is -inf and
+ * vqkv_combine skips them).  A sequence of length 0 gets a zero output.
+ *   seq_lens      device, int32 [B], 4-byte aligned; each value is clamped on
+ *                 the device to [0, max_tokens], so no value can make the
+ *                 kernel read outside the cache (values above max_seq_len are
+ *                 an error the caller must avoid: tokens past the last split
+ *                 would be ignored)
+ *   max_seq_len   host, 1 <= max_seq_len <= max_tokens, >= every seq_lens[b]
+ *   num_splits    host, 1 <= num_splits <= ceil(max_seq_len / 64)
+ *   other arguments as for vqkv_decode_attention. */
+vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* shape, const float* q_prime,
+                                         const uint16_t* k_book, const uint16_t* v_book,
+                                         const uint8_t* k_codes, const uint8_t* v_codes,
+                                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                         int32_t num_splits, void* workspace, void* stream);
 
 /* Log-sum-exp merge of the splits (split-context flash decoding):
  * out[b][g] = sum_i exp(lse_i - L) o_i, L = log sum_i exp(lse_i).

@@ -96,6 +96,23 @@ def test_append_argument_checks():
     assert call(0, 1, 0, k=None) == INVALID
 
 
+def test_varlen_argument_checks():
+    L = vq.lib()
+    sh = ctypes.byref(vq.make_shape(2, 32, 8, 1024, vq.FMT_2BIT))
+    call = lambda lens, mx, S, ws=FAKE: L.vqkv_decode_attention_varlen(sh, FAKE, FAKE, FAKE, FAKE, FAKE, lens, mx,
+                                                                      0.088, S, ws, None)
+    assert call(FAKE, 0, 1) == INVALID                   # empty maximum
+    assert call(FAKE, 1025, 1) == INVALID                # beyond capacity
+    assert call(None, 100, 1) == INVALID                 # no lengths
+    assert call(ctypes.c_void_p(FAKE.value + 2), 100, 1) == INVALID   # lengths not 4-byte aligned
+    assert call(FAKE, 100, 3) == INVALID                 # more splits than tiles of the longest
+    assert call(FAKE, 100, 1, ws=MISALIGNED) == INVALID
+    app = lambda pos, dt=0: L.vqkv_quantize_append_varlen(sh, FAKE, FAKE, dt, pos, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert app(None) == INVALID
+    assert app(ctypes.c_void_p(FAKE.value + 1)) == INVALID
+    assert app(FAKE, dt=4) == INVALID
+
+
 def test_transform_combine_and_calibration_checks():
     L = vq.lib()
     sh = ctypes.byref(vq.make_shape(1, 4, 1, 64, vq.FMT_2BIT))

@@ -336,6 +336,73 @@ def test_decode_matches_oracle(fmt, B, Hq, Hkv, T, S, path):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("fmt,Hq,Hkv", [(0, 8, 2), (1, 10, 2)])
+@pytest.mark.parametrize("S", [1, 5, 64])
+def test_decode_varlen_matches_oracle(fmt, Hq, Hkv, S):
+    """Ragged batch: each sequence its own length (1, a ragged tail, the longest,
+    and 0); the codes past a sequence's length belong to other data and must be
+    ignored; a zero-length sequence gives a zero output."""
+    lens = [1, 777, 4099, 0]
+    B, T = len(lens), max(lens)
+    say(f"decode varlen fmt{fmt} Hq{Hq} Hkv{Hkv} S{S} lens {lens}")
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, B, Hq, Hkv, T, 500 + fmt)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    vq.transform_query(shape, dev(q), dev(s), qp)
+    ws = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    vq.decode_attention_varlen(shape, qp, book_dev(kb), book_dev(vb), dev(kbytes), dev(vbytes), seq, T, S, ws)
+    vq.combine(shape, S, ws, out)
+    got = out.cpu().numpy()
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[b] == 0.0)
+            continue
+        ref = oracle.attention(fmt, q[b:b + 1], s, kb, vb, kc[b:b + 1, :, :L], vc[b:b + 1, :, :L])
+        err = rel_err(got[b:b + 1], ref)
+        print(f"  b={b} L={L} max relative error {err:.3e}", flush=True)
+        assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_append_varlen_bit_exact(fmt):
+    """One token per sequence at its own position (odd, even, block edges);
+    a position outside the cache leaves that sequence untouched; every other
+    byte keeps its sentinel."""
+    say(f"quantize_append varlen fmt{fmt}")
+    B, Hkv, cap = 4, 2, 192
+    positions = [0, 65, 130, cap]
+    case, s, kb, vb = _quant_case(fmt, B, Hkv, 1, "bf16", 70 + fmt)
+    kc_ref, vc_ref = _oracle_codes(fmt, case, s, kb, vb)
+    shape = vq.make_shape(B, Hkv, Hkv, cap, fmt)
+    W = vq.code_bytes_per_token(fmt)
+    sentinel = np.random.default_rng(4).integers(0, 256, (B, Hkv, cap * W), dtype=np.uint8)
+    kcodes, vcodes = dev(sentinel), dev(sentinel)
+    pos = torch.tensor(positions, dtype=torch.int32, device=DEV)
+    vq.quantize_append_varlen(shape, dev(case.k, torch.bfloat16), dev(case.v, torch.bfloat16), pos, dev(s),
+                              book_dev(kb), book_dev(vb), kcodes, vcodes)
+    torch.cuda.synchronize()
+    gk, gv = kcodes.cpu().numpy(), vcodes.cpu().numpy()
+    for b, t in enumerate(positions):
+        for h in range(Hkv):
+            if t >= cap:
+                assert np.array_equal(gk[b, h], sentinel[b, h]) and np.array_equal(gv[b, h], sentinel[b, h])
+                continue
+            # Expected: the sentinel with this token's codes packed at position t.
+            J = kc_ref.shape[-1]
+            full_k = oracle.unpack_k(fmt, sentinel[b, h], cap)
+            full_v = oracle.unpack_v(fmt, sentinel[b, h], cap)
+            full_k[t] = kc_ref[b, h, 0]
+            full_v[t] = vc_ref[b, h, 0]
+            expect_k = oracle.pack_k(fmt, full_k, cap, sentinel[b, h].copy())
+            expect_v = oracle.pack_v(fmt, full_v, cap, sentinel[b, h].copy())
+            assert np.array_equal(gk[b, h], expect_k), (b, h)
+            assert np.array_equal(gv[b, h], expect_v), (b, h)
+            assert J > 0
+
+
 def test_decode_single_token_returns_its_value():
     say("decode T=1")
     q, s, kb, vb, kc, vc, cap = _attn_inputs(0, 1, 8, 2, 1, 77, cap=128)

@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         "vqkv_quantize_append": (I32, [SP, P, P, I32, I32, I32, P, P, P, P, P, P]),
         "vqkv_decode_attention": (I32, [SP, P, P, P, P, P, I32, F32, I32, P, P]),
         "vqkv_combine": (I32, [SP, I32, P, P, P]),
+        "vqkv_decode_attention_varlen": (I32, [SP, P, P, P, P, P, P, I32, F32, I32, P, P]),
+        "vqkv_quantize_append_varlen": (I32, [SP, P, P, I32, P, P, P, P, P, P, P]),
         "vqkv_smooth_scales": (I32, [I32, I32, P, I32, P, P]),
         "vqkv_train_workspace_bytes": (SZ, [I32, I32]),
         "vqkv_train_codebook": (I32, [I32, I32, P, I32, I32, P, P, I32, P, P, P, P]),
@@ -160,6 +162,31 @@ def decode_attention(shape: Shape, q_prime, k_book, v_book, k_codes, v_codes, se
     _check(lib().vqkv_decode_attention(ctypes.byref(shape), _ptr(q_prime), _ptr(k_book), _ptr(v_book),
                                        _ptr(k_codes), _ptr(v_codes), seq_len, sm_scale, num_splits,
                                        _ptr(workspace), _stream(q_prime)))
+
+
+def decode_attention_varlen(shape: Shape, q_prime, k_book, v_book, k_codes, v_codes, seq_lens, max_seq_len: int,
+                            num_splits: int, workspace, sm_scale: float | None = None) -> None:
+    """Ragged batch: sequence b holds seq_lens[b] tokens (int32 device tensor [B])."""
+    import torch
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    _check(lib().vqkv_decode_attention_varlen(ctypes.byref(shape), _ptr(q_prime), _ptr(k_book), _ptr(v_book),
+                                              _ptr(k_codes), _ptr(v_codes), _ptr(seq_lens), max_seq_len, sm_scale,
+                                              num_splits, _ptr(workspace), _stream(q_prime)))
+
+
+def quantize_append_varlen(shape: Shape, k_new, v_new, positions, smooth, k_book, v_book, k_codes, v_codes) -> None:
+    """One new token per sequence [B][Hkv][1][128], sequence b's at positions[b] (int32 device tensor)."""
+    import torch
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype or k_new.shape[2] != 1:
+        raise ValueError("k_new and v_new must both be [B][Hkv][1][128] of one dtype")
+    if positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    _check(lib().vqkv_quantize_append_varlen(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                             _ptr(positions), _ptr(smooth), _ptr(k_book), _ptr(v_book),
+                                             _ptr(k_codes), _ptr(v_codes), _stream(k_new)))
 
 
 def combine(shape: Shape, num_splits: int, workspace, out) -> None:

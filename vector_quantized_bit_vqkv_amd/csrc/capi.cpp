@@ -175,6 +175,25 @@ vqkv_status vqkv_quantize_append(const vqkv_shape* s, const void* k_new, const v
     return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append launch");
 }
 
+vqkv_status vqkv_quantize_append_varlen(const vqkv_shape* s, const void* k_new, const void* v_new, int32_t dtype,
+                                        const int32_t* positions, const float* smooth, const uint16_t* k_book,
+                                        const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, void* stream) {
+    VQKV_CHECK(check_shape(s, true));
+    VQKV_CHECK(check_dtype(dtype));
+    if (!positions) return fail(VQKV_ERR_INVALID_ARG, "positions is NULL");
+    if ((uintptr_t)positions & 3) return fail(VQKV_ERR_INVALID_ARG, "positions is not 4-byte aligned");
+    VQKV_CHECK(check_ptr(k_new, "k_new"));
+    VQKV_CHECK(check_ptr(v_new, "v_new"));
+    VQKV_CHECK(check_ptr(smooth, "smooth"));
+    VQKV_CHECK(check_ptr(k_book, "k_book"));
+    VQKV_CHECK(check_ptr(v_book, "v_book"));
+    VQKV_CHECK(check_ptr(k_codes, "k_codes"));
+    VQKV_CHECK(check_ptr(v_codes, "v_codes"));
+    vqkv::AppendArgs a{k_new, v_new, dtype, 1, 0, smooth, k_book, v_book, k_codes, v_codes,
+                       s->batch, s->num_kv_heads, s->max_tokens, s->fmt, positions};
+    return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append_varlen launch");
+}
+
 vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
                                   const uint16_t* v_book, const uint8_t* k_codes, const uint8_t* v_codes,
                                   int32_t seq_len, float sm_scale, int32_t num_splits, void* workspace,
@@ -204,6 +223,39 @@ vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, con
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), path};
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention launch");
+}
+
+vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
+                                         const uint16_t* v_book, const uint8_t* k_codes, const uint8_t* v_codes,
+                                         const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                         int32_t num_splits, void* workspace, void* stream) {
+    VQKV_CHECK(check_shape(s, true));
+    if (max_seq_len < 1 || max_seq_len > s->max_tokens)
+        return fail(VQKV_ERR_INVALID_ARG, "max_seq_len %d outside [1, max_tokens = %d]", max_seq_len, s->max_tokens);
+    if (!seq_lens) return fail(VQKV_ERR_INVALID_ARG, "seq_lens is NULL");
+    if ((uintptr_t)seq_lens & 3) return fail(VQKV_ERR_INVALID_ARG, "seq_lens is not 4-byte aligned");
+    if (!std::isfinite(sm_scale)) return fail(VQKV_ERR_INVALID_ARG, "sm_scale is not finite");
+    if (num_splits < 1 || num_splits > ceil_div(max_seq_len, 64))
+        return fail(VQKV_ERR_INVALID_ARG, "num_splits %d outside [1, ceil(max_seq_len / 64) = %lld]", num_splits,
+                    (long long)ceil_div(max_seq_len, 64));
+    VQKV_CHECK(check_ptr(q_prime, "q_prime"));
+    VQKV_CHECK(check_ptr(k_book, "k_book"));
+    VQKV_CHECK(check_ptr(v_book, "v_book"));
+    VQKV_CHECK(check_ptr(k_codes, "k_codes"));
+    VQKV_CHECK(check_ptr(v_codes, "v_codes"));
+    VQKV_CHECK(check_ptr(workspace, "workspace"));
+    const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
+    float* part_o = (float*)workspace;
+    float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
+    const int path = decode_path_from_env();
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if (path == 1 && !(s->fmt == VQKV_FMT_2BIT && G <= 4))
+        return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
+    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
+                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
+                       max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
+                       (float)((double)sm_scale * 1.4426950408889634), path, seq_lens};
+    return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention_varlen launch");
 }
 
 vqkv_status vqkv_combine(const vqkv_shape* s, int32_t num_splits, const void* workspace, float* out, void* stream) {

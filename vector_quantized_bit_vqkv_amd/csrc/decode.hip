@@ -33,6 +33,15 @@ namespace vqkv {
 
 namespace {
 
+// Context length of sequence b: the uniform seq_len, or the caller's
+// per-sequence length clamped to [0, capacity] (an out-of-range length can
+// never make a kernel read outside the cache).
+__device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int b) {
+    if (!a.seq_lens) return a.seq_len;
+    const int n = a.seq_lens[b];
+    return n < 0 ? 0 : (n > a.cap ? a.cap : n);
+}
+
 // Bytes of the per-(b, h) code stream per token.
 template <int FMT> struct DFmt;
 template <> struct DFmt<0> { static constexpr int E = 256, DS = 4, J = 32, W = 32; };
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t_begin = s * a.chunk;
-    const int t_end = min(a.seq_len, t_begin + a.chunk);
+    const int t_end = min(seq_len_of(a, b), t_begin + a.chunk);
 
     {
         const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * E * 4);
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t_begin = s * a.chunk;
-    const int t_end = min(a.seq_len, t_begin + a.chunk);
+    const int t_end = min(seq_len_of(a, b), t_begin + a.chunk);
 
     if constexpr (FMT == 0) {
         const uint2* kb = (const uint2*)(a.k_book + (int64_t)h * 256 * 4);
@@ -676,7 +685,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t_begin = s * a.chunk;
-    const int t_end = min(a.seq_len, t_begin + a.chunk);
+    const int t_end = min(seq_len_of(a, b), t_begin + a.chunk);
 
     {
         const uint4* kb = (const uint4*)(a.k_book + (int64_t)h * E * DS);

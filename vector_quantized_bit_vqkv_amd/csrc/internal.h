@@ -49,6 +49,7 @@ struct AppendArgs {
     uint8_t* k_codes;       // [B][Hkv][cap * W]
     uint8_t* v_codes;
     int batch, hkv, cap, fmt;
+    const int32_t* positions;  // device [B] or null: one token per sequence at its own position
 };
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream);
 
@@ -64,6 +65,7 @@ struct DecodeArgs {
     int seq_len, splits, chunk;
     float qscale;           // sm_scale * log2(e)
     int path;               // 0 auto, 1 score table (2-bit), 2 gather, 3 matrix cores (2-bit)
+    const int32_t* seq_lens;   // device [B] or null (then seq_len for every sequence)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -539,6 +539,10 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
 
     const int ph = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t stream = (int64_t)b * a.hkv + h;
+    // Position of the token: uniform, or per sequence (a position outside the
+    // cache is skipped, block-uniformly, so nothing is written out of bounds).
+    const int64_t t = a.positions ? (int64_t)a.positions[b] : (int64_t)a.start_pos;
+    if (t < 0 || t >= a.cap) return;
     {
         const uint4* src = (const uint4*)((ph == 0 ? a.k_book : a.v_book) + (int64_t)h * E * DS);
         for (int i = threadIdx.x; i < E * DS / 8; i += NT) ((uint4*)book)[i] = src[i];
@@ -587,7 +591,6 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
         codes[j] = (uint16_t)idx;
     }
     __syncthreads();
-    const int64_t t = a.start_pos;
     if (FMT == 0) {
         if (threadIdx.x < J) {
             const int j = threadIdx.x;
@@ -768,7 +771,7 @@ hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
     const int TT = a.fmt == 0 ? AppendTile<0>::TT : AppendTile<1>::TT;
     const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
     const dim3 grid(last - first + 1, a.hkv, a.batch);
-    if (a.n_new == 1) {
+    if (a.n_new == 1 || a.positions) {
         const dim3 g1(2, a.hkv, a.batch);
         if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(1024), 0, stream, a);
         else hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
