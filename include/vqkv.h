@@ -202,6 +202,32 @@ vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* shape, const float* q
                                          const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                                          int32_t num_splits, void* workspace, void* stream);
 
+/* Paged caches: the codes of each (b, KV head) stream live in 64-token blocks
+ * of a shared pool, block_table naming the pool block of each logical block
+ * (the 64-token blocks of the cache layout above, each 64 * W bytes).  Same
+ * computation and arguments as vqkv_decode_attention_varlen, with
+ *   k_pool, v_pool  device, [num_blocks][64 * W] bytes each
+ *   num_blocks      host, >= 1
+ *   block_table     device, int32 [B][Hkv][max_tokens / 64], 4-byte aligned;
+ *                   entries are clamped to [0, num_blocks) on the device
+ * Runs on the matrix-core kernel only (a measurement override to another
+ * kernel returns VQKV_ERR_UNSUPPORTED). */
+vqkv_status vqkv_decode_attention_paged(const vqkv_shape* shape, const float* q_prime,
+                                        const uint16_t* k_book, const uint16_t* v_book,
+                                        const uint8_t* k_pool, const uint8_t* v_pool, int32_t num_blocks,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        int32_t max_seq_len, float sm_scale, int32_t num_splits,
+                                        void* workspace, void* stream);
+
+/* Paged caches: one new token per sequence at positions[b] (as
+ * vqkv_quantize_append_varlen), written into the pool block the table names
+ * for its logical block.  Pool and table as for vqkv_decode_attention_paged. */
+vqkv_status vqkv_quantize_append_paged(const vqkv_shape* shape, const void* k_new, const void* v_new,
+                                       int32_t dtype, const int32_t* positions, const float* smooth,
+                                       const uint16_t* k_book, const uint16_t* v_book, uint8_t* k_pool,
+                                       uint8_t* v_pool, int32_t num_blocks, const int32_t* block_table,
+                                       void* stream);
+
 /* Log-sum-exp merge of the splits (split-context flash decoding):
  * out[b][g] = sum_i exp(lse_i - L) o_i, L = log sum_i exp(lse_i).
  *   workspace   device, as written by vqkv_decode_attention with the same

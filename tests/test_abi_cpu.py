@@ -113,6 +113,23 @@ def test_varlen_argument_checks():
     assert app(FAKE, dt=4) == INVALID
 
 
+def test_paged_argument_checks():
+    L = vq.lib()
+    sh = ctypes.byref(vq.make_shape(2, 32, 8, 1024, vq.FMT_2BIT))
+    dec = lambda nb, tab, lens=FAKE, mx=100: L.vqkv_decode_attention_paged(sh, FAKE, FAKE, FAKE, FAKE, FAKE, nb, tab,
+                                                                           lens, mx, 0.088, 1, FAKE, None)
+    assert dec(0, FAKE) == INVALID                      # empty pool
+    assert dec(4, None) == INVALID                      # no table
+    assert dec(4, ctypes.c_void_p(FAKE.value + 2)) == INVALID
+    assert dec(4, FAKE, lens=None) == INVALID
+    assert dec(4, FAKE, mx=2000) == INVALID
+    app = lambda nb, tab, pos=FAKE: L.vqkv_quantize_append_paged(sh, FAKE, FAKE, 0, pos, FAKE, FAKE, FAKE, FAKE,
+                                                                 FAKE, nb, tab, None)
+    assert app(0, FAKE) == INVALID
+    assert app(4, None) == INVALID
+    assert app(4, FAKE, pos=None) == INVALID
+
+
 def test_transform_combine_and_calibration_checks():
     L = vq.lib()
     sh = ctypes.byref(vq.make_shape(1, 4, 1, 64, vq.FMT_2BIT))

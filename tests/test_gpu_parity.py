@@ -403,6 +403,81 @@ def test_quantize_append_varlen_bit_exact(fmt):
             assert J > 0
 
 
+def _paged_pool(kbytes, vbytes, W, seed, spare=3):
+    """Scatter the 64-token blocks of contiguous streams [B][Hkv][cap * W] into a
+    shuffled pool with a few unused blocks; returns pools and the block table."""
+    B, H, n = kbytes.shape
+    nb = n // (64 * W)
+    total = B * H * nb + spare
+    perm = np.random.default_rng(seed).permutation(total)[:B * H * nb].reshape(B, H, nb).astype(np.int32)
+    kpool = np.random.default_rng(seed + 1).integers(0, 256, (total, 64 * W), dtype=np.uint8)
+    vpool = kpool.copy()
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                kpool[perm[b, h, i]] = kbytes[b, h, i * 64 * W:(i + 1) * 64 * W]
+                vpool[perm[b, h, i]] = vbytes[b, h, i * 64 * W:(i + 1) * 64 * W]
+    return kpool, vpool, perm
+
+
+@pytest.mark.parametrize("fmt,Hq,Hkv", [(0, 8, 2), (1, 10, 2)])
+@pytest.mark.parametrize("S", [1, 7])
+def test_decode_paged_equals_contiguous(fmt, Hq, Hkv, S):
+    """A cache scattered over a shuffled block pool gives bitwise the same output
+    as the contiguous cache (same arithmetic in the same order)."""
+    lens = [1000, 700]
+    B, T = len(lens), max(lens)
+    say(f"decode paged fmt{fmt} S{S}")
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, B, Hq, Hkv, T, 600 + fmt)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    W = vq.code_bytes_per_token(fmt)
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    kpool, vpool, table = _paged_pool(kbytes, vbytes, W, 9)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    vq.transform_query(shape, dev(q), dev(s), qp)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ws = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+    outs = []
+    for paged in (False, True):
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+        if paged:
+            vq.decode_attention_paged(shape, qp, book_dev(kb), book_dev(vb), dev(kpool), dev(vpool),
+                                      torch.from_numpy(table).to(DEV), seq, T, S, ws)
+        else:
+            vq.decode_attention_varlen(shape, qp, book_dev(kb), book_dev(vb), dev(kbytes), dev(vbytes), seq, T, S, ws)
+        vq.combine(shape, S, ws, out)
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    ref = oracle.attention(fmt, q[1:2], s, kb, vb, kc[1:2, :, :700], vc[1:2, :, :700])
+    assert rel_err(outs[1][1:2], ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_append_paged_bit_exact(fmt):
+    """One token per sequence into a paged cache lands in the pool block its table
+    names, byte for byte as in the contiguous cache; other pool bytes untouched."""
+    say(f"quantize_append paged fmt{fmt}")
+    B, Hkv, cap = 3, 2, 192
+    positions = [5, 64 + 33, 191]
+    case, s, kb, vb = _quant_case(fmt, B, Hkv, 1, "bf16", 80 + fmt)
+    shape = vq.make_shape(B, Hkv, Hkv, cap, fmt)
+    W = vq.code_bytes_per_token(fmt)
+    base = np.random.default_rng(6).integers(0, 256, (B, Hkv, cap * W), dtype=np.uint8)
+    kpool, vpool, table = _paged_pool(base, base, W, 12)
+    kc_c, vc_c = dev(base), dev(base)
+    kp, vp = dev(kpool), dev(vpool)
+    pos = torch.tensor(positions, dtype=torch.int32, device=DEV)
+    k_new, v_new = dev(case.k, torch.bfloat16), dev(case.v, torch.bfloat16)
+    vq.quantize_append_varlen(shape, k_new, v_new, pos, dev(s), book_dev(kb), book_dev(vb), kc_c, vc_c)
+    vq.quantize_append_paged(shape, k_new, v_new, pos, dev(s), book_dev(kb), book_dev(vb), kp, vp,
+                             torch.from_numpy(table).to(DEV))
+    torch.cuda.synchronize()
+    want_k, want_v, _ = _paged_pool(kc_c.cpu().numpy(), vc_c.cpu().numpy(), W, 12)
+    assert np.array_equal(kp.cpu().numpy(), want_k)
+    assert np.array_equal(vp.cpu().numpy(), want_v)
+    assert not np.array_equal(kc_c.cpu().numpy(), base)            # the appends did write
+
+
 def test_decode_single_token_returns_its_value():
     say("decode T=1")
     q, s, kb, vb, kc, vc, cap = _attn_inputs(0, 1, 8, 2, 1, 77, cap=128)

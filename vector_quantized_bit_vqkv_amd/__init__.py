@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         "vqkv_combine": (I32, [SP, I32, P, P, P]),
         "vqkv_decode_attention_varlen": (I32, [SP, P, P, P, P, P, P, I32, F32, I32, P, P]),
         "vqkv_quantize_append_varlen": (I32, [SP, P, P, I32, P, P, P, P, P, P, P]),
+        "vqkv_decode_attention_paged": (I32, [SP, P, P, P, P, P, I32, P, P, I32, F32, I32, P, P]),
+        "vqkv_quantize_append_paged": (I32, [SP, P, P, I32, P, P, P, P, P, P, I32, P, P]),
         "vqkv_smooth_scales": (I32, [I32, I32, P, I32, P, P]),
         "vqkv_train_workspace_bytes": (SZ, [I32, I32]),
         "vqkv_train_codebook": (I32, [I32, I32, P, I32, I32, P, P, I32, P, P, P, P]),
@@ -187,6 +189,40 @@ def quantize_append_varlen(shape: Shape, k_new, v_new, positions, smooth, k_book
     _check(lib().vqkv_quantize_append_varlen(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
                                              _ptr(positions), _ptr(smooth), _ptr(k_book), _ptr(v_book),
                                              _ptr(k_codes), _ptr(v_codes), _stream(k_new)))
+
+
+def decode_attention_paged(shape: Shape, q_prime, k_book, v_book, k_pool, v_pool, block_table, seq_lens,
+                           max_seq_len: int, num_splits: int, workspace, sm_scale: float | None = None) -> None:
+    """Paged cache: pools [num_blocks][64 * W] bytes, block_table int32 [B][Hkv][max_tokens / 64]."""
+    import torch
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    W = code_bytes_per_token(shape.fmt)
+    num_blocks = k_pool.numel() // (64 * W)
+    if v_pool.numel() // (64 * W) != num_blocks:
+        raise ValueError("k_pool and v_pool must hold the same number of blocks")
+    _check(lib().vqkv_decode_attention_paged(ctypes.byref(shape), _ptr(q_prime), _ptr(k_book), _ptr(v_book),
+                                             _ptr(k_pool), _ptr(v_pool), num_blocks, _ptr(block_table),
+                                             _ptr(seq_lens), max_seq_len, sm_scale, num_splits, _ptr(workspace),
+                                             _stream(q_prime)))
+
+
+def quantize_append_paged(shape: Shape, k_new, v_new, positions, smooth, k_book, v_book, k_pool, v_pool,
+                          block_table) -> None:
+    """One new token per sequence into a paged cache (see decode_attention_paged)."""
+    import torch
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype or k_new.shape[2] != 1:
+        raise ValueError("k_new and v_new must both be [B][Hkv][1][128] of one dtype")
+    if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("positions and block_table must be int32")
+    W = code_bytes_per_token(shape.fmt)
+    num_blocks = k_pool.numel() // (64 * W)
+    _check(lib().vqkv_quantize_append_paged(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                            _ptr(positions), _ptr(smooth), _ptr(k_book), _ptr(v_book),
+                                            _ptr(k_pool), _ptr(v_pool), num_blocks, _ptr(block_table),
+                                            _stream(k_new)))
 
 
 def combine(shape: Shape, num_splits: int, workspace, out) -> None:

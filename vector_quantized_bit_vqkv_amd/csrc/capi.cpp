@@ -194,6 +194,29 @@ vqkv_status vqkv_quantize_append_varlen(const vqkv_shape* s, const void* k_new, 
     return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append_varlen launch");
 }
 
+vqkv_status vqkv_quantize_append_paged(const vqkv_shape* s, const void* k_new, const void* v_new, int32_t dtype,
+                                       const int32_t* positions, const float* smooth, const uint16_t* k_book,
+                                       const uint16_t* v_book, uint8_t* k_pool, uint8_t* v_pool, int32_t num_blocks,
+                                       const int32_t* block_table, void* stream) {
+    VQKV_CHECK(check_shape(s, true));
+    VQKV_CHECK(check_dtype(dtype));
+    if (num_blocks < 1) return fail(VQKV_ERR_INVALID_ARG, "num_blocks %d < 1", num_blocks);
+    if (!block_table) return fail(VQKV_ERR_INVALID_ARG, "block_table is NULL");
+    if ((uintptr_t)block_table & 3) return fail(VQKV_ERR_INVALID_ARG, "block_table is not 4-byte aligned");
+    if (!positions) return fail(VQKV_ERR_INVALID_ARG, "positions is NULL");
+    if ((uintptr_t)positions & 3) return fail(VQKV_ERR_INVALID_ARG, "positions is not 4-byte aligned");
+    VQKV_CHECK(check_ptr(k_new, "k_new"));
+    VQKV_CHECK(check_ptr(v_new, "v_new"));
+    VQKV_CHECK(check_ptr(smooth, "smooth"));
+    VQKV_CHECK(check_ptr(k_book, "k_book"));
+    VQKV_CHECK(check_ptr(v_book, "v_book"));
+    VQKV_CHECK(check_ptr(k_pool, "k_pool"));
+    VQKV_CHECK(check_ptr(v_pool, "v_pool"));
+    vqkv::AppendArgs a{k_new, v_new, dtype, 1, 0, smooth, k_book, v_book, k_pool, v_pool,
+                       s->batch, s->num_kv_heads, s->max_tokens, s->fmt, positions, block_table, num_blocks};
+    return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append_paged launch");
+}
+
 vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
                                   const uint16_t* v_book, const uint8_t* k_codes, const uint8_t* v_codes,
                                   int32_t seq_len, float sm_scale, int32_t num_splits, void* workspace,
@@ -256,6 +279,41 @@ vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* s, const float* q_pri
                        max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), path, seq_lens};
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention_varlen launch");
+}
+
+vqkv_status vqkv_decode_attention_paged(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
+                                        const uint16_t* v_book, const uint8_t* k_pool, const uint8_t* v_pool,
+                                        int32_t num_blocks, const int32_t* block_table, const int32_t* seq_lens,
+                                        int32_t max_seq_len, float sm_scale, int32_t num_splits, void* workspace,
+                                        void* stream) {
+    VQKV_CHECK(check_shape(s, true));
+    if (num_blocks < 1) return fail(VQKV_ERR_INVALID_ARG, "num_blocks %d < 1", num_blocks);
+    if (!block_table) return fail(VQKV_ERR_INVALID_ARG, "block_table is NULL");
+    if ((uintptr_t)block_table & 3) return fail(VQKV_ERR_INVALID_ARG, "block_table is not 4-byte aligned");
+    if (max_seq_len < 1 || max_seq_len > s->max_tokens)
+        return fail(VQKV_ERR_INVALID_ARG, "max_seq_len %d outside [1, max_tokens = %d]", max_seq_len, s->max_tokens);
+    if (!seq_lens) return fail(VQKV_ERR_INVALID_ARG, "seq_lens is NULL");
+    if ((uintptr_t)seq_lens & 3) return fail(VQKV_ERR_INVALID_ARG, "seq_lens is not 4-byte aligned");
+    if (!std::isfinite(sm_scale)) return fail(VQKV_ERR_INVALID_ARG, "sm_scale is not finite");
+    if (num_splits < 1 || num_splits > ceil_div(max_seq_len, 64))
+        return fail(VQKV_ERR_INVALID_ARG, "num_splits %d outside [1, ceil(max_seq_len / 64) = %lld]", num_splits,
+                    (long long)ceil_div(max_seq_len, 64));
+    VQKV_CHECK(check_ptr(q_prime, "q_prime"));
+    VQKV_CHECK(check_ptr(k_book, "k_book"));
+    VQKV_CHECK(check_ptr(v_book, "v_book"));
+    VQKV_CHECK(check_ptr(k_pool, "k_pool"));
+    VQKV_CHECK(check_ptr(v_pool, "v_pool"));
+    VQKV_CHECK(check_ptr(workspace, "workspace"));
+    if (decode_path_from_env() != 0)
+        return fail(VQKV_ERR_UNSUPPORTED, "paged caches run on the matrix-core kernel only");
+    const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
+    float* part_o = (float*)workspace;
+    float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
+    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_pool, v_pool, part_o, part_lse,
+                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
+                       max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
+                       (float)((double)sm_scale * 1.4426950408889634), 0, seq_lens, block_table, num_blocks};
+    return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention_paged launch");
 }
 
 vqkv_status vqkv_combine(const vqkv_shape* s, int32_t num_splits, const void* workspace, float* out, void* stream) {

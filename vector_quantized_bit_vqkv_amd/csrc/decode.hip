@@ -387,7 +387,7 @@ __device__ __forceinline__ uint32_t bytes3_at(const uint32_t (&w)[N]) {
 // copies (2 x 64 KB).  Key codes are 24 bytes per token; value codes come in
 // 48-byte streams, one per lane pair, 16 pairs (sub-vectors j, j + 8) in step
 // order.
-template <int FMT, int G, int NW>
+template <int FMT, int G, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int HB = (G + 3) / 4;
     constexpr int PT_BYTES = NW * HB * 512;
@@ -448,8 +448,21 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         o[hb][0] = o[hb][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
     const int64_t stream = (int64_t)b * a.hkv + h;
-    const uint8_t* kbase = a.k_codes + stream * (int64_t)a.cap * W;
-    const uint8_t* vbase = a.v_codes + stream * (int64_t)a.cap * W;
+    // Codes of tile tl (64 tokens, one block) start at byte toff(tl) of the
+    // stream, or, paged, of the pool at the block the table names (clamped to
+    // the pool, so no table entry can make the kernel read outside it).
+    const uint8_t* kbase = PAGED ? a.k_codes : a.k_codes + stream * (int64_t)a.cap * W;
+    const uint8_t* vbase = PAGED ? a.v_codes : a.v_codes + stream * (int64_t)a.cap * W;
+    const int32_t* btab = PAGED ? a.block_table + stream * (int64_t)(a.cap >> 6) : nullptr;
+    auto toff = [&](int tl) -> int64_t {
+        if constexpr (!PAGED) {
+            return (int64_t)tl * W;
+        } else {
+            int blk = btab[tl >> 6];
+            blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+            return (int64_t)blk * (64 * W);
+        }
+    };
     // 2-bit: 32 copies, lane l reads copy l % 32; the value book starts at 64 KB.
     // 1.5-bit: value lookups read half e = lane % 2 of the entry.
     const uint32_t kofs = FMT == 0 ? (uint32_t)(lane & 31) * 8 : 0u;
@@ -469,29 +482,31 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // bytes (3 x 8) of keys, 48 bytes (3 x 16) of values from stream
     // 8 (lane / 16) + 2 ((lane / 4) % 4) + (lane / 2) % 2 of the block.
     const int vstream = 8 * (lane >> 4) + 2 * ((lane >> 2) & 3) + ((lane >> 1) & 1);
-    const uint4* kc0 = (const uint4*)(kbase + (int64_t)lane * 32);
-    const uint4* vc0 = (const uint4*)(vbase + (int64_t)lane * 32);
-    const uint2* kc1 = (const uint2*)(kbase + (int64_t)lane * 24);
-    const uint4* vc1 = (const uint4*)(vbase + (int64_t)vstream * 48);
+    const uint8_t* kl0 = kbase + lane * 32;
+    const uint8_t* vl0 = vbase + lane * 32;
+    const uint8_t* kl1 = kbase + lane * 24;
+    const uint8_t* vl1 = vbase + vstream * 48;
     uint4 ck0, ck1, cv0, cv1;                               // 2-bit
     uint2 dk[3];                                            // 1.5-bit
     uint4 dv[3];
     auto load_k = [&](int tl) {
         if constexpr (FMT == 0) {
-            ck0 = kc0[(int64_t)tl * 2];
-            ck1 = kc0[(int64_t)tl * 2 + 1];
+            const int64_t o = toff(tl);
+            ck0 = *(const uint4*)(kl0 + o);
+            ck1 = *(const uint4*)(kl0 + o + 16);
         } else {
 #pragma unroll
-            for (int i = 0; i < 3; ++i) dk[i] = kc1[(int64_t)tl * 3 + i];
+            for (int i = 0; i < 3; ++i) dk[i] = *(const uint2*)(kl1 + toff(tl) + 8 * i);
         }
     };
     auto load_v = [&](int tl) {
         if constexpr (FMT == 0) {
-            cv0 = vc0[(int64_t)tl * 2];
-            cv1 = vc0[(int64_t)tl * 2 + 1];
+            const int64_t o = toff(tl);
+            cv0 = *(const uint4*)(vl0 + o);
+            cv1 = *(const uint4*)(vl0 + o + 16);
         } else {
 #pragma unroll
-            for (int i = 0; i < 3; ++i) dv[i] = vc1[(int64_t)tl * 3 / 2 + i];   // tl * 24 bytes
+            for (int i = 0; i < 3; ++i) dv[i] = *(const uint4*)(vl1 + toff(tl) + 16 * i);
         }
     };
     if (first < t_end) {
@@ -520,8 +535,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                     for (int hb = 0; hb < HB; ++hb) sacc[hb] = mfma_bcast<jj>(qa[hb][half], kv, sacc[hb]);
                 });
                 __builtin_amdgcn_sched_barrier(0);
-                if (half == 0) ck0 = kc0[(int64_t)nxt * 2];
-                else ck1 = kc0[(int64_t)nxt * 2 + 1];
+                if (half == 0) ck0 = *(const uint4*)(kl0 + toff(nxt));
+                else ck1 = *(const uint4*)(kl0 + toff(nxt) + 16);
             }
         } else {
             // Scores: 16 sub-vectors in 8 pairs; each 16-byte entry feeds the
@@ -598,8 +613,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                     }
                 });
                 __builtin_amdgcn_sched_barrier(0);
-                if (hv == 0) cv0 = vc0[(int64_t)nxt * 2];
-                else cv1 = vc0[(int64_t)nxt * 2 + 1];
+                if (hv == 0) cv0 = *(const uint4*)(vl0 + toff(nxt));
+                else cv1 = *(const uint4*)(vl0 + toff(nxt) + 16);
             }
         } else {
             // Values: step st takes pair st of the lane's stream (bytes 3 st..).
@@ -627,10 +642,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         uint4 bk0, bk1, bv0, bv1;
         if (first < t_end) {
             const int second = first + kStride < t_end ? first + kStride : first;
-            bk0 = kc0[(int64_t)second * 2];
-            bk1 = kc0[(int64_t)second * 2 + 1];
-            bv0 = vc0[(int64_t)second * 2];
-            bv1 = vc0[(int64_t)second * 2 + 1];
+            const int64_t o = toff(second);
+            bk0 = *(const uint4*)(kl0 + o);
+            bk1 = *(const uint4*)(kl0 + o + 16);
+            bv0 = *(const uint4*)(vl0 + o);
+            bv1 = *(const uint4*)(vl0 + o + 16);
         }
         for (int tile = first; tile < t_end; tile += 2 * kStride) {
             step(tile, tile + 2 * kStride < t_end ? tile + 2 * kStride : tile, ck0, ck1, cv0, cv1);
@@ -885,6 +901,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     // The matrix-core kernel unless a measurement override asks for the
     // score-table (2-bit, G <= 4) or gather kernel.
     if (a.fmt == 0 && a.path == 1) {
+        if (a.block_table) return hipErrorInvalidValue;
         constexpr int NW = 16;
         switch (G) {
             case 1: hipLaunchKernelGGL((decode_table_kernel<1, NW>), grid, dim3(NW * 64), 0, stream, a); break;
@@ -897,23 +914,26 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     }
     if (a.path != 2) {
         constexpr int NW = 16;
+        const bool paged = a.block_table != nullptr;
+#define VQKV_G(F, GV) case GV:                                                                                     \
+            if (paged) hipLaunchKernelGGL((decode_mfma_kernel<F, GV, NW, true>), grid, dim3(NW * 64), 0, stream, a); \
+            else hipLaunchKernelGGL((decode_mfma_kernel<F, GV, NW, false>), grid, dim3(NW * 64), 0, stream, a);      \
+            break;
         if (a.fmt == 0) {
             switch (G) {
-#define VQKV_G(GV) case GV: hipLaunchKernelGGL((decode_mfma_kernel<0, GV, NW>), grid, dim3(NW * 64), 0, stream, a); break;
-                VQKV_G(1) VQKV_G(2) VQKV_G(3) VQKV_G(4) VQKV_G(5) VQKV_G(6) VQKV_G(7) VQKV_G(8)
-#undef VQKV_G
+                VQKV_G(0, 1) VQKV_G(0, 2) VQKV_G(0, 3) VQKV_G(0, 4) VQKV_G(0, 5) VQKV_G(0, 6) VQKV_G(0, 7) VQKV_G(0, 8)
                 default: return hipErrorInvalidValue;
             }
         } else {
             switch (G) {
-#define VQKV_G(GV) case GV: hipLaunchKernelGGL((decode_mfma_kernel<1, GV, NW>), grid, dim3(NW * 64), 0, stream, a); break;
-                VQKV_G(1) VQKV_G(2) VQKV_G(3) VQKV_G(4) VQKV_G(5) VQKV_G(6) VQKV_G(7) VQKV_G(8)
-#undef VQKV_G
+                VQKV_G(1, 1) VQKV_G(1, 2) VQKV_G(1, 3) VQKV_G(1, 4) VQKV_G(1, 5) VQKV_G(1, 6) VQKV_G(1, 7) VQKV_G(1, 8)
                 default: return hipErrorInvalidValue;
             }
         }
+#undef VQKV_G
         return hipGetLastError();
     }
+    if (a.block_table) return hipErrorInvalidValue;      // paged caches: matrix-core kernel only
     if (a.fmt == 0) return launch_gather<0, 8>(a, grid, stream);
     return launch_gather<1, 8>(a, grid, stream);
 }

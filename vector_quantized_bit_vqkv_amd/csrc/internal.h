@@ -50,6 +50,8 @@ struct AppendArgs {
     uint8_t* v_codes;
     int batch, hkv, cap, fmt;
     const int32_t* positions;  // device [B] or null: one token per sequence at its own position
+    const int32_t* block_table;  // device [B][Hkv][cap / 64] or null: codes in a pool of 64-token blocks
+    int num_blocks;
 };
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream);
 
@@ -66,6 +68,8 @@ struct DecodeArgs {
     float qscale;           // sm_scale * log2(e)
     int path;               // 0 auto, 1 score table (2-bit), 2 gather, 3 matrix cores (2-bit)
     const int32_t* seq_lens;   // device [B] or null (then seq_len for every sequence)
+    const int32_t* block_table;  // device [B][Hkv][cap / 64] or null: k_codes / v_codes are block pools
+    int num_blocks;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -591,19 +591,32 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
         codes[j] = (uint16_t)idx;
     }
     __syncthreads();
+    // The token's 64-token block: in the stream, or (paged) the pool block the
+    // table names, clamped to the pool; u = position inside the block.
+    uint8_t* kblk;
+    uint8_t* vblk;
+    if (a.block_table) {
+        int blk = a.block_table[stream * (int64_t)(a.cap >> 6) + (t >> 6)];
+        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+        kblk = a.k_codes + (int64_t)blk * (64 * W);
+        vblk = a.v_codes + (int64_t)blk * (64 * W);
+    } else {
+        kblk = a.k_codes + stream * (int64_t)a.cap * W + (t >> 6) * (64 * W);
+        vblk = a.v_codes + stream * (int64_t)a.cap * W + (t >> 6) * (64 * W);
+    }
+    const int u = (int)(t & 63);
     if (FMT == 0) {
         if (threadIdx.x < J) {
             const int j = threadIdx.x;
-            if (ph == 0) a.k_codes[stream * (int64_t)a.cap * W + t * W + j] = (uint8_t)codes[j];
-            else a.v_codes[stream * (int64_t)a.cap * W + v_code_offset_2bit(t, j)] = (uint8_t)codes[j];
+            if (ph == 0) kblk[u * W + j] = (uint8_t)codes[j];
+            else vblk[v_code_offset_2bit(u, j)] = (uint8_t)codes[j];
         }
     } else if (threadIdx.x < J / 2) {
         // Keys: sub-vectors (2i, 2i+1) share 3 bytes; values: (i, i + 8).
         const int i = threadIdx.x;
         const uint32_t c0 = ph == 0 ? codes[2 * i] : codes[i];
         const uint32_t c1 = ph == 0 ? codes[2 * i + 1] : codes[i + 8];
-        uint8_t* p = ph == 0 ? a.k_codes + stream * (int64_t)a.cap * W + t * W + 3 * i
-                             : a.v_codes + stream * (int64_t)a.cap * W + v_pair_offset_1p5(t, i);
+        uint8_t* p = ph == 0 ? kblk + u * W + 3 * i : vblk + v_pair_offset_1p5(u, i);
         p[0] = (uint8_t)(c0 & 0xff);
         p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
         p[2] = (uint8_t)(c1 >> 4);
