@@ -478,6 +478,63 @@ def test_quantize_append_paged_bit_exact(fmt):
     assert not np.array_equal(kc_c.cpu().numpy(), base)            # the appends did write
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_step_captured_in_a_graph_replays_exactly(fmt):
+    """One decode step (append of one token per sequence, query transform,
+    decode, combine) captured in a HIP graph: every replay, with eager work and
+    synchronizations between replays, equals the eager step bit for bit (the
+    library launches only kernels on the caller's stream, no memsets or
+    allocations)."""
+    say(f"graph capture fmt{fmt}")
+    B, Hq, Hkv, T = 2, 8, 2, 900
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, B, Hq, Hkv, T, 700 + fmt)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    rng = np.random.default_rng(3)
+    k_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32))
+    v_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32))
+    S = 3
+    books = (book_dev(kb), book_dev(vb))
+    sm = dev(s)
+    qd = dev(q)
+
+    def make_state():
+        return {"kc": dev(kbytes), "vc": dev(vbytes), "qp": torch.empty((B, Hq, D), dtype=torch.float32, device=DEV),
+                "ws": torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV),
+                "out": torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)}
+
+    def step(st):
+        vq.quantize_append(shape, k_new, v_new, T, sm, books[0], books[1], st["kc"], st["vc"])
+        vq.transform_query(shape, qd, sm, st["qp"])
+        vq.decode_attention(shape, st["qp"], books[0], books[1], st["kc"], st["vc"], T + 1, S, st["ws"])
+        vq.combine(shape, S, st["ws"], st["out"])
+
+    eager = make_state()
+    step(eager)
+    torch.cuda.synchronize()
+    want = eager["out"].cpu().numpy()
+    want_k, want_v = eager["kc"].cpu().numpy(), eager["vc"].cpu().numpy()
+
+    g_state = make_state()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                       # warm up outside the capture
+        step(g_state)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_state)
+    for r in range(3):
+        g_state["out"].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(g_state["out"].cpu().numpy().view(np.uint32), want.view(np.uint32)), r
+        assert np.array_equal(g_state["kc"].cpu().numpy(), want_k) and np.array_equal(g_state["vc"].cpu().numpy(), want_v)
+        step(eager)                                     # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_decode_single_token_returns_its_value():
     say("decode T=1")
     q, s, kb, vb, kc, vc, cap = _attn_inputs(0, 1, 8, 2, 1, 77, cap=128)
