@@ -105,6 +105,11 @@ size_t vqkv_cache_bytes(const vqkv_shape* shape);
  * vqkv_combine reads, for `num_splits` splits; 0 if the arguments are invalid. */
 size_t vqkv_workspace_bytes(const vqkv_shape* shape, int32_t num_splits);
 
+/* Bytes of the workspace of vqkv_decode_step for `num_splits` splits (the
+ * split partials plus q' and one counter per (b, KV head)); 0 if the
+ * arguments are invalid. */
+size_t vqkv_step_workspace_bytes(const vqkv_shape* shape, int32_t num_splits);
+
 /* A split count that fills the GPU for this shape and context length
  * (>= 1).  Any value in [1, ceil(seq_len / 64)] is valid for the decode. */
 int32_t vqkv_suggest_splits(const vqkv_shape* shape, int32_t seq_len);
@@ -235,6 +240,31 @@ vqkv_status vqkv_quantize_append_paged(const vqkv_shape* shape, const void* k_ne
  *   out         device, fp32 [B][Hq][128] (output) */
 vqkv_status vqkv_combine(const vqkv_shape* shape, int32_t num_splits, const void* workspace,
                          float* out, void* stream);
+
+/* One decode step in two launches: the append of one new token per sequence
+ * at `position` (with the query transform in the same launch), then the
+ * attention of every query over tokens [0, position] with the split combine
+ * fused into it.  The result is bit-identical to the four calls
+ *   vqkv_quantize_append(n_new = 1, start_pos = position), vqkv_transform_query,
+ *   vqkv_decode_attention(seq_len = position + 1), vqkv_combine
+ * on the same arguments (the same kernels' arithmetic).  With one split the
+ * attention kernel writes `out` itself; with more, the last split of each
+ * (b, KV head) to finish combines that head's splits (a per-head arrival
+ * counter in the workspace, cleared by the first launch of every step, so the
+ * workspace needs no initialization).  Runs on the matrix-core kernel.
+ *   q                 device, [B][Hq][128], dtype (the same dtype as k_new)
+ *   k_new, v_new      device, [B][Hkv][1][128], dtype
+ *   position          host, 0 <= position < max_tokens
+ *   num_splits        host, 1 <= num_splits <= ceil((position + 1) / 64)
+ *   workspace         device, vqkv_step_workspace_bytes(shape, num_splits)
+ *                     bytes, private to the call; steps sharing a workspace
+ *                     must not overlap in time
+ *   out               device, fp32 [B][Hq][128] (output)
+ *   other arguments as for vqkv_quantize_append and vqkv_decode_attention. */
+vqkv_status vqkv_decode_step(const vqkv_shape* shape, const void* q, const void* k_new, const void* v_new,
+                             int32_t dtype, int32_t position, const float* smooth, const uint16_t* k_book,
+                             const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, float sm_scale,
+                             int32_t num_splits, void* workspace, float* out, void* stream);
 
 /* ------------------------------------------------- offline calibration calls */
 

@@ -130,6 +130,27 @@ def test_paged_argument_checks():
     assert app(4, FAKE, pos=None) == INVALID
 
 
+def test_decode_step_argument_checks():
+    L = vq.lib()
+    shape = vq.make_shape(2, 32, 8, 1024, vq.FMT_2BIT)
+    sh = ctypes.byref(shape)
+    call = lambda pos, S, dt=0, ws=FAKE, out=FAKE, scale=0.088: L.vqkv_decode_step(
+        sh, FAKE, FAKE, FAKE, dt, pos, FAKE, FAKE, FAKE, FAKE, FAKE, scale, S, ws, out, None)
+    assert call(-1, 1) == INVALID                        # position before the cache
+    assert call(1024, 1) == INVALID                      # position past the capacity
+    assert call(63, 2) == INVALID                        # 64 tokens: one tile, one split at most
+    assert call(100, 0) == INVALID
+    assert call(100, 1, dt=5) == INVALID
+    assert call(100, 1, ws=None) == INVALID
+    assert call(100, 1, out=None) == INVALID
+    assert call(100, 1, out=MISALIGNED) == INVALID
+    assert call(100, 1, scale=float("inf")) == INVALID
+    ws1, ws4 = vq.step_workspace_bytes(shape, 1), vq.step_workspace_bytes(shape, 4)
+    assert ws1 >= vq.workspace_bytes(shape, 1) + 2 * 32 * 128 * 4 + 2 * 8 * 4
+    assert ws4 - ws1 == vq.workspace_bytes(shape, 4) - vq.workspace_bytes(shape, 1)
+    assert vq.step_workspace_bytes(shape, 0) == 0
+
+
 def test_transform_combine_and_calibration_checks():
     L = vq.lib()
     sh = ctypes.byref(vq.make_shape(1, 4, 1, 64, vq.FMT_2BIT))

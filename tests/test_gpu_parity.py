@@ -478,6 +478,67 @@ def test_quantize_append_paged_bit_exact(fmt):
     assert not np.array_equal(kc_c.cpu().numpy(), base)            # the appends did write
 
 
+STEP_CASES = [
+    # fmt, B, Hq, Hkv, position, S, dtype
+    (0, 2, 32, 8, 0, 1, "bf16"),          # the first token: attention over one token
+    (0, 2, 32, 8, 4098, 1, "bf16"),       # one split: the attention kernel writes out itself
+    (0, 2, 32, 8, 4098, 9, "bf16"),       # ragged tail, fused combine
+    (0, 1, 16, 2, 700, 11, "fp32"),       # G = 8: eight combine groups
+    (0, 1, 8, 8, 2000, 32, "fp32"),       # G = 1
+    (1, 1, 40, 8, 1000, 4, "bf16"),       # G = 5
+    (1, 2, 12, 4, 4098, 9, "fp32"),       # G = 3
+    (1, 1, 2, 2, 3000, 47, "bf16"),       # G = 1, many splits
+]
+
+
+@pytest.mark.parametrize("fmt,B,Hq,Hkv,pos,S,dtype", STEP_CASES)
+def test_decode_step_equals_the_four_calls(fmt, B, Hq, Hkv, pos, S, dtype):
+    """decode_step (two launches, fused combine) against quantize_append +
+    transform_query + decode_attention + combine: the same output bits and the
+    same cache bytes, on two steps in a row that share a workspace filled with
+    0xFF bytes beforehand (the counters need no initialization), and the
+    output within the tolerance of the oracle on the cache as it ends up."""
+    say(f"decode_step fmt{fmt} B{B} Hq{Hq} Hkv{Hkv} pos{pos} S{S} {dtype}")
+    cap = ((pos + 2 + 63) // 64) * 64
+    q, s, kb, vb, kc, vc, _ = _attn_inputs(fmt, B, Hq, Hkv, pos + 2, 5000 + pos + Hq, cap)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rng = np.random.default_rng(pos + S)
+    books, sm = (book_dev(kb), book_dev(vb)), dev(s)
+    ref_k, ref_v = dev(kbytes), dev(vbytes)
+    got_k, got_v = dev(kbytes), dev(vbytes)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    ws_ref = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+    ws = torch.full((vq.step_workspace_bytes(shape, S),), 0xFF, dtype=torch.uint8, device=DEV)
+    assert ws.numel() > ws_ref.numel()
+    for p in (pos, pos + 1):
+        qd = dev(rng.standard_normal((B, Hq, D)).astype(np.float32), tdt)
+        k_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32) * 2.0, tdt)
+        v_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), tdt)
+        want = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+        vq.quantize_append(shape, k_new, v_new, p, sm, books[0], books[1], ref_k, ref_v)
+        vq.transform_query(shape, qd, sm, qp)
+        vq.decode_attention(shape, qp, books[0], books[1], ref_k, ref_v, p + 1, S, ws_ref)
+        vq.combine(shape, S, ws_ref, want)
+        got = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+        vq.decode_step(shape, qd, k_new, v_new, p, sm, books[0], books[1], got_k, got_v, S, ws, got)
+        torch.cuda.synchronize()
+        g, w = got.cpu().numpy(), want.cpu().numpy()
+        assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), f"position {p}: max diff {np.abs(g - w).max()}"
+        assert torch.equal(got_k, ref_k) and torch.equal(got_v, ref_v)
+    # The oracle on the codes the cache holds after the second step.
+    T = pos + 2
+    kc_all = np.stack([np.stack([oracle.unpack_k(fmt, got_k[b, h].cpu().numpy(), T) for h in range(Hkv)])
+                       for b in range(B)])
+    vc_all = np.stack([np.stack([oracle.unpack_v(fmt, got_v[b, h].cpu().numpy(), T) for h in range(Hkv)])
+                       for b in range(B)])
+    ref = oracle.attention(fmt, qd.float().cpu().numpy(), s, kb, vb, kc_all, vc_all)
+    err = rel_err(got.cpu().numpy(), ref)
+    print(f"  max relative error {err:.3e}", flush=True)
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_step_captured_in_a_graph_replays_exactly(fmt):
     """One decode step (append of one token per sequence, query transform,
@@ -532,6 +593,55 @@ def test_step_captured_in_a_graph_replays_exactly(fmt):
         assert np.array_equal(g_state["out"].cpu().numpy().view(np.uint32), want.view(np.uint32)), r
         assert np.array_equal(g_state["kc"].cpu().numpy(), want_k) and np.array_equal(g_state["vc"].cpu().numpy(), want_v)
         step(eager)                                     # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fmt,S", [(0, 3), (1, 4), (0, 1)])
+def test_decode_step_captured_in_a_graph(fmt, S):
+    """decode_step captured in a HIP graph: the prologue clears the arrival
+    counters with ordinary stores (no memset node), so every replay, with eager
+    steps on another workspace between replays, equals the eager step bit for
+    bit."""
+    say(f"decode_step graph fmt{fmt} S{S}")
+    B, Hq, Hkv, T = 2, 8, 2, 1500
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, B, Hq, Hkv, T, 900 + fmt)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    rng = np.random.default_rng(4)
+    k_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), torch.bfloat16)
+    v_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), torch.bfloat16)
+    qd = dev(q, torch.bfloat16)
+    books, sm = (book_dev(kb), book_dev(vb)), dev(s)
+
+    def make_state():
+        return {"kc": dev(kbytes), "vc": dev(vbytes),
+                "ws": torch.empty(vq.step_workspace_bytes(shape, S), dtype=torch.uint8, device=DEV),
+                "out": torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)}
+
+    def step(st):
+        vq.decode_step(shape, qd, k_new, v_new, T - 1, sm, books[0], books[1], st["kc"], st["vc"], S, st["ws"],
+                       st["out"])
+
+    eager = make_state()
+    step(eager)
+    torch.cuda.synchronize()
+    want = eager["out"].cpu().numpy()
+    g_state = make_state()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(g_state)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_state)
+    for r in range(3):
+        g_state["out"].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(g_state["out"].cpu().numpy().view(np.uint32), want.view(np.uint32)), r
+        step(eager)
         torch.cuda.synchronize()
 
 

@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         "vqkv_quantize_append": (I32, [SP, P, P, I32, I32, I32, P, P, P, P, P, P]),
         "vqkv_decode_attention": (I32, [SP, P, P, P, P, P, I32, F32, I32, P, P]),
         "vqkv_combine": (I32, [SP, I32, P, P, P]),
+        "vqkv_step_workspace_bytes": (SZ, [SP, I32]),
+        "vqkv_decode_step": (I32, [SP, P, P, P, I32, I32, P, P, P, P, P, F32, I32, P, P, P]),
         "vqkv_decode_attention_varlen": (I32, [SP, P, P, P, P, P, P, I32, F32, I32, P, P]),
         "vqkv_quantize_append_varlen": (I32, [SP, P, P, I32, P, P, P, P, P, P, P]),
         "vqkv_decode_attention_paged": (I32, [SP, P, P, P, P, P, I32, P, P, I32, F32, I32, P, P]),
@@ -132,6 +134,10 @@ def cache_bytes(shape: Shape) -> int:
 
 def workspace_bytes(shape: Shape, num_splits: int) -> int:
     return int(lib().vqkv_workspace_bytes(ctypes.byref(shape), num_splits))
+
+
+def step_workspace_bytes(shape: Shape, num_splits: int) -> int:
+    return int(lib().vqkv_step_workspace_bytes(ctypes.byref(shape), num_splits))
 
 
 def suggest_splits(shape: Shape, seq_len: int) -> int:
@@ -228,6 +234,21 @@ def quantize_append_paged(shape: Shape, k_new, v_new, positions, smooth, k_book,
 def combine(shape: Shape, num_splits: int, workspace, out) -> None:
     """Log-sum-exp merge of the splits into out [B][Hq][128] fp32."""
     _check(lib().vqkv_combine(ctypes.byref(shape), num_splits, _ptr(workspace), _ptr(out), _stream(out)))
+
+
+def decode_step(shape: Shape, q, k_new, v_new, position: int, smooth, k_book, v_book, k_codes, v_codes,
+                num_splits: int, workspace, out, sm_scale: float | None = None) -> None:
+    """Append one token per sequence at `position`, then attention over [0, position] into out
+    (two launches; bit-identical to quantize_append + transform_query + decode_attention + combine)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype or q.dtype != k_new.dtype:
+        raise ValueError("q, k_new and v_new must share a dtype; k_new and v_new a shape")
+    if k_new.shape[2] != 1:
+        raise ValueError("decode_step appends one token per sequence")
+    _check(lib().vqkv_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                  position, _ptr(smooth), _ptr(k_book), _ptr(v_book), _ptr(k_codes),
+                                  _ptr(v_codes), sm_scale, num_splits, _ptr(workspace), _ptr(out), _stream(q)))
 
 
 # ------------------------------------------------------------------- calibration

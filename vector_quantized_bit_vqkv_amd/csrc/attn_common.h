@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
 // outputs (removed from lse).
 template <int G, int NW>
 __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeArgs& a, int b, int h, int s,
-                                            float l_log2_scale) {
+                                            float l_log2_scale, float* stage = nullptr) {
     const float* mo = scratch;
     const float* ml = scratch + NW * G * kHeadDim;
     for (int idx = threadIdx.x; idx < G * kHeadDim; idx += NW * 64) {
@@ -96,10 +96,100 @@ __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeAr
             o = O / L;
             lse = M + (__builtin_log2f(L) - l_log2_scale);
         }
-        const int64_t row = ((int64_t)b * a.hq + h * G + g) * a.splits + s;
-        a.part_o[row * kHeadDim + d] = o;
-        if (d == 0) a.part_lse[row] = lse;
+        if (stage != nullptr && a.out != nullptr && a.splits > 1) {
+            // Fused combine: the partial waits in LDS for combine_if_last.
+            stage[g * kHeadDim + d] = o;
+            if (d == 0) stage[G * kHeadDim + g] = lse;
+        } else if (a.out != nullptr && a.splits == 1) {
+            // One split: o is already the output (the combine of a single
+            // split returns it unchanged, 0 for an empty row).
+            a.out[((int64_t)b * a.hq + h * G + g) * kHeadDim + d] = o;
+        } else {
+            const int64_t row = ((int64_t)b * a.hq + h * G + g) * a.splits + s;
+            a.part_o[row * kHeadDim + d] = o;
+            if (d == 0) a.part_lse[row] = lse;
+        }
     }
+}
+
+// One (b, q-head) row of the split combine: lse = log2 sum_i 2^lse_i and
+// out = sum_i 2^(lse_i - lse) o_i (empty splits, lse_i = -inf, weigh 0; a row
+// with no token gives 0).  d = output dim in [0, 128) of the row's 128-thread
+// group; red = 2 floats of LDS for the group.  The sum over splits keeps eight
+// loads in flight per thread.  It has block barriers: every thread of the
+// block calls it, threads of an inactive group only pass the barriers.
+__device__ __forceinline__ void combine_row(const float* part_o, const float* part_lse, float* out, int S,
+                                            int64_t bg, int d, bool active, float* red) {
+    const int lane = d & 63, wave = d >> 6;
+    const float* lse = part_lse + bg * S;
+    float M = kNegInf;
+    if (active)
+        for (int s = d; s < S; s += 128) M = fmaxf(M, lse[s]);
+    M = wave_max(M);
+    if (lane == 0) red[wave] = M;
+    __syncthreads();
+    M = fmaxf(red[0], red[1]);
+    __syncthreads();
+    float den = 0.0f, num = 0.0f;
+    if (active && M != kNegInf) {
+        for (int s = d; s < S; s += 128) {
+            const float ls = lse[s];
+            den += ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
+        }
+        const float* po = part_o + bg * S * kHeadDim + d;
+#pragma unroll 8
+        for (int s = 0; s < S; ++s) {
+            const float ls = lse[s];
+            const float w = ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
+            num += w * po[(int64_t)s * kHeadDim];
+        }
+    }
+    den = wave_sum(den);
+    if (lane == 0) red[wave] = den;
+    __syncthreads();
+    den = red[0] + red[1];
+    if (active) out[bg * kHeadDim + d] = den > 0.0f ? num / den : 0.0f;
+}
+
+// Fused combine after merge_waves(..., stage), for more than one split.
+// Wave 0 writes the split's partials (G rows of o, G lse values, staged in
+// LDS by merge_waves), makes them visible device-wide with one release fence,
+// and counts the work-group in arrivals[b][h] (lane 0, after the fence: all of
+// the wave's stores precede the count).  The last of the head's splits to
+// arrive fences again (acquire) before the block reads the other splits'
+// partials, combines the head's G rows (one 128-thread group per query head)
+// and clears the counter for the next launch.  One fence pair per work-group:
+// a device-scope fence writes back the L2 of the XCD, too slow to run in every
+// wave.
+template <int G, int NW>
+__device__ __forceinline__ void combine_if_last(unsigned char* smem, const float* stage, const DecodeArgs& a,
+                                                int b, int h) {
+    static_assert(G * 128 <= NW * 64, "one 128-thread group per query head");
+    int* last = (int*)smem;
+    float* red = (float*)(smem + 16);
+    const int64_t stream = (int64_t)b * a.hkv + h;
+    __syncthreads();                                        // the stage is complete, the merge scratch free
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x, s = blockIdx.x;
+        for (int i = lane; i < G * kHeadDim; i += 64) {
+            const int64_t row = ((int64_t)b * a.hq + h * G + i / kHeadDim) * a.splits + s;
+            a.part_o[row * kHeadDim + i % kHeadDim] = stage[i];
+        }
+        if (lane < G) a.part_lse[((int64_t)b * a.hq + h * G + lane) * a.splits + s] = stage[G * kHeadDim + lane];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        int prev = 0;
+        if (lane == 0) prev = __hip_atomic_fetch_add(a.arrivals + stream, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __shfl(prev, 0, 64);
+        if (prev == a.splits - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (lane == 0) *last = prev == a.splits - 1;
+    }
+    __syncthreads();
+    if (!*last) return;                                     // block-uniform
+    const int grp = threadIdx.x >> 7;
+    const bool active = grp < G;
+    combine_row(a.part_o, a.part_lse, a.out, a.splits, (int64_t)b * a.hq + h * G + (active ? grp : 0),
+                threadIdx.x & 127, active, red + 2 * grp);
+    if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + stream, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stash one wave's (m, l) for merge_waves (lane 0 writes).

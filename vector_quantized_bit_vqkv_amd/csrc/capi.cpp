@@ -120,6 +120,13 @@ size_t vqkv_workspace_bytes(const vqkv_shape* s, int32_t num_splits) {
     return align256(rows * 128 * sizeof(float)) + align256(rows * sizeof(float));
 }
 
+size_t vqkv_step_workspace_bytes(const vqkv_shape* s, int32_t num_splits) {
+    const size_t base = vqkv_workspace_bytes(s, num_splits);
+    if (base == 0) return 0;
+    return base + align256((size_t)s->batch * s->num_q_heads * 128 * sizeof(float)) +
+           align256((size_t)s->batch * s->num_kv_heads * sizeof(int32_t));
+}
+
 int32_t vqkv_suggest_splits(const vqkv_shape* s, int32_t seq_len) {
     if (check_shape(s, false) != VQKV_OK || seq_len < 1) return 1;
     const int64_t streams = (int64_t)s->batch * s->num_kv_heads;
@@ -314,6 +321,50 @@ vqkv_status vqkv_decode_attention_paged(const vqkv_shape* s, const float* q_prim
                        max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), 0, seq_lens, block_table, num_blocks};
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention_paged launch");
+}
+
+vqkv_status vqkv_decode_step(const vqkv_shape* s, const void* q, const void* k_new, const void* v_new,
+                             int32_t dtype, int32_t position, const float* smooth, const uint16_t* k_book,
+                             const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, float sm_scale,
+                             int32_t num_splits, void* workspace, float* out, void* stream) {
+    VQKV_CHECK(check_shape(s, true));
+    VQKV_CHECK(check_dtype(dtype));
+    if (position < 0 || position >= s->max_tokens)
+        return fail(VQKV_ERR_INVALID_ARG, "position %d outside [0, max_tokens = %d)", position, s->max_tokens);
+    const int seq_len = position + 1;
+    if (!std::isfinite(sm_scale)) return fail(VQKV_ERR_INVALID_ARG, "sm_scale is not finite");
+    if (num_splits < 1 || num_splits > ceil_div(seq_len, 64))
+        return fail(VQKV_ERR_INVALID_ARG, "num_splits %d outside [1, ceil((position + 1) / 64) = %lld]", num_splits,
+                    (long long)ceil_div(seq_len, 64));
+    VQKV_CHECK(check_ptr(q, "q"));
+    VQKV_CHECK(check_ptr(k_new, "k_new"));
+    VQKV_CHECK(check_ptr(v_new, "v_new"));
+    VQKV_CHECK(check_ptr(smooth, "smooth"));
+    VQKV_CHECK(check_ptr(k_book, "k_book"));
+    VQKV_CHECK(check_ptr(v_book, "v_book"));
+    VQKV_CHECK(check_ptr(k_codes, "k_codes"));
+    VQKV_CHECK(check_ptr(v_codes, "v_codes"));
+    VQKV_CHECK(check_ptr(workspace, "workspace"));
+    VQKV_CHECK(check_ptr(out, "out"));
+    // Workspace: partial o | partial lse | q' | arrival counters.
+    const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
+    char* ws = (char*)workspace;
+    float* part_o = (float*)ws;
+    ws += align256(rows * 128 * sizeof(float));
+    float* part_lse = (float*)ws;
+    ws += align256(rows * sizeof(float));
+    float* q_prime = (float*)ws;
+    ws += align256((size_t)s->batch * s->num_q_heads * 128 * sizeof(float));
+    int32_t* arrivals = (int32_t*)ws;
+    vqkv::AppendArgs ap{k_new, v_new, dtype, 1, position, smooth, k_book, v_book, k_codes, v_codes,
+                        s->batch, s->num_kv_heads, s->max_tokens, s->fmt, nullptr, nullptr, 0,
+                        q, q_prime, arrivals, s->num_q_heads};
+    VQKV_CHECK(hip_status(vqkv::launch_quantize_append(ap, (hipStream_t)stream), "decode_step append launch"));
+    vqkv::DecodeArgs d{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
+                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
+                       seq_len, num_splits, split_chunk(seq_len, num_splits),
+                       (float)((double)sm_scale * 1.4426950408889634), 3, nullptr, nullptr, 0, out, arrivals};
+    return hip_status(vqkv::launch_decode(d, (hipStream_t)stream), "decode_step decode launch");
 }
 
 vqkv_status vqkv_combine(const vqkv_shape* s, int32_t num_splits, const void* workspace, float* out, void* stream) {

@@ -679,7 +679,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
     stash_ml<G, NW>(scratch, m, l);
     __syncthreads();
-    merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2);
+    float* stage = scratch + NW * G * (kHeadDim + 2);       // after the merge scratch
+    static_assert(SMEM >= MERGE_BYTES + G * (kHeadDim + 1) * 4, "LDS holds the merge scratch and the stage");
+    merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2, stage);
+    if (a.out != nullptr && a.splits > 1) combine_if_last<G, NW>(smem, stage, a, b, h);
 }
 
 // ------------------------------------------------------------------ gather path
@@ -844,41 +847,10 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
 
 // ----------------------------------------------------------------------- combine
 
-// One block per (b, q-head), thread d = output dim.  The split maximum and the
-// normalizer are reduced by all threads; the weighted sum over splits keeps
-// eight loads in flight per thread (empty splits, lse = -inf, weigh 0).
+// One block per (b, q-head), thread d = output dim (combine_row).
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     __shared__ float red[2];
-    const int64_t bg = blockIdx.x;
-    const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
-    const int S = a.splits;
-    const float* lse = a.part_lse + bg * S;
-    float M = kNegInf;
-    for (int s = d; s < S; s += 128) M = fmaxf(M, lse[s]);
-    M = wave_max(M);
-    if (lane == 0) red[wave] = M;
-    __syncthreads();
-    M = fmaxf(red[0], red[1]);
-    __syncthreads();
-    float den = 0.0f, num = 0.0f;
-    if (M != kNegInf) {
-        for (int s = d; s < S; s += 128) {
-            const float ls = lse[s];
-            den += ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
-        }
-        const float* po = a.part_o + bg * S * kHeadDim + d;
-#pragma unroll 8
-        for (int s = 0; s < S; ++s) {
-            const float ls = lse[s];
-            const float w = ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
-            num += w * po[(int64_t)s * kHeadDim];
-        }
-    }
-    den = wave_sum(den);
-    if (lane == 0) red[wave] = den;
-    __syncthreads();
-    den = red[0] + red[1];
-    a.out[bg * kHeadDim + d] = den > 0.0f ? num / den : 0.0f;
+    combine_row(a.part_o, a.part_lse, a.out, a.splits, blockIdx.x, threadIdx.x, true, red);
 }
 
 template <int FMT, int NW>
@@ -900,6 +872,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const int G = a.hq / a.hkv;
     // The matrix-core kernel unless a measurement override asks for the
     // score-table (2-bit, G <= 4) or gather kernel.
+    if (a.out != nullptr && (a.path == 1 || a.path == 2)) return hipErrorInvalidValue;   // fused combine: matrix-core kernel
     if (a.fmt == 0 && a.path == 1) {
         if (a.block_table) return hipErrorInvalidValue;
         constexpr int NW = 16;

@@ -52,6 +52,13 @@ struct AppendArgs {
     const int32_t* positions;  // device [B] or null: one token per sequence at its own position
     const int32_t* block_table;  // device [B][Hkv][cap / 64] or null: codes in a pool of 64-token blocks
     int num_blocks;
+    // Decode-step prologue (q_prime non-null): a third block per (b, kv-head)
+    // writes q' = H (q * s) for the head's Hq / Hkv query heads and clears the
+    // head's arrival counter for the decode that follows.
+    const void* q;          // [B][Hq][128], dtype as k_new
+    float* q_prime;         // [B][Hq][128]
+    int32_t* arrivals;      // [B][Hkv]
+    int hq;
 };
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream);
 
@@ -70,6 +77,12 @@ struct DecodeArgs {
     const int32_t* seq_lens;   // device [B] or null (then seq_len for every sequence)
     const int32_t* block_table;  // device [B][Hkv][cap / 64] or null: k_codes / v_codes are block pools
     int num_blocks;
+    // Fused combine (matrix-core kernel only), out non-null: with one split the
+    // work-group writes out directly; with more, each work-group counts itself
+    // in arrivals[b][kv-head] (zero at launch) and the last one of a head
+    // combines the head's splits into out and clears the counter.
+    float* out;             // [B][Hq][128]
+    int32_t* arrivals;      // [B][Hkv]
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
