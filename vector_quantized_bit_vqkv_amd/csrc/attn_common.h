@@ -115,11 +115,13 @@ __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeAr
 // One (b, q-head) row of the split combine: lse = log2 sum_i 2^lse_i and
 // out = sum_i 2^(lse_i - lse) o_i (empty splits, lse_i = -inf, weigh 0; a row
 // with no token gives 0).  d = output dim in [0, 128) of the row's 128-thread
-// group; red = 2 floats of LDS for the group.  The sum over splits keeps eight
-// loads in flight per thread.  It has block barriers: every thread of the
-// block calls it, threads of an inactive group only pass the barriers.
+// group; red = 2 floats and wts = 128 floats of LDS for the group.  Splits go
+// in chunks of 128: thread d computes the weight of split c + d into wts, then
+// every thread sums its dim over the chunk in split order, 16 partial rows in
+// flight.  It has block barriers: every thread of the block calls it, threads
+// of an inactive group only pass the barriers.
 __device__ __forceinline__ void combine_row(const float* part_o, const float* part_lse, float* out, int S,
-                                            int64_t bg, int d, bool active, float* red) {
+                                            int64_t bg, int d, bool active, float* red, float* wts) {
     const int lane = d & 63, wave = d >> 6;
     const float* lse = part_lse + bg * S;
     float M = kNegInf;
@@ -130,19 +132,24 @@ __device__ __forceinline__ void combine_row(const float* part_o, const float* pa
     __syncthreads();
     M = fmaxf(red[0], red[1]);
     __syncthreads();
+    const bool any = active && M != kNegInf;
+    const float* po = part_o + bg * S * kHeadDim + d;
     float den = 0.0f, num = 0.0f;
-    if (active && M != kNegInf) {
-        for (int s = d; s < S; s += 128) {
-            const float ls = lse[s];
-            den += ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
+    for (int c = 0; c < S; c += 128) {                      // the same trip count in every thread
+        float w = 0.0f;
+        if (any && c + d < S) {
+            const float ls = lse[c + d];
+            w = ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
         }
-        const float* po = part_o + bg * S * kHeadDim + d;
-#pragma unroll 8
-        for (int s = 0; s < S; ++s) {
-            const float ls = lse[s];
-            const float w = ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
-            num += w * po[(int64_t)s * kHeadDim];
+        den += w;
+        wts[d] = w;
+        __syncthreads();
+        if (any) {
+            const int n = S - c < 128 ? S - c : 128;
+#pragma unroll 16
+            for (int i = 0; i < n; ++i) num += wts[i] * po[(int64_t)(c + i) * kHeadDim];
         }
+        __syncthreads();
     }
     den = wave_sum(den);
     if (lane == 0) red[wave] = den;
@@ -166,7 +173,8 @@ __device__ __forceinline__ void combine_if_last(unsigned char* smem, const float
                                                 int b, int h) {
     static_assert(G * 128 <= NW * 64, "one 128-thread group per query head");
     int* last = (int*)smem;
-    float* red = (float*)(smem + 16);
+    float* red = (float*)(smem + 16);                       // 2 floats per group
+    float* wts = (float*)(smem + 128);                      // 128 floats per group
     const int64_t stream = (int64_t)b * a.hkv + h;
     __syncthreads();                                        // the stage is complete, the merge scratch free
     if (threadIdx.x < 64) {
@@ -188,7 +196,7 @@ __device__ __forceinline__ void combine_if_last(unsigned char* smem, const float
     const int grp = threadIdx.x >> 7;
     const bool active = grp < G;
     combine_row(a.part_o, a.part_lse, a.out, a.splits, (int64_t)b * a.hq + h * G + (active ? grp : 0),
-                threadIdx.x & 127, active, red + 2 * grp);
+                threadIdx.x & 127, active, red + 2 * grp, wts + 128 * grp);
     if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + stream, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

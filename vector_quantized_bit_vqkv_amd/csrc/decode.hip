@@ -849,8 +849,8 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
 
 // One block per (b, q-head), thread d = output dim (combine_row).
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-    __shared__ float red[2];
-    combine_row(a.part_o, a.part_lse, a.out, a.splits, blockIdx.x, threadIdx.x, true, red);
+    __shared__ float red[2], wts[128];
+    combine_row(a.part_o, a.part_lse, a.out, a.splits, blockIdx.x, threadIdx.x, true, red, wts);
 }
 
 template <int FMT, int NW>

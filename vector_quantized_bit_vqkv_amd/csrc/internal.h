@@ -52,9 +52,9 @@ struct AppendArgs {
     const int32_t* positions;  // device [B] or null: one token per sequence at its own position
     const int32_t* block_table;  // device [B][Hkv][cap / 64] or null: codes in a pool of 64-token blocks
     int num_blocks;
-    // Decode-step prologue (q_prime non-null): a third block per (b, kv-head)
-    // writes q' = H (q * s) for the head's Hq / Hkv query heads and clears the
-    // head's arrival counter for the decode that follows.
+    // Decode-step prologue (q_prime non-null): the key block of each (b, kv-head)
+    // also writes q' = H (q * s) for the head's Hq / Hkv query heads (waves
+    // 1..G, first) and clears the head's arrival counter for the decode.
     const void* q;          // [B][Hq][128], dtype as k_new
     float* q_prime;         // [B][Hq][128]
     int32_t* arrivals;      // [B][Hkv]

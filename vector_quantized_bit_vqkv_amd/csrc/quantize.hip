@@ -540,15 +540,14 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
 
     const int ph = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t stream = (int64_t)b * a.hkv + h;
-    if (ph == 2) {                              // decode-step prologue: q' of this head's query group
-        const int G = a.hq / a.hkv, wave = threadIdx.x >> 6;
-        if (wave < G) {
-            const int64_t vec = (int64_t)b * a.hq + h * G + wave;
+    if (a.q_prime != nullptr && ph == 0) {      // decode-step prologue, before the key's own work:
+        const int G = a.hq / a.hkv, w = (int)(threadIdx.x >> 6) - 1;
+        if (w >= 0 && w < G) {                  // waves 1..G: q' of this head's query group
+            const int64_t vec = (int64_t)b * a.hq + h * G + w;
             transform_query_wave((const char*)a.q + vec * kHeadDim * (a.dtype == 0 ? 2 : 4), a.dtype,
                                  a.smooth + (int64_t)h * kHeadDim, a.q_prime + vec * kHeadDim, threadIdx.x & 63);
         }
         if (threadIdx.x == 0) a.arrivals[stream] = 0;
-        return;
     }
     // Position of the token: uniform, or per sequence (a position outside the
     // cache is skipped, block-uniformly, so nothing is written out of bounds).
@@ -796,7 +795,7 @@ hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
     const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
     const dim3 grid(last - first + 1, a.hkv, a.batch);
     if (a.n_new == 1 || a.positions) {
-        const dim3 g1(a.q_prime ? 3 : 2, a.hkv, a.batch);
+        const dim3 g1(2, a.hkv, a.batch);
         if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(1024), 0, stream, a);
         else hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
         return hipGetLastError();
