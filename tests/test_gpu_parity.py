@@ -197,10 +197,12 @@ def test_quantize_ties_go_to_lowest_index(fmt):
     kb[0, 200] = kb[0, 17]                                      # duplicate: 17 must win over 200
     vb = np.zeros((1, E, dsub), np.float16)
     vb[0, :, 0] = np.arange(E, dtype=np.float64) * 0.25          # entries 0, .25, .5, ... on dim 0
+    vb[0, E - 1] = vb[0, 5]                                     # the last entry duplicates entry 5
     vb = vb.view(np.uint16)
     n = 64
     v = np.zeros((n, D), np.float32)
     v[:, ::dsub] = (rng.integers(0, 200, (n, J)) * 0.25 + 0.125).astype(np.float32)   # exact midpoints
+    v[:4, 0] = 1.25                                             # exactly entries 5 and E - 1: 5 wins
     k = rng.standard_normal((n, D)).astype(np.float32)
     s = np.ones(D, np.float32)
     kc_ref, vc_ref = oracle.quantize(fmt, k, v, s, kb[0], vb[0])
@@ -214,8 +216,10 @@ def test_quantize_ties_go_to_lowest_index(fmt):
     gv = oracle.unpack_v(fmt, vcodes[0, 0].cpu().numpy(), n)
     assert np.array_equal(gk, kc_ref) and np.array_equal(gv, vc_ref)
     assert not np.any(gk == 200)
-    # Halfway between entries m and m+1 the lower index wins.
-    assert np.array_equal(gv, (v[:, ::dsub] / 0.25 - 0.5).astype(np.uint16))
+    # Halfway between entries m and m+1 the lower index wins; of two equal entries, the lower.
+    expect = (v[:, ::dsub] / 0.25 - 0.5).astype(np.uint16)
+    expect[:4, 0] = 5
+    assert np.array_equal(gv, expect)
     # The same tokens appended one at a time (the per-step append path).
     kcodes1 = torch.zeros_like(kcodes)
     vcodes1 = torch.zeros_like(kcodes)

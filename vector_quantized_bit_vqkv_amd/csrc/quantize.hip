@@ -518,29 +518,52 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
 
 // ------------------------------------------------- append of a single token
 
+// Lexicographic (distance, index) minimum over aligned groups of L lanes
+// (L a power of two <= 64); every lane of a group gets its group's minimum.
+template <int L>
+__device__ __forceinline__ void group_argmin(double& d, int& idx) {
+#pragma unroll
+    for (int m = 1; m < L; m <<= 1) {
+        const double od = __shfl_xor(d, m, 64);
+        const int oi = __shfl_xor(idx, m, 64);
+        if (od < d || (od == d && oi < idx)) { d = od; idx = oi; }
+    }
+}
+
+// Blocks per key (and per value) of the one-token append: a 4096-entry search
+// is split over 4 blocks of 4 sub-vectors each, so the grid fills the GPU.
+template <int FMT> struct TokenSplit { static constexpr int P = FMT == 0 ? 1 : 4; };
+
 // The per-step append (one new token per sequence), latency-bound: grid
-// (2, Hkv, B), block x = 0 codes the key, x = 1 the value.  The codebook and
-// the row are staged in LDS at once; the key block rotates the key with one
-// wave (the same butterflies as block_fwht, stage h exchanged between lanes l
-// and l ^ h, so the result is identical); the nearest-centroid searches run
-// over slices of the codebook, merged in slice order (ties keep the lowest
-// index).
+// (2P, Hkv, B), block x / P = 0 codes the key, 1 the value, x % P = part p
+// codes J / P of the sub-vectors (keys: consecutive ones; 1.5-bit values: the
+// pairs (i, i + 8) that share three bytes, kept in one block).  The codebook
+// and the row are staged in LDS at once; the key blocks rotate the key with
+// one wave (the same butterflies as block_fwht, stage h exchanged between
+// lanes l and l ^ h, so the result is identical).  Each sub-vector's search
+// runs over ES interleaved slices of the codebook, one per thread; the slices'
+// minima are merged as (distance, index) pairs, lowest pair first, which is
+// the scan's lowest-index minimum whatever the merge order.
 template <int FMT>
 __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
     using F = Fmt<FMT>;
     constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
-    constexpr int NT = 1024;
-    constexpr int ES = NT / J;                  // slices per sub-vector
+    constexpr int NT = 1024, P = TokenSplit<FMT>::P;
+    constexpr int JB = J / P;                   // sub-vectors per block
+    constexpr int ES = NT / JB;                 // slices per sub-vector
     constexpr int EPS = E / ES;                 // centroids per slice
+    constexpr int L = ES < 64 ? ES : 64;        // lanes of one sub-vector in a wave
+    constexpr int WPS = ES / L;                 // waves per sub-vector
+    static_assert(JB % 2 == 0 && E % ES == 0 && (L & (L - 1)) == 0, "token search shape");
     __shared__ __align__(16) uint16_t book[E * DS];
     __shared__ double x[kHeadDim];
-    __shared__ double red_d[NT];
-    __shared__ int red_i[NT];
-    __shared__ uint16_t codes[J];
+    __shared__ double part_d[NT / 64];
+    __shared__ int part_i[NT / 64];
+    __shared__ uint16_t codes[JB];
 
-    const int ph = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int ph = blockIdx.x / P, part = blockIdx.x % P, h = blockIdx.y, b = blockIdx.z;
     const int64_t stream = (int64_t)b * a.hkv + h;
-    if (a.q_prime != nullptr && ph == 0) {      // decode-step prologue, before the key's own work:
+    if (a.q_prime != nullptr && ph == 0 && part == 0) {   // decode-step prologue, before the key's own work:
         const int G = a.hq / a.hkv, w = (int)(threadIdx.x >> 6) - 1;
         if (w >= 0 && w < G) {                  // waves 1..G: q' of this head's query group
             const int64_t vec = (int64_t)b * a.hq + h * G + w;
@@ -553,6 +576,11 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
     // cache is skipped, block-uniformly, so nothing is written out of bounds).
     const int64_t t = a.positions ? (int64_t)a.positions[b] : (int64_t)a.start_pos;
     if (t < 0 || t >= a.cap) return;
+    // Sub-vector j of the block's jj-th.
+    auto sub_of = [&](int jj) -> int {
+        if (FMT == 1 && ph == 1) return 2 * part + (jj & 1) + 8 * (jj >> 1);
+        return part * JB + jj;
+    };
     {
         const uint4* src = (const uint4*)((ph == 0 ? a.k_book : a.v_book) + (int64_t)h * E * DS);
         for (int i = threadIdx.x; i < E * DS / 8; i += NT) ((uint4*)book)[i] = src[i];
@@ -578,29 +606,41 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
     }
     __syncthreads();
     {
-        const int j = threadIdx.x / ES, sl = threadIdx.x % ES;
+        const int jj = threadIdx.x / ES, sl = threadIdx.x % ES;
+        const int j = sub_of(jj);
         double xs[DS];
 #pragma unroll
         for (int i = 0; i < DS; ++i) xs[i] = x[j * DS + i];
+        // Slice sl = entries sl, sl + ES, sl + 2 ES, ...: at every step the
+        // lanes read consecutive entries (no LDS bank conflicts).
         double best = __builtin_inf();
-        int idx = sl * EPS;
-        for (int e = sl * EPS; e < (sl + 1) * EPS; ++e) {
+        int idx = sl;
+        for (int k = 0; k < EPS; ++k) {
+            const int e = sl + k * ES;
             const double d = dist_h<DS>(xs, book + e * DS);
             if (d < best) { best = d; idx = e; }
         }
-        red_d[threadIdx.x] = best;
-        red_i[threadIdx.x] = idx;
+        group_argmin<L>(best, idx);
+        if (WPS == 1) {
+            if (sl == 0) codes[jj] = (uint16_t)idx;
+        } else if ((threadIdx.x & 63) == 0) {
+            part_d[threadIdx.x >> 6] = best;
+            part_i[threadIdx.x >> 6] = idx;
+        }
     }
     __syncthreads();
-    if (threadIdx.x < J) {
-        const int j = threadIdx.x;
-        double best = red_d[j * ES];
-        int idx = red_i[j * ES];
-        for (int sl = 1; sl < ES; ++sl)
-            if (red_d[j * ES + sl] < best) { best = red_d[j * ES + sl]; idx = red_i[j * ES + sl]; }
-        codes[j] = (uint16_t)idx;
+    if (WPS > 1 && threadIdx.x < JB) {
+        const int jj = threadIdx.x;
+        double best = part_d[jj * WPS];
+        int idx = part_i[jj * WPS];
+        for (int w = 1; w < WPS; ++w) {
+            const double d = part_d[jj * WPS + w];
+            const int i = part_i[jj * WPS + w];
+            if (d < best || (d == best && i < idx)) { best = d; idx = i; }
+        }
+        codes[jj] = (uint16_t)idx;
     }
-    __syncthreads();
+    if (WPS > 1) __syncthreads();
     // The token's 64-token block: in the stream, or (paged) the pool block the
     // table names, clamped to the pool; u = position inside the block.
     uint8_t* kblk;
@@ -616,22 +656,25 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
     }
     const int u = (int)(t & 63);
     if (FMT == 0) {
-        if (threadIdx.x < J) {
-            const int j = threadIdx.x;
-            if (ph == 0) kblk[u * W + j] = (uint8_t)codes[j];
-            else vblk[v_code_offset_2bit(u, j)] = (uint8_t)codes[j];
+        if (threadIdx.x < JB) {
+            const int j = sub_of(threadIdx.x);
+            if (ph == 0) kblk[u * W + j] = (uint8_t)codes[threadIdx.x];
+            else vblk[v_code_offset_2bit(u, j)] = (uint8_t)codes[threadIdx.x];
         }
-    } else if (threadIdx.x < J / 2) {
-        // Keys: sub-vectors (2i, 2i+1) share 3 bytes; values: (i, i + 8).
-        const int i = threadIdx.x;
-        const uint32_t c0 = ph == 0 ? codes[2 * i] : codes[i];
-        const uint32_t c1 = ph == 0 ? codes[2 * i + 1] : codes[i + 8];
-        uint8_t* p = ph == 0 ? kblk + u * W + 3 * i : vblk + v_pair_offset_1p5(u, i);
+    } else if (threadIdx.x < JB / 2) {
+        // Keys: sub-vectors (2i, 2i+1) share 3 bytes (the block's jj = 2m, 2m+1);
+        // values: (i, i + 8) (the block's jj = m, m + 2).
+        const int m = threadIdx.x;
+        const int jj0 = ph == 0 ? 2 * m : m, jj1 = ph == 0 ? 2 * m + 1 : m + 2;
+        const uint32_t c0 = codes[jj0], c1 = codes[jj1];
+        const int j0 = sub_of(jj0);
+        uint8_t* p = ph == 0 ? kblk + u * W + 3 * (j0 >> 1) : vblk + v_pair_offset_1p5(u, j0);
         p[0] = (uint8_t)(c0 & 0xff);
         p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
         p[2] = (uint8_t)(c1 >> 4);
     }
 }
+
 
 // --------------------------------------------------------- smoothing scales
 
@@ -795,7 +838,7 @@ hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
     const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
     const dim3 grid(last - first + 1, a.hkv, a.batch);
     if (a.n_new == 1 || a.positions) {
-        const dim3 g1(2, a.hkv, a.batch);
+        const dim3 g1(2 * (a.fmt == 0 ? TokenSplit<0>::P : TokenSplit<1>::P), a.hkv, a.batch);
         if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(1024), 0, stream, a);
         else hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
         return hipGetLastError();
