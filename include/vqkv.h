@@ -105,9 +105,9 @@ size_t vqkv_cache_bytes(const vqkv_shape* shape);
  * vqkv_combine reads, for `num_splits` splits; 0 if the arguments are invalid. */
 size_t vqkv_workspace_bytes(const vqkv_shape* shape, int32_t num_splits);
 
-/* Bytes of the workspace of vqkv_decode_step for `num_splits` splits (the
- * split partials plus q' and one counter per (b, KV head)); 0 if the
- * arguments are invalid. */
+/* Bytes of the workspace of the vqkv_decode_step calls for `num_splits`
+ * splits (the split partials, q', one counter per (b, KV head) and one length
+ * per sequence); 0 if the arguments are invalid. */
 size_t vqkv_step_workspace_bytes(const vqkv_shape* shape, int32_t num_splits);
 
 /* A split count that fills the GPU for this shape and context length
@@ -265,6 +265,36 @@ vqkv_status vqkv_decode_step(const vqkv_shape* shape, const void* q, const void*
                              int32_t dtype, int32_t position, const float* smooth, const uint16_t* k_book,
                              const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, float sm_scale,
                              int32_t num_splits, void* workspace, float* out, void* stream);
+
+/* The fused step for ragged batches: sequence b's new token lands at
+ * positions[b] and its queries attend to tokens [0, positions[b]].  The result
+ * is bit-identical to vqkv_quantize_append_varlen(positions),
+ * vqkv_transform_query, vqkv_decode_attention_varlen(seq_lens = positions + 1,
+ * max_seq_len) and vqkv_combine; a position outside [0, max_tokens) leaves the
+ * cache untouched and its length is clamped to [0, max_tokens] as in the
+ * varlen decode (a negative position gives a zero output).  The lengths are
+ * computed on the device into the workspace.
+ *   positions     device, int32 [B], 4-byte aligned
+ *   max_seq_len   host, 1 <= max_seq_len <= max_tokens, >= every positions[b] + 1
+ *   num_splits    host, 1 <= num_splits <= ceil(max_seq_len / 64)
+ *   other arguments as for vqkv_decode_step. */
+vqkv_status vqkv_decode_step_varlen(const vqkv_shape* shape, const void* q, const void* k_new,
+                                    const void* v_new, int32_t dtype, const int32_t* positions,
+                                    int32_t max_seq_len, const float* smooth, const uint16_t* k_book,
+                                    const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes,
+                                    float sm_scale, int32_t num_splits, void* workspace, float* out,
+                                    void* stream);
+
+/* The fused step for paged caches: as vqkv_decode_step_varlen, with the codes
+ * in a pool of 64-token blocks named by block_table (pool and table as for
+ * vqkv_decode_attention_paged); bit-identical to vqkv_quantize_append_paged,
+ * vqkv_transform_query, vqkv_decode_attention_paged and vqkv_combine. */
+vqkv_status vqkv_decode_step_paged(const vqkv_shape* shape, const void* q, const void* k_new,
+                                   const void* v_new, int32_t dtype, const int32_t* positions,
+                                   int32_t max_seq_len, const float* smooth, const uint16_t* k_book,
+                                   const uint16_t* v_book, uint8_t* k_pool, uint8_t* v_pool,
+                                   int32_t num_blocks, const int32_t* block_table, float sm_scale,
+                                   int32_t num_splits, void* workspace, float* out, void* stream);
 
 /* ------------------------------------------------- offline calibration calls */
 

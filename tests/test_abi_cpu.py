@@ -151,6 +151,24 @@ def test_decode_step_argument_checks():
     assert vq.step_workspace_bytes(shape, 0) == 0
 
 
+def test_ragged_and_paged_step_argument_checks():
+    L = vq.lib()
+    sh = ctypes.byref(vq.make_shape(2, 32, 8, 1024, vq.FMT_2BIT))
+    var = lambda pos, mx, S=1: L.vqkv_decode_step_varlen(sh, FAKE, FAKE, FAKE, 0, pos, mx, FAKE, FAKE, FAKE, FAKE,
+                                                          FAKE, 0.088, S, FAKE, FAKE, None)
+    assert var(None, 100) == INVALID                     # no positions
+    assert var(ctypes.c_void_p(FAKE.value + 2), 100) == INVALID
+    assert var(FAKE, 0) == INVALID                       # empty maximum
+    assert var(FAKE, 1025) == INVALID                    # beyond capacity
+    assert var(FAKE, 100, S=3) == INVALID                # more splits than tiles of the longest
+    pag = lambda nb, tab, pos=FAKE: L.vqkv_decode_step_paged(sh, FAKE, FAKE, FAKE, 0, pos, 100, FAKE, FAKE, FAKE,
+                                                             FAKE, FAKE, nb, tab, 0.088, 1, FAKE, FAKE, None)
+    assert pag(4, None) == INVALID
+    assert pag(0, FAKE) == INVALID
+    assert pag(4, ctypes.c_void_p(FAKE.value + 2)) == INVALID
+    assert pag(4, FAKE, pos=None) == INVALID
+
+
 def test_transform_combine_and_calibration_checks():
     L = vq.lib()
     sh = ctypes.byref(vq.make_shape(1, 4, 1, 64, vq.FMT_2BIT))

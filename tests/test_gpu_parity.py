@@ -600,6 +600,82 @@ def test_step_captured_in_a_graph_replays_exactly(fmt):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("fmt,Hq,Hkv,S,paged", [(0, 8, 2, 1, False), (0, 8, 2, 7, False), (1, 10, 2, 5, False),
+                                                (0, 8, 2, 7, True), (1, 10, 2, 3, True), (0, 32, 8, 64, True)])
+def test_decode_step_ragged_equals_the_four_calls(fmt, Hq, Hkv, S, paged):
+    """decode_step_varlen / decode_step_paged against append (varlen / paged) +
+    transform_query + decode (varlen / paged, lengths positions + 1) + combine:
+    the same output bits and cache bytes on two steps in a row (positions: the
+    first token, a ragged tail, the longest, a skipped sequence at -1 that must
+    give zeros, a block start), then the oracle per sequence."""
+    say(f"decode_step ragged fmt{fmt} Hq{Hq} Hkv{Hkv} S{S} paged={paged}")
+    pos0 = [0, 776, 4098, -1, 64]
+    B = len(pos0)
+    cap = ((max(pos0) + 2 + 63) // 64) * 64
+    W = vq.code_bytes_per_token(fmt)
+    q, s, kb, vb, kc, vc, _ = _attn_inputs(fmt, B, Hq, Hkv, max(pos0) + 2, 6100 + S, cap)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    if paged:
+        kpool, vpool, table = _paged_pool(kbytes, vbytes, W, 61 + S)
+        tab = torch.from_numpy(table).to(DEV)
+        ref_k, ref_v, got_k, got_v = dev(kpool), dev(vpool), dev(kpool), dev(vpool)
+    else:
+        ref_k, ref_v, got_k, got_v = dev(kbytes), dev(vbytes), dev(kbytes), dev(vbytes)
+    rng = np.random.default_rng(S)
+    books, sm = (book_dev(kb), book_dev(vb)), dev(s)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    ws_ref = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+    ws = torch.full((vq.step_workspace_bytes(shape, S),), 0xFF, dtype=torch.uint8, device=DEV)
+    for step in range(2):
+        pos = [p + step if p >= 0 else p for p in pos0]
+        mx = max(pos) + 1
+        pos_d = torch.tensor(pos, dtype=torch.int32, device=DEV)
+        lens_d = torch.tensor([max(p + 1, 0) for p in pos], dtype=torch.int32, device=DEV)
+        qd = dev(rng.standard_normal((B, Hq, D)).astype(np.float32), torch.bfloat16)
+        k_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), torch.bfloat16)
+        v_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), torch.bfloat16)
+        want = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+        got = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+        if paged:
+            vq.quantize_append_paged(shape, k_new, v_new, pos_d, sm, books[0], books[1], ref_k, ref_v, tab)
+            vq.transform_query(shape, qd, sm, qp)
+            vq.decode_attention_paged(shape, qp, books[0], books[1], ref_k, ref_v, tab, lens_d, mx, S, ws_ref)
+            vq.decode_step_paged(shape, qd, k_new, v_new, pos_d, mx, sm, books[0], books[1], got_k, got_v, tab, S,
+                                 ws, got)
+        else:
+            vq.quantize_append_varlen(shape, k_new, v_new, pos_d, sm, books[0], books[1], ref_k, ref_v)
+            vq.transform_query(shape, qd, sm, qp)
+            vq.decode_attention_varlen(shape, qp, books[0], books[1], ref_k, ref_v, lens_d, mx, S, ws_ref)
+            vq.decode_step_varlen(shape, qd, k_new, v_new, pos_d, mx, sm, books[0], books[1], got_k, got_v, S,
+                                  ws, got)
+        vq.combine(shape, S, ws_ref, want)
+        torch.cuda.synchronize()
+        g, w = got.cpu().numpy(), want.cpu().numpy()
+        assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), f"step {step}: max diff {np.abs(g - w).max()}"
+        assert torch.equal(got_k, ref_k) and torch.equal(got_v, ref_v)
+        assert np.all(g[3] == 0.0)
+    # The oracle per sequence on the codes the cache holds after the second step.
+    gk, gv = got_k.cpu().numpy(), got_v.cpu().numpy()
+    if paged:
+        nb = cap // 64
+        gk = np.stack([np.stack([np.concatenate([gk[table[b, h, i]] for i in range(nb)]) for h in range(Hkv)])
+                       for b in range(B)])
+        gv = np.stack([np.stack([np.concatenate([gv[table[b, h, i]] for i in range(nb)]) for h in range(Hkv)])
+                       for b in range(B)])
+    qf = qd.float().cpu().numpy()
+    for b, p in enumerate(pos):
+        if p < 0:
+            continue
+        T = p + 1
+        kcb = np.stack([oracle.unpack_k(fmt, gk[b, h], T) for h in range(Hkv)])[None]
+        vcb = np.stack([oracle.unpack_v(fmt, gv[b, h], T) for h in range(Hkv)])[None]
+        ref = oracle.attention(fmt, qf[b:b + 1], s, kb, vb, kcb, vcb)
+        err = rel_err(g[b:b + 1], ref)
+        print(f"  b={b} T={T} max relative error {err:.3e}", flush=True)
+        assert err <= TOL
+
+
 @pytest.mark.parametrize("fmt,S", [(0, 3), (1, 4), (0, 1)])
 def test_decode_step_captured_in_a_graph(fmt, S):
     """decode_step captured in a HIP graph: the prologue clears the arrival

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         "vqkv_combine": (I32, [SP, I32, P, P, P]),
         "vqkv_step_workspace_bytes": (SZ, [SP, I32]),
         "vqkv_decode_step": (I32, [SP, P, P, P, I32, I32, P, P, P, P, P, F32, I32, P, P, P]),
+        "vqkv_decode_step_varlen": (I32, [SP, P, P, P, I32, P, I32, P, P, P, P, P, F32, I32, P, P, P]),
+        "vqkv_decode_step_paged": (I32, [SP, P, P, P, I32, P, I32, P, P, P, P, P, I32, P, F32, I32, P, P, P]),
         "vqkv_decode_attention_varlen": (I32, [SP, P, P, P, P, P, P, I32, F32, I32, P, P]),
         "vqkv_quantize_append_varlen": (I32, [SP, P, P, I32, P, P, P, P, P, P, P]),
         "vqkv_decode_attention_paged": (I32, [SP, P, P, P, P, P, I32, P, P, I32, F32, I32, P, P]),
@@ -249,6 +251,51 @@ def decode_step(shape: Shape, q, k_new, v_new, position: int, smooth, k_book, v_
     _check(lib().vqkv_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
                                   position, _ptr(smooth), _ptr(k_book), _ptr(v_book), _ptr(k_codes),
                                   _ptr(v_codes), sm_scale, num_splits, _ptr(workspace), _ptr(out), _stream(q)))
+
+
+def torch_int32():
+    import torch
+    return torch.int32
+
+
+def _step_inputs(q, k_new, v_new):
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype or q.dtype != k_new.dtype:
+        raise ValueError("q, k_new and v_new must share a dtype; k_new and v_new a shape")
+    if k_new.shape[2] != 1:
+        raise ValueError("a decode step appends one token per sequence")
+
+
+def decode_step_varlen(shape: Shape, q, k_new, v_new, positions, max_seq_len: int, smooth, k_book, v_book,
+                       k_codes, v_codes, num_splits: int, workspace, out, sm_scale: float | None = None) -> None:
+    """Ragged batches: sequence b appends at positions[b] (device int32) and attends to [0, positions[b]]."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    _step_inputs(q, k_new, v_new)
+    if positions.dtype != torch_int32():
+        raise ValueError("positions must be int32")
+    _check(lib().vqkv_decode_step_varlen(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                         _ptr(positions), max_seq_len, _ptr(smooth), _ptr(k_book), _ptr(v_book),
+                                         _ptr(k_codes), _ptr(v_codes), sm_scale, num_splits, _ptr(workspace),
+                                         _ptr(out), _stream(q)))
+
+
+def decode_step_paged(shape: Shape, q, k_new, v_new, positions, max_seq_len: int, smooth, k_book, v_book,
+                      k_pool, v_pool, block_table, num_splits: int, workspace, out,
+                      sm_scale: float | None = None) -> None:
+    """decode_step_varlen over a pool of 64-token code blocks named by block_table [B][Hkv][max_tokens / 64]."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    _step_inputs(q, k_new, v_new)
+    if positions.dtype != torch_int32() or block_table.dtype != torch_int32():
+        raise ValueError("positions and block_table must be int32")
+    W = code_bytes_per_token(shape.fmt)
+    num_blocks = k_pool.numel() // (64 * W)
+    if v_pool.numel() // (64 * W) != num_blocks:
+        raise ValueError("k_pool and v_pool must hold the same number of blocks")
+    _check(lib().vqkv_decode_step_paged(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                        _ptr(positions), max_seq_len, _ptr(smooth), _ptr(k_book), _ptr(v_book),
+                                        _ptr(k_pool), _ptr(v_pool), num_blocks, _ptr(block_table), sm_scale,
+                                        num_splits, _ptr(workspace), _ptr(out), _stream(q)))
 
 
 # ------------------------------------------------------------------- calibration

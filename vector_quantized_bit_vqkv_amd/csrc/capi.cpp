@@ -124,7 +124,8 @@ size_t vqkv_step_workspace_bytes(const vqkv_shape* s, int32_t num_splits) {
     const size_t base = vqkv_workspace_bytes(s, num_splits);
     if (base == 0) return 0;
     return base + align256((size_t)s->batch * s->num_q_heads * 128 * sizeof(float)) +
-           align256((size_t)s->batch * s->num_kv_heads * sizeof(int32_t));
+           align256((size_t)s->batch * s->num_kv_heads * sizeof(int32_t)) +
+           align256((size_t)s->batch * sizeof(int32_t));
 }
 
 int32_t vqkv_suggest_splits(const vqkv_shape* s, int32_t seq_len) {
@@ -323,18 +324,39 @@ vqkv_status vqkv_decode_attention_paged(const vqkv_shape* s, const float* q_prim
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention_paged launch");
 }
 
-vqkv_status vqkv_decode_step(const vqkv_shape* s, const void* q, const void* k_new, const void* v_new,
-                             int32_t dtype, int32_t position, const float* smooth, const uint16_t* k_book,
-                             const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, float sm_scale,
-                             int32_t num_splits, void* workspace, float* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The fused step for every cache form: uniform position (positions null), or
+// one position per sequence, with (block_table) or without a block pool.
+vqkv_status decode_step_impl(const vqkv_shape* s, const void* q, const void* k_new, const void* v_new,
+                             int32_t dtype, int32_t position, const int32_t* positions, int32_t max_seq_len,
+                             const float* smooth, const uint16_t* k_book, const uint16_t* v_book,
+                             uint8_t* k_codes, uint8_t* v_codes, int32_t num_blocks, const int32_t* block_table,
+                             float sm_scale, int32_t num_splits, void* workspace, float* out, void* stream,
+                             const char* name) {
     VQKV_CHECK(check_shape(s, true));
     VQKV_CHECK(check_dtype(dtype));
-    if (position < 0 || position >= s->max_tokens)
-        return fail(VQKV_ERR_INVALID_ARG, "position %d outside [0, max_tokens = %d)", position, s->max_tokens);
-    const int seq_len = position + 1;
+    int seq_len;
+    if (positions == nullptr) {
+        if (position < 0 || position >= s->max_tokens)
+            return fail(VQKV_ERR_INVALID_ARG, "position %d outside [0, max_tokens = %d)", position, s->max_tokens);
+        seq_len = position + 1;
+    } else {
+        if ((uintptr_t)positions & 3) return fail(VQKV_ERR_INVALID_ARG, "positions is not 4-byte aligned");
+        if (max_seq_len < 1 || max_seq_len > s->max_tokens)
+            return fail(VQKV_ERR_INVALID_ARG, "max_seq_len %d outside [1, max_tokens = %d]", max_seq_len,
+                        s->max_tokens);
+        seq_len = max_seq_len;
+    }
+    if (block_table != nullptr) {
+        if (num_blocks < 1) return fail(VQKV_ERR_INVALID_ARG, "num_blocks %d < 1", num_blocks);
+        if ((uintptr_t)block_table & 3) return fail(VQKV_ERR_INVALID_ARG, "block_table is not 4-byte aligned");
+    }
     if (!std::isfinite(sm_scale)) return fail(VQKV_ERR_INVALID_ARG, "sm_scale is not finite");
     if (num_splits < 1 || num_splits > ceil_div(seq_len, 64))
-        return fail(VQKV_ERR_INVALID_ARG, "num_splits %d outside [1, ceil((position + 1) / 64) = %lld]", num_splits,
+        return fail(VQKV_ERR_INVALID_ARG, "num_splits %d outside [1, ceil(%d / 64) = %lld]", num_splits, seq_len,
                     (long long)ceil_div(seq_len, 64));
     VQKV_CHECK(check_ptr(q, "q"));
     VQKV_CHECK(check_ptr(k_new, "k_new"));
@@ -346,7 +368,7 @@ vqkv_status vqkv_decode_step(const vqkv_shape* s, const void* q, const void* k_n
     VQKV_CHECK(check_ptr(v_codes, "v_codes"));
     VQKV_CHECK(check_ptr(workspace, "workspace"));
     VQKV_CHECK(check_ptr(out, "out"));
-    // Workspace: partial o | partial lse | q' | arrival counters.
+    // Workspace: partial o | partial lse | q' | arrival counters | sequence lengths.
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     char* ws = (char*)workspace;
     float* part_o = (float*)ws;
@@ -356,15 +378,57 @@ vqkv_status vqkv_decode_step(const vqkv_shape* s, const void* q, const void* k_n
     float* q_prime = (float*)ws;
     ws += align256((size_t)s->batch * s->num_q_heads * 128 * sizeof(float));
     int32_t* arrivals = (int32_t*)ws;
-    vqkv::AppendArgs ap{k_new, v_new, dtype, 1, position, smooth, k_book, v_book, k_codes, v_codes,
-                        s->batch, s->num_kv_heads, s->max_tokens, s->fmt, nullptr, nullptr, 0,
-                        q, q_prime, arrivals, s->num_q_heads};
-    VQKV_CHECK(hip_status(vqkv::launch_quantize_append(ap, (hipStream_t)stream), "decode_step append launch"));
+    ws += align256((size_t)s->batch * s->num_kv_heads * sizeof(int32_t));
+    int32_t* seq_lens = positions ? (int32_t*)ws : nullptr;
+    vqkv::AppendArgs ap{k_new, v_new, dtype, 1, positions ? 0 : position, smooth, k_book, v_book, k_codes,
+                        v_codes, s->batch, s->num_kv_heads, s->max_tokens, s->fmt, positions, block_table,
+                        num_blocks, q, q_prime, arrivals, s->num_q_heads, seq_lens};
+    char what[64];
+    snprintf(what, sizeof(what), "%s append launch", name);
+    VQKV_CHECK(hip_status(vqkv::launch_quantize_append(ap, (hipStream_t)stream), what));
     vqkv::DecodeArgs d{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
-                       (float)((double)sm_scale * 1.4426950408889634), 3, nullptr, nullptr, 0, out, arrivals};
-    return hip_status(vqkv::launch_decode(d, (hipStream_t)stream), "decode_step decode launch");
+                       (float)((double)sm_scale * 1.4426950408889634), 3, seq_lens, block_table, num_blocks,
+                       out, arrivals};
+    snprintf(what, sizeof(what), "%s decode launch", name);
+    return hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+vqkv_status vqkv_decode_step(const vqkv_shape* s, const void* q, const void* k_new, const void* v_new,
+                             int32_t dtype, int32_t position, const float* smooth, const uint16_t* k_book,
+                             const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, float sm_scale,
+                             int32_t num_splits, void* workspace, float* out, void* stream) {
+    return decode_step_impl(s, q, k_new, v_new, dtype, position, nullptr, 0, smooth, k_book, v_book, k_codes,
+                            v_codes, 0, nullptr, sm_scale, num_splits, workspace, out, stream, "decode_step");
+}
+
+vqkv_status vqkv_decode_step_varlen(const vqkv_shape* s, const void* q, const void* k_new, const void* v_new,
+                                    int32_t dtype, const int32_t* positions, int32_t max_seq_len,
+                                    const float* smooth, const uint16_t* k_book, const uint16_t* v_book,
+                                    uint8_t* k_codes, uint8_t* v_codes, float sm_scale, int32_t num_splits,
+                                    void* workspace, float* out, void* stream) {
+    if (!positions) return fail(VQKV_ERR_INVALID_ARG, "positions is NULL");
+    return decode_step_impl(s, q, k_new, v_new, dtype, 0, positions, max_seq_len, smooth, k_book, v_book,
+                            k_codes, v_codes, 0, nullptr, sm_scale, num_splits, workspace, out, stream,
+                            "decode_step_varlen");
+}
+
+vqkv_status vqkv_decode_step_paged(const vqkv_shape* s, const void* q, const void* k_new, const void* v_new,
+                                   int32_t dtype, const int32_t* positions, int32_t max_seq_len,
+                                   const float* smooth, const uint16_t* k_book, const uint16_t* v_book,
+                                   uint8_t* k_pool, uint8_t* v_pool, int32_t num_blocks,
+                                   const int32_t* block_table, float sm_scale, int32_t num_splits,
+                                   void* workspace, float* out, void* stream) {
+    if (!positions) return fail(VQKV_ERR_INVALID_ARG, "positions is NULL");
+    if (!block_table) return fail(VQKV_ERR_INVALID_ARG, "block_table is NULL");
+    return decode_step_impl(s, q, k_new, v_new, dtype, 0, positions, max_seq_len, smooth, k_book, v_book,
+                            k_pool, v_pool, num_blocks, block_table, sm_scale, num_splits, workspace, out,
+                            stream, "decode_step_paged");
 }
 
 vqkv_status vqkv_combine(const vqkv_shape* s, int32_t num_splits, const void* workspace, float* out, void* stream) {

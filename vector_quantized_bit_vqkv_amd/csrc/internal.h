@@ -59,6 +59,8 @@ struct AppendArgs {
     float* q_prime;         // [B][Hq][128]
     int32_t* arrivals;      // [B][Hkv]
     int hq;
+    int32_t* seq_lens_out;  // [B] or null: sequence b's length after the append, positions[b] + 1
+                            // clamped to [0, cap] (with positions)
 };
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream);
 

@@ -571,6 +571,10 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
                                  a.smooth + (int64_t)h * kHeadDim, a.q_prime + vec * kHeadDim, threadIdx.x & 63);
         }
         if (threadIdx.x == 0) a.arrivals[stream] = 0;
+        if (threadIdx.x == 0 && h == 0 && a.seq_lens_out != nullptr) {
+            const int64_t pos = a.positions[b];
+            a.seq_lens_out[b] = (int32_t)(pos < 0 ? 0 : (pos >= a.cap ? a.cap : pos + 1));
+        }
     }
     // Position of the token: uniform, or per sequence (a position outside the
     // cache is skipped, block-uniformly, so nothing is written out of bounds).
