@@ -380,6 +380,23 @@ __device__ __forceinline__ uint32_t bytes3_at(const uint32_t (&w)[N]) {
     return __builtin_amdgcn_perm(w[d1], w[d], s0 | (s1 << 8) | (s2 << 16) | (0x0cu << 24));
 }
 
+// 16 x the 12-bit code at bits [12 C, 12 C + 12) of the little-endian words w,
+// OR base (whose bits 4..15 are clear): a shift or a funnel shift that puts
+// the code at bit 4, then one AND-OR.
+template <int C, int N>
+__device__ __forceinline__ uint32_t code12_x16(const uint32_t (&w)[N], uint32_t base) {
+    constexpr int S = 12 * C - 4;
+    static_assert(S + 16 <= 32 * N, "code inside the words");
+    uint32_t win;
+    if constexpr (S < 0) win = w[0] << 4;
+    else if constexpr (S % 32 + 16 <= 32) win = w[S / 32] >> (S % 32);
+    else win = __builtin_amdgcn_alignbit(w[S / 32 + 1], w[S / 32], S % 32);
+    uint32_t r;
+    // One v_and_or_b32 (left to itself the compiler splits it into an AND and an ADD).
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(win), "s"(0xfff0u), "v"(base));
+    return r;
+}
+
 // 1.5-bit: an 8-dim centroid is two 4-dim halves, so the same products run on
 // 32 "virtual" sub-vectors j' = 2j + e of 4 dims (e = half).  A score lookup
 // reads the whole 16-byte entry and feeds two products; a value lookup reads
@@ -544,10 +561,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             const uint32_t kw[6] = {dk[0].x, dk[0].y, dk[1].x, dk[1].y, dk[2].x, dk[2].y};
             static_for<0, 8>([&](auto mc) {
                 constexpr int mp = decltype(mc)::value;
-                const uint32_t x = bytes3_at<3 * mp>(kw);
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const uint32_t addr = u == 0 ? ((x << 4) & 0xfff0u) : ((x >> 8) & 0xfff0u);
+                    const uint32_t addr = u == 0 ? code12_x16<2 * mp>(kw, 0u) : code12_x16<2 * mp + 1>(kw, 0u);
                     const uint4 ent = *(const uint4*)(smem + addr);
                     const half4_t lo = __builtin_bit_cast(half4_t, make_uint2(ent.x, ent.y));
                     const half4_t hi = __builtin_bit_cast(half4_t, make_uint2(ent.z, ent.w));
@@ -622,10 +638,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                                      dv[1].z, dv[1].w, dv[2].x, dv[2].y, dv[2].z, dv[2].w};
             static_for<0, 16>([&](auto sc16) {
                 constexpr int st = decltype(sc16)::value;
-                const uint32_t x = bytes3_at<3 * st>(vw);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const uint32_t addr = hh == 0 ? (((x << 4) & 0xfff0u) | vofs) : (((x >> 8) & 0xfff0u) | vofs);
+                    const uint32_t addr = hh == 0 ? code12_x16<2 * st>(vw, vofs) : code12_x16<2 * st + 1>(vw, vofs);
                     const half4_t vv = lds_read_tr16((const lds_char*)(smem + addr));
 #pragma unroll
                     for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_bcast<st>(pt_op[hb], vv, o[hb][hh]);
