@@ -58,9 +58,10 @@ def lib():
             "vqo_transform_key": (None, [P, P, P]),
             "vqo_transform_query": (None, [P, P, P]),
             "vqo_nearest": (I, [P, P, I, I]),
-            "vqo_quantize": (I, [I, I64, P, P, P, P, P, P, P, I]),
+            "vqo_quantize": (I, [I, I64, P, P, P, P, P, P, P, P, I]),
             "vqo_kmeans": (None, [I64, I, I, P, P, I, P, P, I]),
-            "vqo_attention": (I, [I, I, I, I, I64, P, P, P, P, P, P, D, P, I]),
+            "vqo_attention": (I, [I, I, I, I, I64, P, P, P, P, P, P, P, D, P, I]),
+            "vqo_value_output_transform": (None, [P, P]),
             "vqo_attention_fp": (I, [I, I, I, I64, P, P, P, D, P, I]),
             "vqo_pack_k": (I, [I, I64, P, P]),
             "vqo_unpack_k": (I, [I, I64, P, P]),
@@ -162,17 +163,20 @@ def nearest(x, book) -> int:
     return lib().vqo_nearest(_p(x), _p(book), book.shape[0], book.shape[1])
 
 
-def quantize(fmt: int, k, v, s, kbook16, vbook16, nthreads: int | None = None):
-    """k, v: [n][128]; s: [128]; books fp16 bits [E][dsub].  Returns (kcodes, vcodes) [n][J] uint16."""
+def quantize(fmt: int, k, v, s, kbook16, vbook16, nthreads: int | None = None, sv=None):
+    """k, v: [n][128]; s: [128]; books fp16 bits [E][dsub].  Returns (kcodes, vcodes) [n][J] uint16.
+    sv: [128] value scales of the value-transform variant (values quantized as H (v / sv)), or None."""
     E, dsub = FORMATS[fmt]
     k, v, s = _f64(k), _f64(v), _f32(s)
+    sv = None if sv is None else _f32(sv)
     kb, vb = _u16(kbook16), _u16(vbook16)
     assert kb.shape == (E, dsub) and vb.shape == (E, dsub)
     n = k.shape[0]
     J = HEAD_DIM // dsub
     kc = np.zeros((n, J), dtype=np.uint16)
     vc = np.zeros((n, J), dtype=np.uint16)
-    rc = lib().vqo_quantize(fmt, n, _p(k), _p(v), _p(s), _p(kb), _p(vb), _p(kc), _p(vc),
+    rc = lib().vqo_quantize(fmt, n, _p(k), _p(v), _p(s), None if sv is None else _p(sv), _p(kb), _p(vb),
+                            _p(kc), _p(vc),
                             nthreads or default_threads())
     assert rc == 0
     return kc, vc
@@ -194,19 +198,29 @@ def kmeans(points, init_idx, iters: int = 20, nthreads: int | None = None):
 # ----------------------------------------------------------------------- attention
 
 def attention(fmt: int, q, s, kbook16, vbook16, kcodes, vcodes, sm_scale: float | None = None,
-              nthreads: int | None = None) -> np.ndarray:
-    """q [B][Hq][128]; s [Hkv][128]; books [Hkv][E][dsub] fp16 bits; codes [B][Hkv][T][J]."""
+              nthreads: int | None = None, sv=None) -> np.ndarray:
+    """q [B][Hq][128]; s [Hkv][128]; books [Hkv][E][dsub] fp16 bits; codes [B][Hkv][T][J].
+    sv: [Hkv][128] value scales of the value-transform variant (output mapped back), or None."""
     q, s = _f64(q), _f32(s)
+    sv = None if sv is None else _f32(sv)
     kb, vb, kc, vc = _u16(kbook16), _u16(vbook16), _u16(kcodes), _u16(vcodes)
     B, Hq, _ = q.shape
     _, Hkv, T, J = kc.shape
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(HEAD_DIM)
     out = np.zeros((B, Hq, HEAD_DIM), dtype=np.float64)
-    rc = lib().vqo_attention(fmt, B, Hq, Hkv, T, _p(q), _p(s), _p(kb), _p(vb), _p(kc), _p(vc),
+    rc = lib().vqo_attention(fmt, B, Hq, Hkv, T, _p(q), _p(s), None if sv is None else _p(sv), _p(kb), _p(vb),
+                             _p(kc), _p(vc),
                              float(sm_scale), _p(out), nthreads or default_threads())
     assert rc == 0
     return out
+
+
+def value_output_transform(o, sv) -> np.ndarray:
+    """o [128] -> sv * (H o): the inverse of the value transform v' = H (v / sv)."""
+    x = np.array(_f64(o), dtype=np.float64, copy=True)
+    lib().vqo_value_output_transform(_p(x), _p(_f32(sv)))
+    return x
 
 
 def attention_fp(q, k, v, sm_scale: float | None = None, nthreads: int | None = None) -> np.ndarray:

@@ -28,7 +28,11 @@
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - s_c = sqrt(max_t |Kcal[t][c]|), stored as the fp32 nearest the fp64 sqrt;
- *   - keys are divided by s before the rotation; values are not transformed;
+ *   - keys are divided by s before the rotation; values are not transformed,
+ *     except in the value-transform variant (the technical-framework paragraph
+ *     speaks of the preprocessed KV cache): values then get their own scales
+ *     s_v and the same rotation, v' = H (v / s_v), and the attention output is
+ *     mapped back, o = s_v * (H o'), since H is its own inverse;
  *   - the rotation is computed by the fast Walsh-Hadamard butterflies in stage
  *     order h = 1, 2, ..., 64, each (a, b) -> (a + b, a - b), then every element
  *     is multiplied by the fp64 nearest to 1/sqrt(128).  That pins the fp64
@@ -169,6 +173,14 @@ void vqo_transform_query(const double* q, const float* s, double* out)
     vqo_fwht(out);
 }
 
+/* Value-transform variant: the inverse of v' = H (v / s_v) applied to an
+ * attention output, o = s_v * (H o').  In place on o[128]. */
+void vqo_value_output_transform(double* o, const float* sv)
+{
+    vqo_fwht(o);
+    for (int i = 0; i < HD; ++i) o[i] = o[i] * (double)sv[i];
+}
+
 /* ------------------------------------------------------- nearest centroid */
 
 /* Index of the nearest centroid of `book` ([entries][dsub], fp64) to x[dsub]
@@ -198,11 +210,12 @@ static double* decode_book(const uint16_t* book16, int entries, int dsub)
 }
 
 /* [abstract] stages 1-2: transform new keys, then vector-quantize keys and
- * values.  k, v: [n][128] fp64 values; s: [128]; books fp16 [E][dsub].
+ * values.  k, v: [n][128] fp64 values; s: [128]; sv: [128] or NULL (values
+ * untransformed); books fp16 [E][dsub].
  * Codes out: [n][J] with J = 128 / dsub; sub-vector j covers dims
  * [j*dsub, (j+1)*dsub). */
 int vqo_quantize(int fmt, int64_t n, const double* k, const double* v, const float* s,
-                 const uint16_t* kbook16, const uint16_t* vbook16,
+                 const float* sv, const uint16_t* kbook16, const uint16_t* vbook16,
                  uint16_t* kcodes, uint16_t* vcodes, int nthreads)
 {
     int E, dsub;
@@ -212,11 +225,18 @@ int vqo_quantize(int fmt, int64_t n, const double* k, const double* v, const flo
     double* vb = decode_book(vbook16, E, dsub);
 #pragma omp parallel for num_threads(nthreads) schedule(static)
     for (int64_t t = 0; t < n; ++t) {
-        double x[HD];
+        double x[HD], xv[HD];
         vqo_transform_key(k + t * HD, s, x);
+        /* Value-transform variant (sv non-NULL): the values get the keys' steps
+         * with their own scales. */
+        const double* vt = v + t * HD;
+        if (sv) {
+            vqo_transform_key(vt, sv, xv);
+            vt = xv;
+        }
         for (int j = 0; j < J; ++j) {
             kcodes[t * J + j] = (uint16_t)vqo_nearest(x + j * dsub, kb, E, dsub);
-            vcodes[t * J + j] = (uint16_t)vqo_nearest(v + t * HD + j * dsub, vb, E, dsub);
+            vcodes[t * J + j] = (uint16_t)vqo_nearest(vt + j * dsub, vb, E, dsub);
         }
     }
     free(kb);
@@ -270,7 +290,7 @@ void vqo_kmeans(int64_t n, int dsub, int E, const double* pts, const int64_t* in
  *   q' = H (q * s_h);  z_t = sm_scale * sum_j q'_j-slice . C_K[kc_t,j];
  *   p = exp(z - max z) / sum;  o = sum_t p_t * concat_j C_V[vc_t,j]. */
 int vqo_attention(int fmt, int B, int Hq, int Hkv, int64_t T, const double* q, const float* s,
-                  const uint16_t* kbook16, const uint16_t* vbook16,
+                  const float* sv, const uint16_t* kbook16, const uint16_t* vbook16,
                   const uint16_t* kcodes, const uint16_t* vcodes, double sm_scale,
                   double* out, int nthreads)
 {
@@ -310,7 +330,10 @@ int vqo_attention(int fmt, int B, int Hq, int Hkv, int64_t T, const double* q, c
                 for (int i = 0; i < dsub; ++i) o[j * dsub + i] += w * c[i];
             }
         }
-        for (int d = 0; d < HD; ++d) out[bg * HD + d] = o[d] / l;
+        for (int d = 0; d < HD; ++d) o[d] = o[d] / l;
+        /* Value-transform variant: the output of the rotated values mapped back. */
+        if (sv) vqo_value_output_transform(o, sv + (int64_t)h * HD);
+        for (int d = 0; d < HD; ++d) out[bg * HD + d] = o[d];
         free(z);
     }
     free(kb);

@@ -372,6 +372,72 @@ def test_vq_attention_equals_full_precision_on_exact_cache(fmt):
     assert np.abs(vq - fp).max() < 1e-12
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_value_transform_quantize_recovers_codes(fmt):
+    """Value-transform variant: values built as v = sv * H(concat C_V[codes])
+    (scipy's H) quantize back to the generating codes when the quantizer is
+    given sv; without sv they do not (the values are no longer the centroids)."""
+    E, dsub = oracle.FORMATS[fmt]
+    J = D // dsub
+    rng = np.random.default_rng(40 + fmt)
+    kbook = synth.random_fp16_book(41 + fmt, (E, dsub))
+    vbook = synth.random_fp16_book(43 + fmt, (E, dsub))
+    vc = synth.random_codes(45, (40, J), E)
+    s = rng.uniform(0.7, 6.0, D).astype(np.float32)
+    sv = rng.uniform(0.5, 3.0, D).astype(np.float32)
+    H = scipy.linalg.hadamard(D) / math.sqrt(D)
+    vf = vbook.view(np.float16).astype(np.float64)
+    v = (vf[vc].reshape(40, D) @ H) * sv.astype(np.float64)
+    k = rng.standard_normal((40, D))
+    _, gv = oracle.quantize(fmt, k, v, s, kbook, vbook, sv=sv)
+    vmap = np.array([np.flatnonzero((vf == vf[e]).all(axis=1))[0] for e in range(E)])
+    assert np.array_equal(gv, vmap[vc])
+    _, raw = oracle.quantize(fmt, k, v, s, kbook, vbook)
+    assert not np.array_equal(raw, gv)
+
+
+def test_value_output_transform_undoes_the_value_transform():
+    """sv * H(H(v / sv)) = v: the output map inverts the value transform."""
+    rng = np.random.default_rng(47)
+    sv = rng.uniform(0.5, 3.0, D).astype(np.float32)
+    for _ in range(20):
+        v = rng.standard_normal(D) * rng.uniform(0.1, 30.0)
+        back = oracle.value_output_transform(oracle.transform_key(v, sv), sv)
+        assert np.abs(back - v).max() <= 1e-13 * np.abs(v).max()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_vq_attention_with_value_transform_equals_full_precision(fmt):
+    """Keys and values built exactly from centroids in the transformed spaces
+    (k = s * H k', v = sv * H v'): VQ attention with the value transform equals
+    full-precision attention over the raw cache, to fp64 rounding."""
+    E, dsub = oracle.FORMATS[fmt]
+    J = D // dsub
+    rng = np.random.default_rng(48 + fmt)
+    B, Hq, Hkv, T = 2, 6, 2, 40
+    s = rng.uniform(0.7, 6.0, (Hkv, D)).astype(np.float32)
+    sv = rng.uniform(0.5, 3.0, (Hkv, D)).astype(np.float32)
+    kbook = synth.random_fp16_book(50, (Hkv, E, dsub))
+    vbook = synth.random_fp16_book(51, (Hkv, E, dsub))
+    kc = synth.random_codes(52, (B, Hkv, T, J), E)
+    vc = synth.random_codes(53, (B, Hkv, T, J), E)
+    H = scipy.linalg.hadamard(D) / math.sqrt(D)
+    k = np.zeros((B, Hkv, T, D))
+    v = np.zeros((B, Hkv, T, D))
+    for b in range(B):
+        for h in range(Hkv):
+            kf = kbook[h].view(np.float16).astype(np.float64)
+            vf = vbook[h].view(np.float16).astype(np.float64)
+            k[b, h] = (kf[kc[b, h]].reshape(T, D) @ H) * s[h].astype(np.float64)
+            v[b, h] = (vf[vc[b, h]].reshape(T, D) @ H) * sv[h].astype(np.float64)
+    q = rng.standard_normal((B, Hq, D))
+    got = oracle.attention(fmt, q, s, kbook, vbook, kc, vc, sv=sv)
+    fp = oracle.attention_fp(q, k, v)
+    assert np.abs(got - fp).max() < 1e-12
+    plain = oracle.attention(fmt, q, s, kbook, vbook, kc, vc)
+    assert np.abs(plain - fp).max() > 1e-3          # without the output map it is wrong
+
+
 # ------------------------------------------------------------------------ packing
 
 def test_codebook_formats_golden():
