@@ -74,7 +74,14 @@ typedef enum {
 
 typedef enum {
     VQKV_FMT_2BIT = 0,          /* 256 entries x 4 dims, uint8 codes, 32 B per token */
-    VQKV_FMT_1P5BIT = 1         /* 4096 entries x 8 dims, 12-bit codes, 24 B per token */
+    VQKV_FMT_1P5BIT = 1,        /* 4096 entries x 8 dims, 12-bit codes, 24 B per token */
+    /* Flag OR'ed into either format: the value-transform variant.  The pages'
+     * technical-framework paragraph quantizes the "preprocessed KV cache"; read
+     * that way, values get their own per-channel scales s_v and the keys'
+     * rotation, v' = H (v / s_v), are coded as v', and the attention output is
+     * mapped back, o = s_v * (H o') (H is its own inverse).  Calls then take
+     * smooth as [2][Hkv][128] (the keys' scales, then the values'). */
+    VQKV_FMT_VALUE_TRANSFORM = 0x100
 } vqkv_format;
 
 typedef enum {
@@ -128,7 +135,8 @@ const char* vqkv_last_error(void);
  * Sylvester Hadamard matrix, computed in fp32 by an in-register fast
  * Walsh-Hadamard transform.  Then q'.(H (k / s)) = q.k.
  *   q        device, [B][Hq][128], dtype q_dtype (vqkv_dtype)
- *   smooth   device, fp32 [Hkv][128]
+ *   smooth   device, fp32 [Hkv][128] (with VQKV_FMT_VALUE_TRANSFORM its first
+ *            half, the keys' scales)
  *   q_prime  device, fp32 [B][Hq][128] (output)
  * Only shape->batch, num_q_heads, num_kv_heads and head_dim are used. */
 vqkv_status vqkv_transform_query(const vqkv_shape* shape, const void* q, int32_t q_dtype,
@@ -146,7 +154,9 @@ vqkv_status vqkv_transform_query(const vqkv_shape* shape, const void* q, int32_t
  *   k_new, v_new      device, [B][Hkv][n_new][128], dtype (vqkv_dtype)
  *   n_new             host, >= 1;  start_pos: host, >= 0,
  *                     start_pos + n_new <= max_tokens
- *   smooth            device, fp32 [Hkv][128]
+ *   smooth            device, fp32 [Hkv][128]; [2][Hkv][128] with
+ *                     VQKV_FMT_VALUE_TRANSFORM (the values are then coded as
+ *                     H (v / s_v) with the same steps as the keys)
  *   k_book, v_book    device, fp16 [Hkv][E][dsub]
  *   k_codes, v_codes  device, cache buffers (layout above)
  * Calls that write the same stream must not overlap in time. */
@@ -237,7 +247,9 @@ vqkv_status vqkv_quantize_append_paged(const vqkv_shape* shape, const void* k_ne
  * out[b][g] = sum_i exp(lse_i - L) o_i, L = log sum_i exp(lse_i).
  *   workspace   device, as written by vqkv_decode_attention with the same
  *               shape and num_splits
- *   out         device, fp32 [B][Hq][128] (output) */
+ *   out         device, fp32 [B][Hq][128] (output; with VQKV_FMT_VALUE_TRANSFORM
+ *               still in the rotated value space: vqkv_value_output_transform
+ *               maps it back) */
 vqkv_status vqkv_combine(const vqkv_shape* shape, int32_t num_splits, const void* workspace,
                          float* out, void* stream);
 
@@ -259,7 +271,9 @@ vqkv_status vqkv_combine(const vqkv_shape* shape, int32_t num_splits, const void
  *   workspace         device, vqkv_step_workspace_bytes(shape, num_splits)
  *                     bytes, private to the call; steps sharing a workspace
  *                     must not overlap in time
- *   out               device, fp32 [B][Hq][128] (output)
+ *   out               device, fp32 [B][Hq][128] (output; with
+ *                     VQKV_FMT_VALUE_TRANSFORM already mapped back, as
+ *                     vqkv_value_output_transform would)
  *   other arguments as for vqkv_quantize_append and vqkv_decode_attention. */
 vqkv_status vqkv_decode_step(const vqkv_shape* shape, const void* q, const void* k_new, const void* v_new,
                              int32_t dtype, int32_t position, const float* smooth, const uint16_t* k_book,
@@ -295,6 +309,18 @@ vqkv_status vqkv_decode_step_paged(const vqkv_shape* shape, const void* q, const
                                    const uint16_t* v_book, uint8_t* k_pool, uint8_t* v_pool,
                                    int32_t num_blocks, const int32_t* block_table, float sm_scale,
                                    int32_t num_splits, void* workspace, float* out, void* stream);
+
+/* Value-transform variant (shape->fmt has VQKV_FMT_VALUE_TRANSFORM): maps
+ * attention outputs of the rotated values back, in place:
+ * out[b][g] = s_v[h] * (H out[b][g]), h = g / G, with the same fp32
+ * butterflies as vqkv_transform_query, then a multiply by the fp32 nearest
+ * 1/sqrt(128) and one by s_v.  Apply it to the output of vqkv_combine; the
+ * vqkv_decode_step calls apply it themselves.
+ *   smooth   device, fp32 [2][Hkv][128] (keys' scales, then values')
+ *   out      device, fp32 [B][Hq][128], in place
+ * A shape without the flag returns VQKV_ERR_INVALID_ARG. */
+vqkv_status vqkv_value_output_transform(const vqkv_shape* shape, const float* smooth, float* out,
+                                        void* stream);
 
 /* ------------------------------------------------- offline calibration calls */
 

@@ -169,6 +169,19 @@ def test_ragged_and_paged_step_argument_checks():
     assert pag(4, FAKE, pos=None) == INVALID
 
 
+def test_value_transform_flag_checks():
+    L = vq.lib()
+    vt = vq.make_shape(2, 8, 2, 1024, vq.FMT_2BIT | vq.FMT_VALUE_TRANSFORM)
+    assert vq.cache_bytes(vt) == 2 * 2 * 1024 * 32
+    assert vq.code_bytes_per_token(vq.FMT_1P5BIT | vq.FMT_VALUE_TRANSFORM) == 24
+    assert vq.cache_bytes(vq.make_shape(2, 8, 2, 1024, 0x200)) == 0          # unknown flag
+    assert vq.code_bytes_per_token(0x201) == 0
+    plain = ctypes.byref(vq.make_shape(2, 8, 2, 1024, vq.FMT_2BIT))
+    assert L.vqkv_value_output_transform(plain, FAKE, FAKE, None) == INVALID   # nothing to undo
+    assert L.vqkv_value_output_transform(ctypes.byref(vt), None, FAKE, None) == INVALID
+    assert L.vqkv_value_output_transform(ctypes.byref(vt), FAKE, MISALIGNED, None) == INVALID
+
+
 def test_transform_combine_and_calibration_checks():
     L = vq.lib()
     sh = ctypes.byref(vq.make_shape(1, 4, 1, 64, vq.FMT_2BIT))

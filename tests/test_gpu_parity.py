@@ -186,6 +186,141 @@ def test_quantize_append_bit_exact_with_ragged_appends(fmt, dtype):
             assert np.array_equal(gv[b, h], expect_v)
 
 
+VT = vq.FMT_VALUE_TRANSFORM
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_value_transform_append_bit_exact(fmt):
+    """Value-transform variant: bulk appends (2-bit exact scan, 1.5-bit screen)
+    and one-token appends code the values as H (v / s_v), bit-exact against the
+    oracle (and not equal to the untransformed codes)."""
+    say(f"value-transform append fmt{fmt}")
+    B, Hkv, cap, n = 2, 3, 128, 70
+    case, s, kb, vb = _quant_case(fmt, B, Hkv, n, "bf16", 60 + fmt)
+    sv = np.stack([oracle.smooth_scales(case.v_cal[h]) for h in range(Hkv)])
+    J = D // oracle.FORMATS[fmt][1]
+    kc_ref = np.zeros((B, Hkv, n, J), np.uint16)
+    vc_ref = np.zeros_like(kc_ref)
+    vc_plain = np.zeros_like(kc_ref)
+    for b in range(B):
+        for h in range(Hkv):
+            kc_ref[b, h], vc_ref[b, h] = oracle.quantize(fmt, case.k[b, h], case.v[b, h], s[h], kb[h], vb[h],
+                                                         sv=sv[h])
+            _, vc_plain[b, h] = oracle.quantize(fmt, case.k[b, h], case.v[b, h], s[h], kb[h], vb[h])
+    assert not np.array_equal(vc_ref, vc_plain)
+    shape = vq.make_shape(B, Hkv, Hkv, cap, fmt | VT)
+    W = vq.code_bytes_per_token(fmt)
+    kcodes = torch.zeros((B, Hkv, cap * W), dtype=torch.uint8, device=DEV)
+    vcodes = torch.zeros_like(kcodes)
+    smooth2 = dev(np.concatenate([s, sv]))
+    for start, cnt in [(0, 64), (64, 1), (65, 5)]:
+        k_new = dev(case.k[:, :, start:start + cnt], torch.bfloat16).contiguous()
+        v_new = dev(case.v[:, :, start:start + cnt], torch.bfloat16).contiguous()
+        vq.quantize_append(shape, k_new, v_new, start, smooth2, book_dev(kb), book_dev(vb), kcodes, vcodes)
+    torch.cuda.synchronize()
+    gk, gv = kcodes.cpu().numpy(), vcodes.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            assert np.array_equal(oracle.unpack_k(fmt, gk[b, h], n), kc_ref[b, h])
+            assert np.array_equal(oracle.unpack_v(fmt, gv[b, h], n), vc_ref[b, h])
+
+
+@pytest.mark.parametrize("fmt,S", [(0, 1), (0, 7), (1, 3)])
+def test_value_transform_attention_matches_oracle(fmt, S):
+    """Value-transform variant: transform_query + decode_attention + combine +
+    value_output_transform against the oracle's attention with the output map."""
+    say(f"value-transform attention fmt{fmt} S{S}")
+    B, Hq, Hkv, T = 2, 8, 2, 1000
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, B, Hq, Hkv, T, 7000 + 10 * fmt + S)
+    sv = np.random.default_rng(S).uniform(0.5, 3.0, (Hkv, D)).astype(np.float32)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt | VT)
+    smooth2 = dev(np.concatenate([s, sv]))
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    vq.transform_query(shape, dev(q), smooth2, qp)
+    ws = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    vq.decode_attention(shape, qp, book_dev(kb), book_dev(vb), dev(kbytes), dev(vbytes), T, S, ws)
+    vq.combine(shape, S, ws, out)
+    vq.value_output_transform(shape, smooth2, out)
+    torch.cuda.synchronize()
+    ref = oracle.attention(fmt, q, s, kb, vb, kc, vc, sv=sv)
+    err = rel_err(out.cpu().numpy(), ref)
+    print(f"  max relative error {err:.3e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt,S,paged", [(0, 1, False), (0, 6, False), (1, 1, False), (1, 4, False),
+                                         (0, 5, True), (1, 3, True)])
+def test_value_transform_step_equals_the_calls(fmt, S, paged):
+    """Value-transform variant: decode_step (uniform) or decode_step_paged
+    (ragged positions) against append + transform_query + decode + combine +
+    value_output_transform: the same output bits and cache bytes; then the
+    oracle with the output map on the cache as it ends up."""
+    say(f"value-transform step fmt{fmt} S{S} paged={paged}")
+    B, Hq, Hkv = 3, 8, 2
+    pos = [777, 1500, 64] if paged else [1500] * B
+    cap = ((max(pos) + 1 + 63) // 64) * 64
+    W = vq.code_bytes_per_token(fmt)
+    q, s, kb, vb, kc, vc, _ = _attn_inputs(fmt, B, Hq, Hkv, max(pos) + 1, 7100 + 10 * fmt + S, cap)
+    sv = np.random.default_rng(S + 5).uniform(0.5, 3.0, (Hkv, D)).astype(np.float32)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt | VT)
+    smooth2 = dev(np.concatenate([s, sv]))
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    if paged:
+        kpool, vpool, table = _paged_pool(kbytes, vbytes, W, 71 + S)
+        tab = torch.from_numpy(table).to(DEV)
+        ref_k, ref_v, got_k, got_v = dev(kpool), dev(vpool), dev(kpool), dev(vpool)
+    else:
+        ref_k, ref_v, got_k, got_v = dev(kbytes), dev(vbytes), dev(kbytes), dev(vbytes)
+    rng = np.random.default_rng(S)
+    books = (book_dev(kb), book_dev(vb))
+    qd = dev(rng.standard_normal((B, Hq, D)).astype(np.float32), torch.bfloat16)
+    k_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), torch.bfloat16)
+    v_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), torch.bfloat16)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    ws_ref = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+    ws = torch.full((vq.step_workspace_bytes(shape, S),), 0xFF, dtype=torch.uint8, device=DEV)
+    want = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    got = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+    mx = max(pos) + 1
+    if paged:
+        pos_d = torch.tensor(pos, dtype=torch.int32, device=DEV)
+        lens_d = torch.tensor([p + 1 for p in pos], dtype=torch.int32, device=DEV)
+        vq.quantize_append_paged(shape, k_new, v_new, pos_d, smooth2, books[0], books[1], ref_k, ref_v, tab)
+        vq.transform_query(shape, qd, smooth2, qp)
+        vq.decode_attention_paged(shape, qp, books[0], books[1], ref_k, ref_v, tab, lens_d, mx, S, ws_ref)
+        vq.decode_step_paged(shape, qd, k_new, v_new, pos_d, mx, smooth2, books[0], books[1], got_k, got_v, tab, S,
+                             ws, got)
+    else:
+        vq.quantize_append(shape, k_new, v_new, pos[0], smooth2, books[0], books[1], ref_k, ref_v)
+        vq.transform_query(shape, qd, smooth2, qp)
+        vq.decode_attention(shape, qp, books[0], books[1], ref_k, ref_v, mx, S, ws_ref)
+        vq.decode_step(shape, qd, k_new, v_new, pos[0], smooth2, books[0], books[1], got_k, got_v, S, ws, got)
+    vq.combine(shape, S, ws_ref, want)
+    vq.value_output_transform(shape, smooth2, want)
+    torch.cuda.synchronize()
+    g, w = got.cpu().numpy(), want.cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), f"max diff {np.abs(g - w).max()}"
+    assert torch.equal(got_k, ref_k) and torch.equal(got_v, ref_v)
+    gk, gv = got_k.cpu().numpy(), got_v.cpu().numpy()
+    if paged:
+        nb = cap // 64
+        gk = np.stack([np.stack([np.concatenate([gk[table[b, h, i]] for i in range(nb)]) for h in range(Hkv)])
+                       for b in range(B)])
+        gv = np.stack([np.stack([np.concatenate([gv[table[b, h, i]] for i in range(nb)]) for h in range(Hkv)])
+                       for b in range(B)])
+    qf = qd.float().cpu().numpy()
+    for b, p in enumerate(pos):
+        T = p + 1
+        kcb = np.stack([oracle.unpack_k(fmt, gk[b, h], T) for h in range(Hkv)])[None]
+        vcb = np.stack([oracle.unpack_v(fmt, gv[b, h], T) for h in range(Hkv)])[None]
+        ref = oracle.attention(fmt, qf[b:b + 1], s, kb, vb, kcb, vcb, sv=sv)
+        err = rel_err(g[b:b + 1], ref)
+        print(f"  b={b} T={T} max relative error {err:.3e}", flush=True)
+        assert err <= TOL
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_quantize_ties_go_to_lowest_index(fmt):
     """Duplicate codebook entries and values exactly halfway between two entries."""

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libvqkv.so")
 
 FMT_2BIT = 0
 FMT_1P5BIT = 1
+FMT_VALUE_TRANSFORM = 0x100      # OR'ed into a format: values smoothed and rotated too
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 HEAD_DIM = 128
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "vqkv_decode_attention": (I32, [SP, P, P, P, P, P, I32, F32, I32, P, P]),
         "vqkv_combine": (I32, [SP, I32, P, P, P]),
         "vqkv_step_workspace_bytes": (SZ, [SP, I32]),
+        "vqkv_value_output_transform": (I32, [SP, P, P, P]),
         "vqkv_decode_step": (I32, [SP, P, P, P, I32, I32, P, P, P, P, P, F32, I32, P, P, P]),
         "vqkv_decode_step_varlen": (I32, [SP, P, P, P, I32, P, I32, P, P, P, P, P, F32, I32, P, P, P]),
         "vqkv_decode_step_paged": (I32, [SP, P, P, P, I32, P, I32, P, P, P, P, P, I32, P, F32, I32, P, P, P]),
@@ -296,6 +298,11 @@ def decode_step_paged(shape: Shape, q, k_new, v_new, positions, max_seq_len: int
                                         _ptr(positions), max_seq_len, _ptr(smooth), _ptr(k_book), _ptr(v_book),
                                         _ptr(k_pool), _ptr(v_pool), num_blocks, _ptr(block_table), sm_scale,
                                         num_splits, _ptr(workspace), _ptr(out), _stream(q)))
+
+
+def value_output_transform(shape: Shape, smooth, out) -> None:
+    """Value-transform variant: out [B][Hq][128] <- s_v * (H out) in place (smooth [2][Hkv][128])."""
+    _check(lib().vqkv_value_output_transform(ctypes.byref(shape), _ptr(smooth), _ptr(out), _stream(out)))
 
 
 # ------------------------------------------------------------------- calibration

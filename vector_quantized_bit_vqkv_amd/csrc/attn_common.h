@@ -3,6 +3,7 @@
 
 #include "device_util.h"
 #include "internal.h"
+#include "qtransform.h"
 
 namespace vqkv {
 
@@ -96,8 +97,9 @@ __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeAr
             o = O / L;
             lse = M + (__builtin_log2f(L) - l_log2_scale);
         }
-        if (stage != nullptr && a.out != nullptr && a.splits > 1) {
-            // Fused combine: the partial waits in LDS for combine_if_last.
+        if (stage != nullptr && a.out != nullptr && (a.splits > 1 || a.v_smooth != nullptr)) {
+            // Fused combine (the partial waits in LDS for combine_if_last), or one
+            // split of the value-transform variant (o waits for its output map).
             stage[g * kHeadDim + d] = o;
             if (d == 0) stage[G * kHeadDim + g] = lse;
         } else if (a.out != nullptr && a.splits == 1) {
@@ -121,7 +123,8 @@ __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeAr
 // flight.  It has block barriers: every thread of the block calls it, threads
 // of an inactive group only pass the barriers.
 __device__ __forceinline__ void combine_row(const float* part_o, const float* part_lse, float* out, int S,
-                                            int64_t bg, int d, bool active, float* red, float* wts) {
+                                            int64_t bg, int d, bool active, float* red, float* wts,
+                                            float* lds_row = nullptr) {
     const int lane = d & 63, wave = d >> 6;
     const float* lse = part_lse + bg * S;
     float M = kNegInf;
@@ -155,7 +158,11 @@ __device__ __forceinline__ void combine_row(const float* part_o, const float* pa
     if (lane == 0) red[wave] = den;
     __syncthreads();
     den = red[0] + red[1];
-    if (active) out[bg * kHeadDim + d] = den > 0.0f ? num / den : 0.0f;
+    const float r = den > 0.0f ? num / den : 0.0f;
+    if (active) {
+        if (lds_row != nullptr) lds_row[d] = r;            // the caller maps the row back
+        else out[bg * kHeadDim + d] = r;
+    }
 }
 
 // Fused combine after merge_waves(..., stage), for more than one split.
@@ -195,8 +202,17 @@ __device__ __forceinline__ void combine_if_last(unsigned char* smem, const float
     if (!*last) return;                                     // block-uniform
     const int grp = threadIdx.x >> 7;
     const bool active = grp < G;
+    // Value-transform variant: the combined rows wait in LDS for the output map.
+    float* rows = a.v_smooth != nullptr ? (float*)(smem + 4352) : nullptr;   // G x 128 floats
     combine_row(a.part_o, a.part_lse, a.out, a.splits, (int64_t)b * a.hq + h * G + (active ? grp : 0),
-                threadIdx.x & 127, active, red + 2 * grp, wts + 128 * grp);
+                threadIdx.x & 127, active, red + 2 * grp, wts + 128 * grp, rows ? rows + 128 * grp : nullptr);
+    if (rows != nullptr) {                                  // block-uniform
+        __syncthreads();
+        const int wave = threadIdx.x >> 6;
+        if (wave < G)
+            value_untransform_wave(rows + 128 * wave, a.v_smooth + (int64_t)h * kHeadDim,
+                                   a.out + ((int64_t)b * a.hq + h * G + wave) * kHeadDim, threadIdx.x & 63);
+    }
     if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + stream, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -36,6 +36,13 @@ vqkv_status hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The code format without the variant flag, and the values' scales of the
+// value-transform variant (the second half of smooth) or null.
+int base_fmt(int fmt) { return fmt & 0xff; }
+const float* value_scales(const vqkv_shape* s, const float* smooth) {
+    return (s->fmt & VQKV_FMT_VALUE_TRANSFORM) ? smooth + (int64_t)s->num_kv_heads * 128 : nullptr;
+}
+
 int entries_of(int fmt) { return fmt == VQKV_FMT_2BIT ? 256 : 4096; }
 int dsub_of(int fmt) { return fmt == VQKV_FMT_2BIT ? 4 : 8; }
 
@@ -54,7 +61,8 @@ vqkv_status check_shape(const vqkv_shape* s, bool need_cache) {
     if ((int64_t)s->batch * s->num_q_heads > (1 << 24))
         return fail(VQKV_ERR_UNSUPPORTED, "batch * Hq too large");
     if (need_cache) {
-        if (s->fmt != VQKV_FMT_2BIT && s->fmt != VQKV_FMT_1P5BIT)
+        if ((base_fmt(s->fmt) != VQKV_FMT_2BIT && base_fmt(s->fmt) != VQKV_FMT_1P5BIT) ||
+            (s->fmt & ~(0xff | VQKV_FMT_VALUE_TRANSFORM)) != 0)
             return fail(VQKV_ERR_INVALID_ARG, "unknown format %d", s->fmt);
         if (s->max_tokens < 64 || s->max_tokens % 64 != 0)
             return fail(VQKV_ERR_INVALID_ARG, "max_tokens %d must be a positive multiple of 64", s->max_tokens);
@@ -104,8 +112,9 @@ int decode_path_from_env() {
 extern "C" {
 
 size_t vqkv_code_bytes_per_token(int32_t fmt) {
-    if (fmt == VQKV_FMT_2BIT) return 32;
-    if (fmt == VQKV_FMT_1P5BIT) return 24;
+    if ((fmt & ~(0xff | VQKV_FMT_VALUE_TRANSFORM)) != 0) return 0;
+    if (base_fmt(fmt) == VQKV_FMT_2BIT) return 32;
+    if (base_fmt(fmt) == VQKV_FMT_1P5BIT) return 24;
     return 0;
 }
 
@@ -179,7 +188,8 @@ vqkv_status vqkv_quantize_append(const vqkv_shape* s, const void* k_new, const v
     VQKV_CHECK(check_ptr(k_codes, "k_codes"));
     VQKV_CHECK(check_ptr(v_codes, "v_codes"));
     vqkv::AppendArgs a{k_new, v_new, dtype, n_new, start_pos, smooth, k_book, v_book, k_codes, v_codes,
-                       s->batch, s->num_kv_heads, s->max_tokens, s->fmt};
+                       s->batch, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt)};
+    a.v_smooth = value_scales(s, smooth);
     return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append launch");
 }
 
@@ -198,7 +208,8 @@ vqkv_status vqkv_quantize_append_varlen(const vqkv_shape* s, const void* k_new, 
     VQKV_CHECK(check_ptr(k_codes, "k_codes"));
     VQKV_CHECK(check_ptr(v_codes, "v_codes"));
     vqkv::AppendArgs a{k_new, v_new, dtype, 1, 0, smooth, k_book, v_book, k_codes, v_codes,
-                       s->batch, s->num_kv_heads, s->max_tokens, s->fmt, positions};
+                       s->batch, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt), positions};
+    a.v_smooth = value_scales(s, smooth);
     return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append_varlen launch");
 }
 
@@ -221,7 +232,8 @@ vqkv_status vqkv_quantize_append_paged(const vqkv_shape* s, const void* k_new, c
     VQKV_CHECK(check_ptr(k_pool, "k_pool"));
     VQKV_CHECK(check_ptr(v_pool, "v_pool"));
     vqkv::AppendArgs a{k_new, v_new, dtype, 1, 0, smooth, k_book, v_book, k_pool, v_pool,
-                       s->batch, s->num_kv_heads, s->max_tokens, s->fmt, positions, block_table, num_blocks};
+                       s->batch, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt), positions, block_table, num_blocks};
+    a.v_smooth = value_scales(s, smooth);
     return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append_paged launch");
 }
 
@@ -247,10 +259,10 @@ vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, con
     float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
     const int path = decode_path_from_env();
     const int G = s->num_q_heads / s->num_kv_heads;
-    if (path == 1 && !(s->fmt == VQKV_FMT_2BIT && G <= 4))
+    if (path == 1 && !(base_fmt(s->fmt) == VQKV_FMT_2BIT && G <= 4))
         return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
     vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
-                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
+                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), path};
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention launch");
@@ -280,10 +292,10 @@ vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* s, const float* q_pri
     float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
     const int path = decode_path_from_env();
     const int G = s->num_q_heads / s->num_kv_heads;
-    if (path == 1 && !(s->fmt == VQKV_FMT_2BIT && G <= 4))
+    if (path == 1 && !(base_fmt(s->fmt) == VQKV_FMT_2BIT && G <= 4))
         return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
     vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
-                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
+                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), path, seq_lens};
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention_varlen launch");
@@ -318,7 +330,7 @@ vqkv_status vqkv_decode_attention_paged(const vqkv_shape* s, const float* q_prim
     float* part_o = (float*)workspace;
     float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
     vqkv::DecodeArgs a{q_prime, k_book, v_book, k_pool, v_pool, part_o, part_lse,
-                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
+                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), 0, seq_lens, block_table, num_blocks};
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention_paged launch");
@@ -381,16 +393,17 @@ vqkv_status decode_step_impl(const vqkv_shape* s, const void* q, const void* k_n
     ws += align256((size_t)s->batch * s->num_kv_heads * sizeof(int32_t));
     int32_t* seq_lens = positions ? (int32_t*)ws : nullptr;
     vqkv::AppendArgs ap{k_new, v_new, dtype, 1, positions ? 0 : position, smooth, k_book, v_book, k_codes,
-                        v_codes, s->batch, s->num_kv_heads, s->max_tokens, s->fmt, positions, block_table,
+                        v_codes, s->batch, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt), positions, block_table,
                         num_blocks, q, q_prime, arrivals, s->num_q_heads, seq_lens};
     char what[64];
     snprintf(what, sizeof(what), "%s append launch", name);
+    ap.v_smooth = value_scales(s, smooth);
     VQKV_CHECK(hip_status(vqkv::launch_quantize_append(ap, (hipStream_t)stream), what));
     vqkv::DecodeArgs d{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
-                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, s->fmt,
+                       s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), 3, seq_lens, block_table, num_blocks,
-                       out, arrivals};
+                       out, arrivals, value_scales(s, smooth)};
     snprintf(what, sizeof(what), "%s decode launch", name);
     return hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what);
 }
@@ -441,6 +454,16 @@ vqkv_status vqkv_combine(const vqkv_shape* s, int32_t num_splits, const void* wo
     const float* part_lse = (const float*)((const char*)workspace + align256(rows * 128 * sizeof(float)));
     vqkv::CombineArgs a{part_o, part_lse, out, s->batch, s->num_q_heads, num_splits};
     return hip_status(vqkv::launch_combine(a, (hipStream_t)stream), "combine launch");
+}
+
+vqkv_status vqkv_value_output_transform(const vqkv_shape* s, const float* smooth, float* out, void* stream) {
+    VQKV_CHECK(check_shape(s, true));
+    if (!(s->fmt & VQKV_FMT_VALUE_TRANSFORM))
+        return fail(VQKV_ERR_INVALID_ARG, "the shape's format has no value transform to undo");
+    VQKV_CHECK(check_ptr(smooth, "smooth"));
+    VQKV_CHECK(check_ptr(out, "out"));
+    vqkv::ValueOutputArgs a{out, value_scales(s, smooth), s->batch, s->num_q_heads, s->num_kv_heads};
+    return hip_status(vqkv::launch_value_output_transform(a, (hipStream_t)stream), "value_output_transform launch");
 }
 
 vqkv_status vqkv_smooth_scales(int32_t num_kv_heads, int32_t n_cal, const void* k_cal, int32_t dtype,

@@ -697,7 +697,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     float* stage = scratch + NW * G * (kHeadDim + 2);       // after the merge scratch
     static_assert(SMEM >= MERGE_BYTES + G * (kHeadDim + 1) * 4, "LDS holds the merge scratch and the stage");
     merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2, stage);
-    if (a.out != nullptr && a.splits > 1) combine_if_last<G, NW>(smem, stage, a, b, h);
+    if (a.out != nullptr && a.splits > 1) {
+        combine_if_last<G, NW>(smem, stage, a, b, h);
+    } else if (a.out != nullptr && a.v_smooth != nullptr) {
+        // One split of the value-transform variant: the merged o (staged in LDS)
+        // mapped back, one wave per query head.
+        __syncthreads();
+        if (wave < G)
+            value_untransform_wave(stage + kHeadDim * wave, a.v_smooth + (int64_t)h * kHeadDim,
+                                   a.out + ((int64_t)b * a.hq + h * G + wave) * kHeadDim, lane);
+    }
 }
 
 // ------------------------------------------------------------------ gather path

@@ -61,6 +61,7 @@ struct AppendArgs {
     int hq;
     int32_t* seq_lens_out;  // [B] or null: sequence b's length after the append, positions[b] + 1
                             // clamped to [0, cap] (with positions)
+    const float* v_smooth;  // [Hkv][128] or null: value-transform variant, values coded as H (v / s_v)
 };
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream);
 
@@ -85,6 +86,7 @@ struct DecodeArgs {
     // combines the head's splits into out and clears the counter.
     float* out;             // [B][Hq][128]
     int32_t* arrivals;      // [B][Hkv]
+    const float* v_smooth;  // [Hkv][128] or null: with out, the output is mapped back, s_v * (H o)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
@@ -95,6 +97,14 @@ struct CombineArgs {
     int batch, hq, splits;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// Value-transform variant: out[b][g] = s_v[h] * (H out[b][g]) in place.
+struct ValueOutputArgs {
+    float* out;             // [B][Hq][128]
+    const float* v_smooth;  // [Hkv][128]
+    int batch, hq, hkv;
+};
+hipError_t launch_value_output_transform(const ValueOutputArgs& a, hipStream_t stream);
 
 // Offline calibration.
 hipError_t launch_smooth_scales(int hkv, int n_cal, const void* k_cal, int dtype, float* smooth,

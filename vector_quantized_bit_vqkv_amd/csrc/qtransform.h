@@ -56,4 +56,32 @@ __device__ __forceinline__ void transform_query_wave(const void* q, int dtype, c
     *((float2*)q_prime + lane) = out;
 }
 
+// Value-transform variant: out = s_v * (H o) for one fp32 output row o (the
+// inverse of v' = H (v / s_v)), by one wave, with the butterflies above: lane
+// i holds elements 2i and 2i+1, then one multiply by 1/sqrt(128) and one by
+// s_v.  `in` and `out` may be the same row (every lane reads before it
+// writes), in global memory or LDS.
+__device__ __forceinline__ void value_untransform_wave(const float* in, const float* sv, float* out, int lane) {
+#pragma clang fp contract(off)
+    const float2 w = *((const float2*)in + lane);
+    float x0 = w.x, x1 = w.y;
+    {
+        const float a0 = x0, b0 = x1;
+        x0 = a0 + b0;
+        x1 = a0 - b0;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(x0, m, 64);
+        const float p1 = __shfl_xor(x1, m, 64);
+        const bool upper = (lane & m) != 0;
+        x0 = upper ? p0 - x0 : x0 + p0;
+        x1 = upper ? p1 - x1 : x1 + p1;
+    }
+    float2 r;
+    r.x = (x0 * kInvSqrtHeadDimF) * sv[2 * lane];
+    r.y = (x1 * kInvSqrtHeadDimF) * sv[2 * lane + 1];
+    *((float2*)out + lane) = r;
+}
+
 }  // namespace vqkv

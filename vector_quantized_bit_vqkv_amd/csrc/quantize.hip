@@ -323,9 +323,16 @@ __global__ __launch_bounds__(1024) void quantize_screen_kernel(AppendArgs a) {
     const int P = nt * J;                       // points per phase, contiguous from row off
     for (int phase = 0; phase < 2; ++phase) {
         if (phase == 1) {
+            // Values; in the value-transform variant divided by s_v and rotated like the keys.
+            const float* sv = a.v_smooth ? a.v_smooth + (int64_t)h * kHeadDim : nullptr;
             for (int idx = threadIdx.x; idx < nt * kHeadDim; idx += blockDim.x) {
                 const int r = idx / kHeadDim, c = idx % kHeadDim;
-                x[(off + r) * kHeadDim + c] = load_elem_d(a.v_new, (row0 + r) * kHeadDim + c, a.dtype);
+                const double e = load_elem_d(a.v_new, (row0 + r) * kHeadDim + c, a.dtype);
+                x[(off + r) * kHeadDim + c] = sv ? e / (double)sv[c] : e;
+            }
+            if (sv) {                                       // block-uniform
+                __syncthreads();
+                block_fwht(x + off * kHeadDim, nt);
             }
         }
         const uint4* src = (const uint4*)((phase == 0 ? a.k_book : a.v_book) + (int64_t)h * E * DS);
@@ -444,6 +451,15 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
     while (ES * 2 * P <= 256 && ES * 2 <= E / 16) ES *= 2;
 
     for (int phase = 0; phase < 2; ++phase) {
+        if (phase == 1 && a.v_smooth != nullptr) {         // value-transform variant: x = H (v / s_v)
+            const float* sv = a.v_smooth + (int64_t)h * kHeadDim;
+            for (int idx = threadIdx.x; idx < nt * kHeadDim; idx += blockDim.x) {
+                const int r = idx / kHeadDim, c = idx % kHeadDim;
+                xk[(off + r) * kHeadDim + c] = load_elem_d(a.v_new, (row0 + r) * kHeadDim + c, a.dtype) / (double)sv[c];
+            }
+            __syncthreads();
+            block_fwht(xk + off * kHeadDim, nt);
+        }
         const uint16_t* src = (phase == 0 ? a.k_book : a.v_book) + (int64_t)h * E * DS;
         for (int i = threadIdx.x; i < E * DS; i += blockDim.x) book[i] = half_bits_to_float(src[i]);
         __syncthreads();
@@ -452,7 +468,7 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
             const int pt = it / ES, sl = it % ES;
             const int r = pt / J, j = pt % J;
             double x[DS];
-            if (phase == 0) {
+            if (phase == 0 || a.v_smooth != nullptr) {
 #pragma unroll
                 for (int i = 0; i < DS; ++i) x[i] = xk[(off + r) * kHeadDim + j * DS + i];
             } else {
@@ -590,13 +606,14 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
         for (int i = threadIdx.x; i < E * DS / 8; i += NT) ((uint4*)book)[i] = src[i];
         if (threadIdx.x < kHeadDim) {
             const int c = threadIdx.x;
-            x[c] = ph == 0 ? load_elem_d(a.k_new, stream * kHeadDim + c, a.dtype) /
-                                 (double)a.smooth[(int64_t)h * kHeadDim + c]
-                           : load_elem_d(a.v_new, stream * kHeadDim + c, a.dtype);
+            // Keys, and values of the value-transform variant: divided by their scales.
+            const float* div = ph == 0 ? a.smooth : a.v_smooth;
+            const double e = load_elem_d(ph == 0 ? a.k_new : a.v_new, stream * kHeadDim + c, a.dtype);
+            x[c] = div ? e / (double)div[(int64_t)h * kHeadDim + c] : e;
         }
     }
     __syncthreads();
-    if (ph == 0 && threadIdx.x < 64) {
+    if ((ph == 0 || a.v_smooth != nullptr) && threadIdx.x < 64) {   // the rotation (block-uniform)
         const int l = threadIdx.x;
         double lo = x[l], hi = x[l + 64];
         for (int st = 1; st < 64; st <<= 1) {
