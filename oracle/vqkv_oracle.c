@@ -21,7 +21,8 @@
  *     so q'.k' == q.k ([card] Summary; [abstract]);
  *   - nearest-centroid codes under squared L2 over contiguous sub-vectors,
  *     ties to the lowest index, with codebooks of 2^8 x 4 (2-bit) or
- *     2^12 x 8 (1.5-bit) fp16 entries ([card] Key points, codebook size);
+ *     2^12 x 8 (1.5-bit) fp16 entries ([card] Key points, codebook size), and
+ *     a third width inside the pages' 1.25-4 bit range, 2^12 x 4 (3-bit);
  *   - offline K-Means (Lloyd) codebooks ([card] Summary, "trained offline");
  *   - exact softmax attention over the dequantized cache, one query head at a
  *     time (the definition the fused kernel must reproduce; [abstract]).
@@ -63,8 +64,15 @@ int vqo_format(int fmt, int* entries, int* dsub)
      * 2^12 entries x 8 dims for 1.5 bits. */
     if (fmt == 0) { *entries = 256; *dsub = 4; return 0; }
     if (fmt == 1) { *entries = 4096; *dsub = 8; return 0; }
+    /* A third bit-width inside the pages' 1.25-4 bit range (their results
+     * span it; the shape is not printed): 2^12 entries x 4 dims, 3 bits per
+     * element. */
+    if (fmt == 2) { *entries = 4096; *dsub = 4; return 0; }
     return -1;
 }
+
+/* Bytes of one token's codes per (b, KV head): 32 (2-bit), 24 (1.5-bit), 48 (3-bit). */
+static int code_bytes(int fmt) { return fmt == 0 ? 32 : (fmt == 1 ? 24 : 48); }
 
 /* ------------------------------------------------------------------ fp16 */
 
@@ -417,7 +425,7 @@ int vqo_pack_k(int fmt, int64_t T, const uint16_t* codes, uint8_t* out)
         for (int j = 0; j < J; ++j) {
             uint16_t c = codes[t * J + j];
             if (fmt == 0) out[t * 32 + j] = (uint8_t)c;
-            else put12(out + t * 24 + 3 * (j / 2), j & 1, c);
+            else put12(out + t * code_bytes(fmt) + 3 * (j / 2), j & 1, c);
         }
     return 0;
 }
@@ -429,7 +437,7 @@ int vqo_unpack_k(int fmt, int64_t T, const uint8_t* in, uint16_t* codes)
     int J = HD / dsub;
     for (int64_t t = 0; t < T; ++t)
         for (int j = 0; j < J; ++j)
-            codes[t * J + j] = fmt == 0 ? in[t * 32 + j] : get12(in + t * 24 + 3 * (j / 2), j & 1);
+            codes[t * J + j] = fmt == 0 ? in[t * 32 + j] : get12(in + t * code_bytes(fmt) + 3 * (j / 2), j & 1);
     return 0;
 }
 
@@ -443,6 +451,16 @@ static int64_t v_offset(int fmt, int64_t t, int j, int* which)
         int64_t chunk = 16 * ((j % 16) / 4) + 4 * (u % 4) + (j % 4);
         *which = 0;
         return (t / 64) * 2048 + 32 * chunk + 2 * (u / 4) + j / 16;
+    }
+    if (fmt == 2) {
+        /* 64-token blocks of 3072 bytes, 64 chunks of 48 bytes.  Chunk
+           16*((j%16)/4) + 4*(u%4) + j%4 (u = t % 64, as in the 2-bit layout)
+           holds, in bytes 3*(u/4)..3*(u/4)+2, the pair (sub-vector j%16,
+           sub-vector j%16 + 16) of token t; sub-vector j is element j/16. */
+        int64_t u = t % 64;
+        int64_t chunk = 16 * ((j % 16) / 4) + 4 * (u % 4) + (j % 4);
+        *which = j / 16;
+        return (t / 64) * 3072 + 48 * chunk + 3 * (u / 4);
     }
     {
         /* 64-token blocks of 1536 bytes, 32 streams of 48 bytes.  Stream

@@ -514,6 +514,52 @@ def test_pack_2bit_positions():
     assert np.array_equal(oracle.unpack_k(0, kb, T), c)
 
 
+def test_pack_3bit_positions():
+    """Hand-computed positions of the 3-bit layouts (2^12 x 4, 12-bit codes):
+    keys token-major, 48 bytes per token, pairs (2i, 2i+1) in bytes 3i..3i+2;
+    values in 64-token blocks of 3072 bytes, (t, j) -> chunk
+    16*((j%16)//4) + 4*(u%4) + j%4 (u = t % 64), bytes 3*(u//4)..+2 of that
+    48-byte chunk, element j // 16 of the pair (j%16, j%16 + 16)."""
+    T = 130
+    c = synth.random_codes(5, (T, 32), 4096)
+    kb = oracle.pack_k(2, c, 192)
+    vb = oracle.pack_v(2, c, 192)
+    assert kb.size == vb.size == 192 * 48
+
+    def pair(buf, off):
+        b0, b1, b2 = (int(x) for x in buf[off:off + 3])
+        return b0 | ((b1 & 0xF) << 8), (b1 >> 4) | (b2 << 4)
+    assert pair(kb, 0) == (c[0, 0], c[0, 1])
+    assert pair(kb, 48 * 7 + 3 * 15) == (c[7, 30], c[7, 31])
+    assert pair(vb, 0) == (c[0, 0], c[0, 16])                       # chunk 0
+    assert pair(vb, 48 * 23) == (c[1, 7], c[1, 23])                 # chunk 16 + 4 + 3
+    assert pair(vb, 48 * 23 + 24) == (c[33, 7], c[33, 23])          # same chunk, u // 4 = 8
+    assert pair(vb, 3072 + 48 * 63 + 21) == (c[95, 15], c[95, 31])  # block 1, u = 31: 48 + 12 + 3
+    assert pair(vb, 2 * 3072 + 48 * 1 + 0) == (c[128, 1], c[128, 17])  # block 2, u = 0, j = 1: chunk 1
+    assert np.array_equal(oracle.unpack_k(2, kb, T), c)
+    assert np.array_equal(oracle.unpack_v(2, vb, T), c)
+
+
+def test_3bit_format_is_twelve_bits_per_four_dims():
+    """The third width: 4096 entries of 4 dims, so 12 bits per 4 elements
+    (3 bits each, inside the pages' 1.25-4 bit range) and 32 codes, 48 bytes,
+    per token; quantizing keys built from its centroids recovers their codes."""
+    E, dsub = oracle.FORMATS[2]
+    assert (E, dsub) == (4096, 4)
+    assert math.log2(E) / dsub == 3.0 and oracle.code_bytes_per_token(2) * 8 == 12 * 32
+    rng = np.random.default_rng(77)
+    kbook = synth.random_fp16_book(78, (E, dsub))
+    vbook = synth.random_fp16_book(79, (E, dsub))
+    kc = synth.random_codes(80, (30, 32), E)
+    s = rng.uniform(0.7, 6.0, D).astype(np.float32)
+    H = scipy.linalg.hadamard(D) / math.sqrt(D)
+    kf = kbook.view(np.float16).astype(np.float64)
+    k = (kf[kc].reshape(30, D) @ H) * s.astype(np.float64)
+    gk, _ = oracle.quantize(2, k, rng.standard_normal((30, D)), s, kbook, vbook)
+    kmap = np.array([np.flatnonzero((kf == kf[e]).all(axis=1))[0] for e in range(E)])
+    assert np.array_equal(gk, kmap[kc])
+
+
 # ------------------------------------------------------------------------ K-Means
 
 def _blobs(seed, E, dsub, per):
