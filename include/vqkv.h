@@ -39,7 +39,8 @@
  *   byte j holds the code of sub-vector j (dims 4j..4j+3).  1.5-bit: the
  *   12-bit codes of sub-vectors 2i and 2i+1 (dims 8*2i.. and 8*(2i+1)..) share
  *   bytes 3i..3i+2 as b0 = c0 & 0xFF, b1 = (c0 >> 8) | ((c1 & 0xF) << 4),
- *   b2 = c1 >> 4.
+ *   b2 = c1 >> 4.  3-bit: the same 12-bit pairs for sub-vectors 2i and 2i+1
+ *   (dims 4*2i..), 48 bytes per token.
  * - Value codes, blocked by tokens and arranged so that every lane of the
  *   decode kernel reads its codes for a block with one wide load.  2-bit:
  *   blocks of 64 tokens, 2048 bytes each, cut into 64 chunks of 32 bytes;
@@ -48,7 +49,10 @@
  *   1.5-bit: blocks of 64 tokens, 1536 bytes each, cut into 32 streams of 48
  *   bytes; the codes of sub-vectors j and j + 8 (j < 8) of token t form one
  *   12-bit pair (c0 = sub-vector j, packed by the rule above) in stream
- *   8*(j/2) + 2*(u%4) + j%2, bytes 3*(u/4)..3*(u/4)+2.
+ *   8*(j/2) + 2*(u%4) + j%2, bytes 3*(u/4)..3*(u/4)+2.  3-bit: blocks of 64
+ *   tokens, 3072 bytes each, cut into 64 chunks of 48 bytes; the codes of
+ *   sub-vectors j and j + 16 (j < 16) of token t form one 12-bit pair in chunk
+ *   16*(j/4) + 4*(u%4) + j%4 (as in the 2-bit layout), bytes 3*(u/4)..+2.
  * - Codebooks: fp16 [Hkv][E][dsub], one for keys and one for values per KV
  *   head, shared by every sub-vector position.  Key codebooks live in the
  *   rotated space.
@@ -75,6 +79,10 @@ typedef enum {
 typedef enum {
     VQKV_FMT_2BIT = 0,          /* 256 entries x 4 dims, uint8 codes, 32 B per token */
     VQKV_FMT_1P5BIT = 1,        /* 4096 entries x 8 dims, 12-bit codes, 24 B per token */
+    /* A third width inside the pages' 1.25-4 bit range (the pages report that
+     * range but print only the two shapes above): 4096 entries x 4 dims,
+     * 12-bit codes, 3 bits per element, 48 B per token. */
+    VQKV_FMT_3BIT = 2,
     /* Flag OR'ed into either format: the value-transform variant.  The pages'
      * technical-framework paragraph quantizes the "preprocessed KV cache"; read
      * that way, values get their own per-channel scales s_v and the keys'

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libvqkv.so")
 
 FMT_2BIT = 0
 FMT_1P5BIT = 1
+FMT_3BIT = 2                      # 4096 x 4: a third width inside the pages' 1.25-4 bit range
 FMT_VALUE_TRANSFORM = 0x100      # OR'ed into a format: values smoothed and rotated too
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1

@@ -44,7 +44,8 @@ const float* value_scales(const vqkv_shape* s, const float* smooth) {
 }
 
 int entries_of(int fmt) { return fmt == VQKV_FMT_2BIT ? 256 : 4096; }
-int dsub_of(int fmt) { return fmt == VQKV_FMT_2BIT ? 4 : 8; }
+int dsub_of(int fmt) { return fmt == VQKV_FMT_1P5BIT ? 8 : 4; }
+bool known_fmt(int fmt) { return fmt == VQKV_FMT_2BIT || fmt == VQKV_FMT_1P5BIT || fmt == VQKV_FMT_3BIT; }
 
 // Checks shared by every call that takes a shape.  `need_cache` adds the
 // capacity and format checks.
@@ -61,7 +62,7 @@ vqkv_status check_shape(const vqkv_shape* s, bool need_cache) {
     if ((int64_t)s->batch * s->num_q_heads > (1 << 24))
         return fail(VQKV_ERR_UNSUPPORTED, "batch * Hq too large");
     if (need_cache) {
-        if ((base_fmt(s->fmt) != VQKV_FMT_2BIT && base_fmt(s->fmt) != VQKV_FMT_1P5BIT) ||
+        if (!known_fmt(base_fmt(s->fmt)) ||
             (s->fmt & ~(0xff | VQKV_FMT_VALUE_TRANSFORM)) != 0)
             return fail(VQKV_ERR_INVALID_ARG, "unknown format %d", s->fmt);
         if (s->max_tokens < 64 || s->max_tokens % 64 != 0)
@@ -115,6 +116,7 @@ size_t vqkv_code_bytes_per_token(int32_t fmt) {
     if ((fmt & ~(0xff | VQKV_FMT_VALUE_TRANSFORM)) != 0) return 0;
     if (base_fmt(fmt) == VQKV_FMT_2BIT) return 32;
     if (base_fmt(fmt) == VQKV_FMT_1P5BIT) return 24;
+    if (base_fmt(fmt) == VQKV_FMT_3BIT) return 48;
     return 0;
 }
 
@@ -261,6 +263,8 @@ vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, con
     const int G = s->num_q_heads / s->num_kv_heads;
     if (path == 1 && !(base_fmt(s->fmt) == VQKV_FMT_2BIT && G <= 4))
         return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
+    if (path == 2 && base_fmt(s->fmt) == VQKV_FMT_3BIT)
+        return fail(VQKV_ERR_UNSUPPORTED, "the gather path takes the 2-bit and 1.5-bit formats");
     vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
@@ -294,6 +298,8 @@ vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* s, const float* q_pri
     const int G = s->num_q_heads / s->num_kv_heads;
     if (path == 1 && !(base_fmt(s->fmt) == VQKV_FMT_2BIT && G <= 4))
         return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
+    if (path == 2 && base_fmt(s->fmt) == VQKV_FMT_3BIT)
+        return fail(VQKV_ERR_UNSUPPORTED, "the gather path takes the 2-bit and 1.5-bit formats");
     vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
@@ -478,7 +484,7 @@ vqkv_status vqkv_smooth_scales(int32_t num_kv_heads, int32_t n_cal, const void* 
 }
 
 size_t vqkv_train_workspace_bytes(int32_t fmt, int32_t n_cal) {
-    if ((fmt != VQKV_FMT_2BIT && fmt != VQKV_FMT_1P5BIT) || n_cal < 1) return 0;
+    if (!known_fmt(fmt) || n_cal < 1) return 0;
     const size_t n_pts = (size_t)n_cal * (128 / dsub_of(fmt));
     return align256((size_t)n_cal * 128 * sizeof(double)) + align256(n_pts * sizeof(int32_t)) +
            align256((size_t)entries_of(fmt) * dsub_of(fmt) * sizeof(double));
@@ -487,7 +493,7 @@ size_t vqkv_train_workspace_bytes(int32_t fmt, int32_t n_cal) {
 vqkv_status vqkv_train_codebook(int32_t fmt, int32_t n_cal, const void* rows, int32_t dtype, int32_t is_key,
                                 const float* smooth, const int64_t* init_idx, int32_t iters, uint16_t* book,
                                 double* centroids, void* workspace, void* stream) {
-    if (fmt != VQKV_FMT_2BIT && fmt != VQKV_FMT_1P5BIT) return fail(VQKV_ERR_INVALID_ARG, "unknown format %d", fmt);
+    if (!known_fmt(fmt)) return fail(VQKV_ERR_INVALID_ARG, "unknown format %d", fmt);
     const int E = entries_of(fmt);
     const int64_t n_pts = (int64_t)n_cal * (128 / dsub_of(fmt));
     if (n_cal < 1 || n_pts < E)

@@ -380,21 +380,25 @@ __device__ __forceinline__ uint32_t bytes3_at(const uint32_t (&w)[N]) {
     return __builtin_amdgcn_perm(w[d1], w[d], s0 | (s1 << 8) | (s2 << 16) | (0x0cu << 24));
 }
 
-// 16 x the 12-bit code at bits [12 C, 12 C + 12) of the little-endian words w,
-// OR base (whose bits 4..15 are clear): a shift or a funnel shift that puts
-// the code at bit 4, then one AND-OR.
-template <int C, int N>
-__device__ __forceinline__ uint32_t code12_x16(const uint32_t (&w)[N], uint32_t base) {
-    constexpr int S = 12 * C - 4;
-    static_assert(S + 16 <= 32 * N, "code inside the words");
+// 2^SH x the 12-bit code at bits [12 C, 12 C + 12) of the little-endian words
+// w, OR base (whose bits SH..SH+11 are clear): a shift or a funnel shift that
+// puts the code at bit SH, then one AND-OR.
+template <int C, int SH, int N>
+__device__ __forceinline__ uint32_t code12_at(const uint32_t (&w)[N], uint32_t base) {
+    constexpr int S = 12 * C - SH;
+    static_assert(S + SH + 12 <= 32 * N, "code inside the words");
     uint32_t win;
-    if constexpr (S < 0) win = w[0] << 4;
-    else if constexpr (S % 32 + 16 <= 32) win = w[S / 32] >> (S % 32);
+    if constexpr (S < 0) win = w[0] << SH;
+    else if constexpr (S % 32 + SH + 12 <= 32) win = w[S / 32] >> (S % 32);
     else win = __builtin_amdgcn_alignbit(w[S / 32 + 1], w[S / 32], S % 32);
     uint32_t r;
     // One v_and_or_b32 (left to itself the compiler splits it into an AND and an ADD).
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(win), "s"(0xfff0u), "v"(base));
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(win), "s"(0xfffu << SH), "v"(base));
     return r;
+}
+template <int C, int N>
+__device__ __forceinline__ uint32_t code12_x16(const uint32_t (&w)[N], uint32_t base) {
+    return code12_at<C, 4>(w, base);
 }
 
 // 1.5-bit: an 8-dim centroid is two 4-dim halves, so the same products run on
@@ -411,8 +415,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int MERGE_BYTES = NW * G * (kHeadDim + 2) * 4;
     constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES;
     constexpr int SMEM = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
-    constexpr int W = FMT == 0 ? 32 : 24;
-    static_assert(FMT == 0 || 4096 * 16 == kBookBytes, "a 1.5-bit book fills one book region");
+    constexpr int W = FMT == 0 ? 32 : (FMT == 1 ? 24 : 48);
+    static_assert(FMT != 1 || 4096 * 16 == kBookBytes, "a 1.5-bit book fills one book region");
+    static_assert(FMT != 2 || 4096 * 8 <= kBookBytes, "a 3-bit book fits one book region");
     __shared__ __align__(16) unsigned char smem[SMEM];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -426,6 +431,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         for (int i = threadIdx.x; i < 256 * 32; i += NW * 64) {
             ((uint2*)smem)[i] = kb[i >> 5];
             ((uint2*)(smem + kBookBytes))[i] = vb[i >> 5];
+        }
+    } else if constexpr (FMT == 2) {
+        // 3-bit: single copies, 8-byte entries (4 dims).
+        const uint2* kb = (const uint2*)(a.k_book + (int64_t)h * 4096 * 4);
+        const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * 4096 * 4);
+        for (int i = threadIdx.x; i < 4096; i += NW * 64) {
+            ((uint2*)smem)[i] = kb[i];
+            ((uint2*)(smem + kBookBytes))[i] = vb[i];
         }
     } else {
         const uint4* kb = (const uint4*)(a.k_book + (int64_t)h * 4096 * 8);
@@ -483,7 +496,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // 2-bit: 32 copies, lane l reads copy l % 32; the value book starts at 64 KB.
     // 1.5-bit: value lookups read half e = lane % 2 of the entry.
     const uint32_t kofs = FMT == 0 ? (uint32_t)(lane & 31) * 8 : 0u;
-    const uint32_t vofs = FMT == 0 ? (kofs | (1u << 16)) : (((uint32_t)(lane & 1) << 3) | (1u << 16));
+    const uint32_t vofs = FMT == 0   ? (kofs | (1u << 16))
+                          : FMT == 1 ? (((uint32_t)(lane & 1) << 3) | (1u << 16))
+                                     : (1u << 16);
     unsigned char* pt = smem + 2 * kBookBytes + wave * (HB * 512);
     const int row_w = lane * 8;
     const int row_r = ((lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3)) * 8;
@@ -503,14 +518,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const uint8_t* vl0 = vbase + lane * 32;
     const uint8_t* kl1 = kbase + lane * 24;
     const uint8_t* vl1 = vbase + vstream * 48;
+    // 3-bit: 48 bytes per lane per tile for keys (the lane's token) and
+    // values (chunk = lane of the block).
+    const uint8_t* kl2 = kbase + lane * 48;
+    const uint8_t* vl2 = vbase + lane * 48;
     uint4 ck0, ck1, cv0, cv1;                               // 2-bit
     uint2 dk[3];                                            // 1.5-bit
     uint4 dv[3];
+    uint4 ek[3], ev[3];                                     // 3-bit
     auto load_k = [&](int tl) {
         if constexpr (FMT == 0) {
             const int64_t o = toff(tl);
             ck0 = *(const uint4*)(kl0 + o);
             ck1 = *(const uint4*)(kl0 + o + 16);
+        } else if constexpr (FMT == 2) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) ek[i] = *(const uint4*)(kl2 + toff(tl) + 16 * i);
         } else {
 #pragma unroll
             for (int i = 0; i < 3; ++i) dk[i] = *(const uint2*)(kl1 + toff(tl) + 8 * i);
@@ -521,6 +544,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             const int64_t o = toff(tl);
             cv0 = *(const uint4*)(vl0 + o);
             cv1 = *(const uint4*)(vl0 + o + 16);
+        } else if constexpr (FMT == 2) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) ev[i] = *(const uint4*)(vl2 + toff(tl) + 16 * i);
         } else {
 #pragma unroll
             for (int i = 0; i < 3; ++i) dv[i] = *(const uint4*)(vl1 + toff(tl) + 16 * i);
@@ -555,6 +581,20 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 if (half == 0) ck0 = *(const uint4*)(kl0 + toff(nxt));
                 else ck1 = *(const uint4*)(kl0 + toff(nxt) + 16);
             }
+        } else if constexpr (FMT == 2) {
+            // Scores: 32 sub-vectors; the 12-bit code of sub-vector j sits at
+            // bit 12 j of the lane's 48 bytes.
+            const uint32_t kw[12] = {ek[0].x, ek[0].y, ek[0].z, ek[0].w, ek[1].x, ek[1].y,
+                                     ek[1].z, ek[1].w, ek[2].x, ek[2].y, ek[2].z, ek[2].w};
+            static_for<0, 32>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const uint32_t addr = code12_at<j, 3>(kw, 0u);
+                const half4_t kv = *(const half4_t*)(smem + addr);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) sacc[hb] = mfma_bcast<j & 15>(qa[hb][j >> 4], kv, sacc[hb]);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(nxt);
         } else {
             // Scores: 16 sub-vectors in 8 pairs; each 16-byte entry feeds the
             // products of virtual sub-vectors 2j and 2j + 1.
@@ -632,6 +672,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 if (hv == 0) cv0 = *(const uint4*)(vl0 + toff(nxt));
                 else cv1 = *(const uint4*)(vl0 + toff(nxt) + 16);
             }
+        } else if constexpr (FMT == 2) {
+            // Values: step st takes the pair (sub-vector j, j + 16) of token
+            // group st, bytes 3 st.. of the lane's chunk (j % 16 fixed by the lane).
+            const uint32_t vw[12] = {ev[0].x, ev[0].y, ev[0].z, ev[0].w, ev[1].x, ev[1].y,
+                                     ev[1].z, ev[1].w, ev[2].x, ev[2].y, ev[2].z, ev[2].w};
+            static_for<0, 16>([&](auto sc16) {
+                constexpr int st = decltype(sc16)::value;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t addr = hh == 0 ? code12_at<2 * st, 3>(vw, vofs) : code12_at<2 * st + 1, 3>(vw, vofs);
+                    const half4_t vv = lds_read_tr16((const lds_char*)(smem + addr));
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_bcast<st>(pt_op[hb], vv, o[hb][hh]);
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            load_v(nxt);
         } else {
             // Values: step st takes pair st of the lane's stream (bytes 3 st..).
             const uint32_t vw[12] = {dv[0].x, dv[0].y, dv[0].z, dv[0].w, dv[1].x, dv[1].y,
@@ -921,16 +978,21 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                 VQKV_G(0, 1) VQKV_G(0, 2) VQKV_G(0, 3) VQKV_G(0, 4) VQKV_G(0, 5) VQKV_G(0, 6) VQKV_G(0, 7) VQKV_G(0, 8)
                 default: return hipErrorInvalidValue;
             }
-        } else {
+        } else if (a.fmt == 1) {
             switch (G) {
                 VQKV_G(1, 1) VQKV_G(1, 2) VQKV_G(1, 3) VQKV_G(1, 4) VQKV_G(1, 5) VQKV_G(1, 6) VQKV_G(1, 7) VQKV_G(1, 8)
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (G) {
+                VQKV_G(2, 1) VQKV_G(2, 2) VQKV_G(2, 3) VQKV_G(2, 4) VQKV_G(2, 5) VQKV_G(2, 6) VQKV_G(2, 7) VQKV_G(2, 8)
                 default: return hipErrorInvalidValue;
             }
         }
 #undef VQKV_G
         return hipGetLastError();
     }
-    if (a.block_table) return hipErrorInvalidValue;      // paged caches: matrix-core kernel only
+    if (a.block_table || a.fmt == 2) return hipErrorInvalidValue;   // matrix-core kernel only
     if (a.fmt == 0) return launch_gather<0, 8>(a, grid, stream);
     return launch_gather<1, 8>(a, grid, stream);
 }

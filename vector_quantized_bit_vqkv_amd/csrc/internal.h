@@ -29,6 +29,17 @@ __host__ __device__ __forceinline__ int64_t v_pair_offset_1p5(int64_t t, int j) 
     return (t >> 6) * 1536 + 48 * stream + 3 * (u >> 2);
 }
 
+// Byte offset of the 3-byte pair holding the value codes of sub-vectors
+// (j, j + 16), j < 16, of token t in a 3-bit stream.  Blocks of 64 tokens x
+// 32 sub-vectors = 3072 bytes, cut into 64 chunks of 48 bytes as in the 2-bit
+// layout: chunk 16*(j/4) + 4*(t%4) + j%4 holds the pair at bytes
+// 3*((t%64)/4)..+2.  Chunk c is what lane c of the decode wave reads.
+__host__ __device__ __forceinline__ int64_t v_pair_offset_3bit(int64_t t, int j) {
+    const int u = (int)(t & 63);
+    const int chunk = 16 * ((j & 15) >> 2) + 4 * (u & 3) + (j & 3);
+    return (t >> 6) * 3072 + 48 * chunk + 3 * (u >> 2);
+}
+
 struct TransformQueryArgs {
     const void* q;          // [B][Hq][128], bf16 or fp32
     int dtype;              // 0 bf16, 1 fp32

@@ -31,6 +31,13 @@ constexpr double kInvSqrtHeadDimD = 0x1.6a09e667f3bcdp-4;
 template <int FMT> struct Fmt;
 template <> struct Fmt<0> { static constexpr int E = 256, DS = 4, J = 32, W = 32; };
 template <> struct Fmt<1> { static constexpr int E = 4096, DS = 8, J = 16, W = 24; };
+template <> struct Fmt<2> { static constexpr int E = 4096, DS = 4, J = 32, W = 48; };
+
+// Byte offset of the value pair (j, j + J/2) of token t, 12-bit formats.
+template <int FMT>
+__device__ __forceinline__ int64_t v_pair_offset(int64_t t, int j) {
+    return FMT == 1 ? v_pair_offset_1p5(t, j) : v_pair_offset_3bit(t, j);
+}
 
 __device__ __forceinline__ double load_elem_d(const void* base, int64_t i, int dtype) {
     return (double)load_elem(base, i, dtype);
@@ -251,7 +258,7 @@ __device__ __forceinline__ double screen_operands(const double* x, int np, half4
 
 // -------------------------------------------------------------- append kernel
 
-template <int FMT> struct AppendTile { static constexpr int TT = FMT == 0 ? 32 : 16; };
+template <int FMT> struct AppendTile { static constexpr int TT = FMT == 0 ? 32 : 16; };   // 1.5- and 3-bit: 16
 
 // The screen's bound for a point of norm xn against a book with
 // (max |c|^2, max |c|_1) = cb.
@@ -400,12 +407,12 @@ __global__ __launch_bounds__(1024) void quantize_screen_kernel(AppendArgs a) {
             p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
             p[2] = (uint8_t)(c1 >> 4);
         }
-        // Values: sub-vectors (j, j + 8) of a token share 3 bytes.
+        // Values: sub-vectors (j, j + J/2) of a token share 3 bytes.
         for (int idx = threadIdx.x; idx < nt * (J / 2); idx += blockDim.x) {
             const int r = off + idx / (J / 2), j = idx % (J / 2);
             const int64_t t = tile_base + r;
-            const uint32_t c0 = codes[1][r * J + j], c1 = codes[1][r * J + j + 8];
-            uint8_t* p = vc + v_pair_offset_1p5(t, j);
+            const uint32_t c0 = codes[1][r * J + j], c1 = codes[1][r * J + j + J / 2];
+            uint8_t* p = vc + v_pair_offset<FMT>(t, j);
             p[0] = (uint8_t)(c0 & 0xff);
             p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
             p[2] = (uint8_t)(c1 >> 4);
@@ -519,12 +526,12 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
             p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
             p[2] = (uint8_t)(c1 >> 4);
         }
-        // Values: sub-vectors (j, j + 8) of a token share 3 bytes.
+        // Values: sub-vectors (j, j + J/2) of a token share 3 bytes.
         for (int idx = threadIdx.x; idx < nt * (J / 2); idx += blockDim.x) {
             const int r = off + idx / (J / 2), j = idx % (J / 2);
             const int64_t t = tile_base + r;
-            const uint32_t c0 = codes[1][r * J + j], c1 = codes[1][r * J + j + 8];
-            uint8_t* p = vc + v_pair_offset_1p5(t, j);
+            const uint32_t c0 = codes[1][r * J + j], c1 = codes[1][r * J + j + J / 2];
+            uint8_t* p = vc + v_pair_offset<FMT>(t, j);
             p[0] = (uint8_t)(c0 & 0xff);
             p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
             p[2] = (uint8_t)(c1 >> 4);
@@ -548,7 +555,7 @@ __device__ __forceinline__ void group_argmin(double& d, int& idx) {
 
 // Blocks per key (and per value) of the one-token append: a 4096-entry search
 // is split over 4 blocks of 4 sub-vectors each, so the grid fills the GPU.
-template <int FMT> struct TokenSplit { static constexpr int P = FMT == 0 ? 1 : 4; };
+template <int FMT> struct TokenSplit { static constexpr int P = FMT == 0 ? 1 : 4; };   // 4096 entries: 4
 
 // The per-step append (one new token per sequence), latency-bound: grid
 // (2P, Hkv, B), block x / P = 0 codes the key, 1 the value, x % P = part p
@@ -597,8 +604,9 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
     const int64_t t = a.positions ? (int64_t)a.positions[b] : (int64_t)a.start_pos;
     if (t < 0 || t >= a.cap) return;
     // Sub-vector j of the block's jj-th.
+    // 12-bit values: the block's JB / 2 low sub-vectors and their partners J / 2 further.
     auto sub_of = [&](int jj) -> int {
-        if (FMT == 1 && ph == 1) return 2 * part + (jj & 1) + 8 * (jj >> 1);
+        if (FMT != 0 && ph == 1) return (JB / 2) * part + jj % (JB / 2) + (J / 2) * (jj / (JB / 2));
         return part * JB + jj;
     };
     {
@@ -684,12 +692,12 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
         }
     } else if (threadIdx.x < JB / 2) {
         // Keys: sub-vectors (2i, 2i+1) share 3 bytes (the block's jj = 2m, 2m+1);
-        // values: (i, i + 8) (the block's jj = m, m + 2).
+        // values: (i, i + J/2) (the block's jj = m, m + JB/2).
         const int m = threadIdx.x;
-        const int jj0 = ph == 0 ? 2 * m : m, jj1 = ph == 0 ? 2 * m + 1 : m + 2;
+        const int jj0 = ph == 0 ? 2 * m : m, jj1 = ph == 0 ? 2 * m + 1 : m + JB / 2;
         const uint32_t c0 = codes[jj0], c1 = codes[jj1];
         const int j0 = sub_of(jj0);
-        uint8_t* p = ph == 0 ? kblk + u * W + 3 * (j0 >> 1) : vblk + v_pair_offset_1p5(u, j0);
+        uint8_t* p = ph == 0 ? kblk + u * W + 3 * (j0 >> 1) : vblk + v_pair_offset<FMT>(u, j0);
         p[0] = (uint8_t)(c0 & 0xff);
         p[1] = (uint8_t)((c0 >> 8) | ((c1 & 0xf) << 4));
         p[2] = (uint8_t)(c1 >> 4);
@@ -855,17 +863,20 @@ hipError_t train_codebook(const TrainArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
-    const int TT = a.fmt == 0 ? AppendTile<0>::TT : AppendTile<1>::TT;
+    const int TT = a.fmt == 0 ? AppendTile<0>::TT : (a.fmt == 1 ? AppendTile<1>::TT : AppendTile<2>::TT);
     const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
     const dim3 grid(last - first + 1, a.hkv, a.batch);
     if (a.n_new == 1 || a.positions) {
-        const dim3 g1(2 * (a.fmt == 0 ? TokenSplit<0>::P : TokenSplit<1>::P), a.hkv, a.batch);
+        const dim3 g1(2 * (a.fmt == 0 ? TokenSplit<0>::P : (a.fmt == 1 ? TokenSplit<1>::P : TokenSplit<2>::P)),
+                      a.hkv, a.batch);
         if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(1024), 0, stream, a);
-        else hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
+        else if (a.fmt == 1) hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL(quantize_token_kernel<2>, g1, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     if (a.fmt == 0) hipLaunchKernelGGL(quantize_exact_kernel<0>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(quantize_screen_kernel<1>, grid, dim3(1024), 0, stream, a);
+    else if (a.fmt == 1) hipLaunchKernelGGL(quantize_screen_kernel<1>, grid, dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL(quantize_screen_kernel<2>, grid, dim3(1024), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -875,7 +886,8 @@ hipError_t launch_smooth_scales(int hkv, int n_cal, const void* k_cal, int dtype
 }
 
 hipError_t launch_train_codebook(const TrainArgs& a, hipStream_t stream) {
-    return a.fmt == 0 ? train_codebook<0>(a, stream) : train_codebook<1>(a, stream);
+    if (a.fmt == 0) return train_codebook<0>(a, stream);
+    return a.fmt == 1 ? train_codebook<1>(a, stream) : train_codebook<2>(a, stream);
 }
 
 }  // namespace vqkv
