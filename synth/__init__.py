@@ -31,7 +31,9 @@ import numpy as np
 HEAD_DIM = 128
 FMT_2BIT = 0      # 2^8 entries x 4 dims  -> 2 bits per element
 FMT_1P5BIT = 1    # 2^12 entries x 8 dims -> 1.5 bits per element
-FORMATS = {FMT_2BIT: dict(entries=256, dsub=4), FMT_1P5BIT: dict(entries=4096, dsub=8)}
+FMT_3BIT = 2      # 2^12 entries x 4 dims -> 3 bits per element
+FORMATS = {FMT_2BIT: dict(entries=256, dsub=4), FMT_1P5BIT: dict(entries=4096, dsub=8),
+           FMT_3BIT: dict(entries=4096, dsub=4)}
 
 N_OUTLIER = 4
 OUTLIER_SCALE = 15.0
@@ -73,6 +75,8 @@ WORKLOADS = {
     "llama8b_b1_t196k": Workload("llama8b_b1_t196k", 1, 32, 8, 196608, FMT_2BIT, "bf16"),
     "llama8b_b32_t196k": Workload("llama8b_b32_t196k", 32, 32, 8, 196608, FMT_2BIT, "bf16"),
     "qwen14b_b8_t128k_1p5": Workload("qwen14b_b8_t128k_1p5", 8, 40, 8, 131072, FMT_1P5BIT, "bf16"),
+    # The added 3-bit width (2^12 x 4) on the Llama-3.1-8B attention shape.
+    "llama8b_b8_t196k_3bit": Workload("llama8b_b8_t196k_3bit", 8, 32, 8, 196608, FMT_3BIT, "bf16"),
 }
 
 
