@@ -291,23 +291,30 @@ class Workload:
         kn = self.k_new.float().cpu().numpy()
         vn = self.v_new.float().cpu().numpy()
         kc_dev, vc_dev = self.caches[0]
-        spent, done = 0.0, 0
-        for b in range(B):
-            kc = np.stack([oracle.unpack_k(fmt, kc_dev[b, h].cpu().numpy(), T) for h in range(Hkv)])[None]
-            vc = np.stack([oracle.unpack_v(fmt, vc_dev[b, h].cpu().numpy(), T) for h in range(Hkv)])[None]
+        # Sequences in order, each unpacked once (outside the timing); when the
+        # batch is done before the budget, the first few are timed again.
+        kept, spent, done = [], 0.0, 0
+        while spent < budget_s:
+            if done < B:
+                b = done
+                kc = np.stack([oracle.unpack_k(fmt, kc_dev[b, h].cpu().numpy(), T) for h in range(Hkv)])[None]
+                vc = np.stack([oracle.unpack_v(fmt, vc_dev[b, h].cpu().numpy(), T) for h in range(Hkv)])[None]
+                if len(kept) < 4:
+                    kept.append((b, kc, vc))
+            else:
+                b, kc, vc = kept[(done - B) % len(kept)]
             t0 = time.perf_counter()
             for h in range(Hkv):
                 oracle.quantize(fmt, kn[b, h], vn[b, h], s[h], kb[h], vb[h], nthreads=threads)
             oracle.attention(fmt, q[b:b + 1], s, kb, vb, kc, vc, nthreads=threads)
             spent += time.perf_counter() - t0
             done += 1
-            if spent >= budget_s:
-                break
         full_s = spent / done * B
         return {"value": round(self.step_bytes / full_s / 1e9, 3), "unit": "GB/s", "cores": threads,
                 "kind": "oracle",
-                "sample": f"{done} of {B} sequences (all {Hq} q-heads, {T} tokens each): fp64 oracle attention "
-                          f"plus quantization of the appended token, {spent:.1f} s, scaled to the batch",
+                "sample": f"{done} sequence computations over {min(done, B)} of {B} sequences (all {Hq} q-heads, "
+                          f"{T} tokens each): fp64 oracle attention plus quantization of the appended token, "
+                          f"{spent:.1f} s, scaled to the batch",
                 "us_per_step": round(full_s * 1e6, 1)}
 
 
