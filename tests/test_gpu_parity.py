@@ -949,6 +949,14 @@ def test_end_to_end_tiny_workload():
     assert np.array_equal(oracle.unpack_v(0, cache.v_codes[0, 0].cpu().numpy(), 2048), vc)
     ref = oracle.attention(0, case.q, s_ref[None], kb_ref[None], vb_ref[None], kc[None, None], vc[None, None])
     assert rel_err(out, ref) <= TOL
+    # The same through VQCache.step: 2047 tokens appended, then the last token's
+    # step (decode_step), bit-identical to the four calls above.
+    stepped = vq.VQCache.allocate(shape, smooth, k_book, v_book, DEV)
+    stepped.append(dev(case.k[:, :, :2047]).contiguous(), dev(case.v[:, :, :2047]).contiguous(), 0)
+    out2 = stepped.step(dev(case.q), dev(case.k[:, :, 2047:]).contiguous(), dev(case.v[:, :, 2047:]).contiguous(),
+                        2047, num_splits=8).cpu().numpy()
+    assert np.array_equal(out2.view(np.uint32), out.view(np.uint32))
+    assert torch.equal(stepped.k_codes, cache.k_codes) and torch.equal(stepped.v_codes, cache.v_codes)
     # Quality, not parity: the 2-bit cache stays close to full-precision attention.
     fp = oracle.attention_fp(case.q, case.k, case.v)
     print(f"  VQ vs full precision: {rel_err(ref, fp):.3f}", flush=True)
@@ -956,7 +964,7 @@ def test_end_to_end_tiny_workload():
 
 # ---------------------------------------------------------- full sizes, sampled
 
-FULL = ["llama8b_b1_t32k", "llama8b_b1_t196k", "llama8b_b32_t196k", "qwen14b_b8_t128k_1p5"]
+FULL = ["llama8b_b1_t32k", "llama8b_b1_t196k", "llama8b_b32_t196k", "qwen14b_b8_t128k_1p5", "llama8b_b8_t196k_3bit"]
 
 
 @pytest.mark.parametrize("name", FULL)

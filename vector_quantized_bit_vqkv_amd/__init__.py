@@ -370,6 +370,24 @@ class VQCache:
         decode_attention(self.shape, q_prime, self.k_book, self.v_book, self.k_codes, self.v_codes, seq_len,
                          num_splits, workspace)
         combine(self.shape, num_splits, workspace, out)
+        if self.shape.fmt & FMT_VALUE_TRANSFORM:
+            value_output_transform(self.shape, self.smooth, out)
+        return out
+
+    def step(self, q, k_new, v_new, position: int, num_splits: int | None = None, out=None, workspace=None):
+        """One decode step in two launches: append k_new, v_new [B][Hkv][1][128] at `position`,
+        then attend with q over tokens [0, position] (decode_step)."""
+        import torch
+        if num_splits is None:
+            num_splits = suggest_splits(self.shape, position + 1)
+        B, Hq = self.shape.batch, self.shape.num_q_heads
+        if workspace is None:
+            workspace = torch.empty(step_workspace_bytes(self.shape, num_splits), dtype=torch.uint8,
+                                    device=q.device)
+        if out is None:
+            out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        decode_step(self.shape, q, k_new, v_new, position, self.smooth, self.k_book, self.v_book, self.k_codes,
+                    self.v_codes, num_splits, workspace, out)
         return out
 
 
