@@ -1,0 +1,20 @@
+// Stand-ins for the kernel launchers, so that the C-ABI layer's host code
+// (argument checks, workspace layout, launch-argument packing) can be built
+// with g++ under the sanitizers and driven without a GPU.  Each stub records
+// the call and reports success.  Test infrastructure only.
+#include "../../vector_quantized_bit_vqkv_amd/csrc/internal.h"
+
+int g_launches = 0;
+
+// The C-ABI layer only asks the runtime for error text.
+const char* hipGetErrorString(hipError_t) { return "stubbed HIP runtime"; }
+
+namespace vqkv {
+hipError_t launch_transform_query(const TransformQueryArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_quantize_append(const AppendArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_decode(const DecodeArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_combine(const CombineArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_value_output_transform(const ValueOutputArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_smooth_scales(int, int, const void*, int, float*, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_train_codebook(const TrainArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+}  // namespace vqkv
