@@ -15,16 +15,20 @@
 // (o normalized, lse) to the workspace.  Scores carry the factor
 // sm_scale * log2(e), so exp2 is the exponential and lse is in log2 units.
 //
-// Kernels (the 2-bit one chosen by measurement; the others stay selectable):
-//   * decode_mfma_kernel (2-bit, default): scores and values both on the
-//     matrix cores, v_mfma_f32_4x4x4f16, with the centroids gathered from
-//     LDS codebooks (details at the kernel);
+// Kernels (the matrix-core one chosen by measurement; the others stay
+// selectable for measurement):
+//   * decode_mfma_kernel (default, every format: 2-bit 2^8 x 4, 1.5-bit
+//     2^12 x 8, 3-bit 2^12 x 4): scores and values both on the matrix cores,
+//     v_mfma_f32_4x4x4f16, with the centroids gathered from LDS codebooks
+//     (details at the kernel).  For the fused decode step it also finishes
+//     the output: with one split the work-group writes it directly, with more
+//     the last split of a head to finish combines the head's splits, and in
+//     the value-transform variant the output is mapped back, s_v * (H o);
 //   * decode_table_kernel (2-bit, G <= 4): per work-group score table
 //     L[j][e][g] = c * q'_g[4j..4j+3] . C_K[e] for all 32 x 256 (j, e), so a
 //     token's score is 32 table reads and adds; values on the matrix cores;
-//   * decode_gather_kernel: the token's centroids are read from the LDS
-//     codebook and dotted with q' (held in LDS, pre-scaled) -- the 1.5-bit
-//     path, where a table would be 16 x 4096 x G floats.
+//   * decode_gather_kernel (2-bit and 1.5-bit): the token's centroids are read
+//     from the LDS codebook and dotted with q' (held in LDS, pre-scaled).
 #include "attn_common.h"
 #include "device_util.h"
 #include "internal.h"
@@ -384,7 +388,7 @@ __device__ __forceinline__ uint32_t bytes3_at(const uint32_t (&w)[N]) {
 // w, OR base (whose bits SH..SH+11 are clear): a shift or a funnel shift that
 // puts the code at bit SH, then one AND-OR.
 template <int C, int SH, int N>
-__device__ __forceinline__ uint32_t code12_at(const uint32_t (&w)[N], uint32_t base) {
+__device__ __forceinline__ uint32_t code12_addr(const uint32_t (&w)[N], uint32_t base) {
     constexpr int S = 12 * C - SH;
     static_assert(S + SH + 12 <= 32 * N, "code inside the words");
     uint32_t win;
@@ -398,7 +402,7 @@ __device__ __forceinline__ uint32_t code12_at(const uint32_t (&w)[N], uint32_t b
 }
 template <int C, int N>
 __device__ __forceinline__ uint32_t code12_x16(const uint32_t (&w)[N], uint32_t base) {
-    return code12_at<C, 4>(w, base);
+    return code12_addr<C, 4>(w, base);
 }
 
 // 1.5-bit: an 8-dim centroid is two 4-dim halves, so the same products run on
@@ -588,7 +592,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                                      ek[1].z, ek[1].w, ek[2].x, ek[2].y, ek[2].z, ek[2].w};
             static_for<0, 32>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
-                const uint32_t addr = code12_at<j, 3>(kw, 0u);
+                const uint32_t addr = code12_addr<j, 3>(kw, 0u);
                 const half4_t kv = *(const half4_t*)(smem + addr);
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) sacc[hb] = mfma_bcast<j & 15>(qa[hb][j >> 4], kv, sacc[hb]);
@@ -681,7 +685,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 constexpr int st = decltype(sc16)::value;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const uint32_t addr = hh == 0 ? code12_at<2 * st, 3>(vw, vofs) : code12_at<2 * st + 1, 3>(vw, vofs);
+                    const uint32_t addr = hh == 0 ? code12_addr<2 * st, 3>(vw, vofs) : code12_addr<2 * st + 1, 3>(vw, vofs);
                     const half4_t vv = lds_read_tr16((const lds_char*)(smem + addr));
 #pragma unroll
                     for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_bcast<st>(pt_op[hb], vv, o[hb][hh]);

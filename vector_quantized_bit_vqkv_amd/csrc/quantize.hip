@@ -5,7 +5,9 @@
 // "technical framework" paragraph: keys are smoothed per channel and rotated
 // by a Hadamard transform, then keys and values are vector-quantized against
 // codebooks trained offline with K-Means ("Key points": 2^8 x 4 entries for
-// 2-bit, 2^12 x 8 for 1.5-bit).
+// 2-bit, 2^12 x 8 for 1.5-bit; a third width inside the pages' 1.25-4 bit
+// range, 2^12 x 4 at 3 bits, takes the same steps).  In the value-transform
+// variant the values take the keys' steps with their own scales s_v.
 //
 // Every decision that turns floating point into an integer (a code, a K-Means
 // assignment) is taken in fp64 with one fixed operation sequence, so the
