@@ -367,6 +367,63 @@ def test_quantize_ties_go_to_lowest_index(fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantize_near_ties_below_fp32_resolution(fmt):
+    """Keys whose rotated sub-vectors sit at the midpoint of two codebook
+    entries one fp16 ulp apart (up to the fp32 rounding of k): the two
+    distances agree to far below fp32 resolution, so only fp64 tells them
+    apart.  The codes, one token at a time and in bulk, equal the oracle's;
+    a plain fp32 argmin would miss many of them (counted on the host)."""
+    say(f"quantize near ties fmt{fmt}")
+    E, dsub = oracle.FORMATS[fmt]
+    J = D // dsub
+    rng = np.random.default_rng(31 + fmt)
+    half = E // 2
+    base = (rng.standard_normal((half, dsub)) * 0.5).astype(np.float16)
+    base[:, 0] = np.abs(base[:, 0]) + np.float16(0.25)           # positive: next entry up is one ulp larger
+    up = base.copy()
+    up[:, 0] = np.nextafter(base[:, 0], np.float16(np.inf))
+    kb = np.concatenate([base, up]).view(np.uint16)[None]         # entry e + E/2 = entry e, one ulp up on dim 0
+    n = 48
+    pick = rng.integers(0, half, (n, J))
+    xt = base[pick].astype(np.float64)                            # (n, J, dsub)
+    xt[:, :, 0] = 0.5 * (base[pick, 0].astype(np.float64) + up[pick, 0].astype(np.float64))
+    H = np.array([[1.0]])
+    while H.shape[0] < D:
+        H = np.block([[H, H], [H, -H]])
+    H /= math.sqrt(D)
+    s = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    k = ((xt.reshape(n, D) @ H) * s).astype(np.float32)          # H is symmetric and orthogonal
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    vb = synth.random_fp16_book(41, (1, E, dsub), 1.0)
+    kc_ref, vc_ref = oracle.quantize(fmt, k, v, s, kb[0], vb[0])
+    # How many codes a plain fp32 argmin gets wrong: x rounded to fp32, fp32 distances.
+    x32 = ((k.astype(np.float64) / s) @ H).reshape(n, J, dsub).astype(np.float32)
+    cb32 = kb[0].view(np.float16).astype(np.float32)
+    d32 = np.zeros((n, J, E), np.float32)
+    for i in range(dsub):
+        t = x32[:, :, None, i] - cb32[None, None, :, i]
+        d32 = d32 + t * t
+    miss = int(np.sum(np.argmin(d32, axis=-1) != kc_ref))
+    print(f"  fp32 argmin differs from the exact code on {miss} of {n * J} sub-vectors", flush=True)
+    assert miss >= 20
+    shape = vq.make_shape(1, 1, 1, 64, fmt)
+    W = vq.code_bytes_per_token(fmt)
+    for mode in ("bulk", "one-token"):
+        kcodes = torch.zeros((1, 1, 64 * W), dtype=torch.uint8, device=DEV)
+        vcodes = torch.zeros_like(kcodes)
+        if mode == "bulk":
+            vq.quantize_append(shape, dev(k[None, None]), dev(v[None, None]), 0, dev(s[None]), book_dev(kb),
+                               book_dev(vb), kcodes, vcodes)
+        else:
+            for t in range(n):
+                vq.quantize_append(shape, dev(k[None, None, t:t + 1]), dev(v[None, None, t:t + 1]), t, dev(s[None]),
+                                   book_dev(kb), book_dev(vb), kcodes, vcodes)
+        torch.cuda.synchronize()
+        assert np.array_equal(oracle.unpack_k(fmt, kcodes[0, 0].cpu().numpy(), n), kc_ref), mode
+        assert np.array_equal(oracle.unpack_v(fmt, vcodes[0, 0].cpu().numpy(), n), vc_ref), mode
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
 def test_quantize_fallbacks_match_oracle(fmt):
     """Points the distance screen cannot take (coordinates beyond the fp16 range,
     NaN) go through the exact scan: codes still equal the oracle's, in the bulk

@@ -555,6 +555,32 @@ __device__ __forceinline__ void group_argmin(double& d, int& idx) {
     }
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// |c|^2 and x.c for one codebook entry of DS fp16 values (LDS, 8- or
+// 16-byte aligned) on the dot units: fp16 pairs, fp32 sums.
+template <int DS>
+__device__ __forceinline__ void screen_dot(const uint16_t* c, const half2_t (&xh)[DS / 2], float& n2, float& xc) {
+    uint32_t w[DS / 2];
+    if constexpr (DS == 8) {
+        const uint4 v = *(const uint4*)c;
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+        static_assert(DS == 4, "screen_dot: 4 or 8 values");
+        const uint2 v = *(const uint2*)c;
+        w[0] = v.x; w[1] = v.y;
+    }
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DS / 2; ++i) {
+        const half2_t ch = __builtin_bit_cast(half2_t, w[i]);
+        a = __builtin_amdgcn_fdot2(ch, ch, a, false);
+        b = __builtin_amdgcn_fdot2(xh[i], ch, b, false);
+    }
+    n2 = a;
+    xc = b;
+}
+
 // Blocks per key (and per value) of the one-token append: a 4096-entry search
 // is split over 4 blocks of 4 sub-vectors each, so the grid fills the GPU.
 template <int FMT> struct TokenSplit { static constexpr int P = FMT == 0 ? 1 : 4; };   // 4096 entries: 4
@@ -570,7 +596,9 @@ template <int FMT> struct TokenSplit { static constexpr int P = FMT == 0 ? 1 : 4
 // minima are merged as (distance, index) pairs, lowest pair first, which is
 // the scan's lowest-index minimum whatever the merge order.
 template <int FMT>
-__global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
+// Two 1024-thread blocks per CU need at most 64 VGPRs (the 3-bit search keeps
+// 32 screened distances per thread; the cap costs it a few spilled dwords).
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void quantize_token_kernel(AppendArgs a) {
     using F = Fmt<FMT>;
     constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
     constexpr int NT = 1024, P = TokenSplit<FMT>::P;
@@ -584,6 +612,7 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
     __shared__ double x[kHeadDim];
     __shared__ double part_d[NT / 64];
     __shared__ int part_i[NT / 64];
+    __shared__ float part_m[NT / 64], part_c[NT / 64];
     __shared__ uint16_t codes[JB];
 
     const int ph = blockIdx.x / P, part = blockIdx.x % P, h = blockIdx.y, b = blockIdx.z;
@@ -646,10 +675,82 @@ __global__ __launch_bounds__(1024) void quantize_token_kernel(AppendArgs a) {
         // lanes read consecutive entries (no LDS bank conflicts).
         double best = __builtin_inf();
         int idx = sl;
-        for (int k = 0; k < EPS; ++k) {
-            const int e = sl + k * ES;
-            const double d = dist_h<DS>(xs, book + e * DS);
-            if (d < best) { best = d; idx = e; }
+        bool exact = FMT == 0;
+        if constexpr (FMT != 0) {
+            // 4096 entries: a screen on the dot units, then the pinned fp64
+            // distance for the candidates only.  Up to the common |x|^2, the
+            // distance is s = |c|^2 - 2 x.c; the screen takes x rounded to
+            // fp16 and fp32 sums of fp16 products (exact products; at most two
+            // roundings per pair).  With R = |x| + max_e |c_e| the screened s32
+            // is within 2^-11.9 R^2 + 2^-11.5 R + 2^-25 of s: 2^-10.9 |x_i| for
+            // x's rounding, 2^-14 per coordinate if the unit flushed fp16
+            // subnormals (of x or c), (DS + 3) 2^-24 R^2 for the sums.  tau =
+            // 2^-11 (R^2 + R) + 2^-24 covers that and the fp64 rounding of the
+            // pinned distance, so the pinned minimum and every entry tied with
+            // it have s32 <= m + 2 tau (m = the smallest s32): refining those
+            // entries and taking the lowest (distance, index) gives the scan's
+            // code.  A coordinate that is not finite or reaches 2^15 (fp16
+            // overflow), or no finite s32, sends the sub-vector to the exact scan.
+            half2_t xh[DS / 2];
+            float s32[EPS];
+            double xn2 = 0.0;
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < DS; ++i) {
+                xn2 = xn2 + xs[i] * xs[i];
+                ok = ok && __builtin_fabs(xs[i]) < 0x1p15;
+            }
+#pragma unroll
+            for (int i = 0; i < DS / 2; ++i)
+                xh[i] = half2_t{(_Float16)(float)xs[2 * i], (_Float16)(float)xs[2 * i + 1]};
+            float m = __builtin_inff(), c2 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < EPS; ++k) {
+                float n2, xc;
+                screen_dot<DS>(book + (sl + k * ES) * DS, xh, n2, xc);
+                s32[k] = __builtin_fmaf(-2.0f, xc, n2);
+                m = fminf(m, s32[k]);
+                c2 = fmaxf(c2, n2);
+            }
+            // The smallest s32 and the largest |c|^2 over the sub-vector's ES slices.
+#pragma unroll
+            for (int o = 1; o < L; o <<= 1) {
+                m = fminf(m, __shfl_xor(m, o, 64));
+                c2 = fmaxf(c2, __shfl_xor(c2, o, 64));
+            }
+            if constexpr (WPS > 1) {
+                if ((threadIdx.x & 63) == 0) {
+                    part_m[threadIdx.x >> 6] = m;
+                    part_c[threadIdx.x >> 6] = c2;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int w = 0; w < WPS; ++w) {
+                    m = fminf(m, part_m[jj * WPS + w]);
+                    c2 = fmaxf(c2, part_c[jj * WPS + w]);
+                }
+            }
+            exact = !ok || !(__builtin_fabsf(m) < __builtin_inff());   // uniform over the sub-vector
+            if (!exact) {
+                // |c| <= sqrt(n2) up to the sums' rounding and flushed subnormals.
+                const double r = __builtin_sqrt(xn2) + __builtin_sqrt((double)c2 * (1.0 + 0x1p-16)) + 0x1p-12;
+                const double thr = (double)m + 2.0 * (0x1p-11 * (r * r + r) + 0x1p-24);
+#pragma unroll
+                for (int k = 0; k < EPS; ++k) {
+                    if ((double)s32[k] <= thr) {
+                        const int e = sl + k * ES;
+                        const double d = dist_h<DS>(xs, book + e * DS);
+                        if (d < best) { best = d; idx = e; }
+                    }
+                }
+            }
+        }
+        if (exact) {
+            for (int k = 0; k < EPS; ++k) {
+                const int e = sl + k * ES;
+                const double d = dist_h<DS>(xs, book + e * DS);
+                if (d < best) { best = d; idx = e; }
+            }
         }
         group_argmin<L>(best, idx);
         if (WPS == 1) {
