@@ -183,7 +183,8 @@ class Workload:
                        kc, vc, self.S, self.step_workspace, self.out)
 
     def time_fused_steps(self, steps, warmup):
-        """The same step through decode_step: two launches, the combine fused into the decode."""
+        """The same step through decode_step: the combine fused into the decode, and with one
+        2-bit split the append too (one launch; else the append is a launch of its own)."""
         import torch
         for i in range(warmup):
             self.fused_step(i)

@@ -261,17 +261,20 @@ vqkv_status vqkv_quantize_append_paged(const vqkv_shape* shape, const void* k_ne
 vqkv_status vqkv_combine(const vqkv_shape* shape, int32_t num_splits, const void* workspace,
                          float* out, void* stream);
 
-/* One decode step in two launches: the append of one new token per sequence
- * at `position` (with the query transform in the same launch), then the
- * attention of every query over tokens [0, position] with the split combine
- * fused into it.  The result is bit-identical to the four calls
+/* One decode step: the append of one new token per sequence at `position`
+ * (with the query transform in the same launch), then the attention of every
+ * query over tokens [0, position] with the split combine fused into it; for
+ * the 2-bit format with num_splits = 1 the attention kernel does the append
+ * and the query transform itself (one launch).  The result is bit-identical
+ * to the four calls
  *   vqkv_quantize_append(n_new = 1, start_pos = position), vqkv_transform_query,
  *   vqkv_decode_attention(seq_len = position + 1), vqkv_combine
  * on the same arguments (the same kernels' arithmetic).  With one split the
  * attention kernel writes `out` itself; with more, the last split of each
  * (b, KV head) to finish combines that head's splits (a per-head arrival
  * counter in the workspace, cleared by the first launch of every step, so the
- * workspace needs no initialization).  Runs on the matrix-core kernel.
+ * workspace needs no initialization; one split needs no counter).  Runs on
+ * the matrix-core kernel.
  *   q                 device, [B][Hq][128], dtype (the same dtype as k_new)
  *   k_new, v_new      device, [B][Hkv][1][128], dtype
  *   position          host, 0 <= position < max_tokens

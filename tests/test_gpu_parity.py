@@ -251,7 +251,7 @@ def test_value_transform_attention_matches_oracle(fmt, S):
 
 
 @pytest.mark.parametrize("fmt,S,paged", [(0, 1, False), (0, 6, False), (1, 1, False), (1, 4, False),
-                                         (0, 5, True), (1, 3, True), (2, 3, False)])
+                                         (0, 5, True), (1, 3, True), (2, 3, False), (0, 1, True)])
 def test_value_transform_step_equals_the_calls(fmt, S, paged):
     """Value-transform variant: decode_step (uniform) or decode_step_paged
     (ragged positions) against append + transform_query + decode + combine +
@@ -692,6 +692,11 @@ STEP_CASES = [
     (1, 1, 2, 2, 3000, 47, "bf16"),       # G = 1, many splits
     (2, 2, 32, 8, 4098, 9, "bf16"),       # 3-bit
     (2, 1, 8, 8, 700, 1, "fp32"),
+    # 2-bit, one split: the append runs inside the attention kernel (one launch).
+    (0, 1, 16, 2, 700, 1, "fp32"),        # G = 8
+    (0, 3, 8, 8, 2000, 1, "fp32"),        # G = 1
+    (0, 2, 12, 4, 63, 1, "bf16"),         # G = 3, the last position of a block
+    (0, 1, 40, 8, 64, 1, "bf16"),         # G = 5, the first position of a block
 ]
 
 
@@ -802,7 +807,7 @@ def test_step_captured_in_a_graph_replays_exactly(fmt):
 
 @pytest.mark.parametrize("fmt,Hq,Hkv,S,paged", [(0, 8, 2, 1, False), (0, 8, 2, 7, False), (1, 10, 2, 5, False),
                                                 (0, 8, 2, 7, True), (1, 10, 2, 3, True), (0, 32, 8, 64, True),
-                                                (2, 8, 2, 5, True)])
+                                                (2, 8, 2, 5, True), (0, 40, 8, 1, True), (0, 8, 8, 1, True)])
 def test_decode_step_ragged_equals_the_four_calls(fmt, Hq, Hkv, S, paged):
     """decode_step_varlen / decode_step_paged against append (varlen / paged) +
     transform_query + decode (varlen / paged, lengths positions + 1) + combine:

@@ -402,14 +402,23 @@ vqkv_status decode_step_impl(const vqkv_shape* s, const void* q, const void* k_n
                         v_codes, s->batch, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt), positions, block_table,
                         num_blocks, q, q_prime, arrivals, s->num_q_heads, seq_lens};
     char what[64];
-    snprintf(what, sizeof(what), "%s append launch", name);
     ap.v_smooth = value_scales(s, smooth);
-    VQKV_CHECK(hip_status(vqkv::launch_quantize_append(ap, (hipStream_t)stream), what));
     vqkv::DecodeArgs d{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), 3, seq_lens, block_table, num_blocks,
                        out, arrivals, value_scales(s, smooth)};
+    if (base_fmt(s->fmt) == 0 && num_splits == 1) {
+        // One launch: each work-group appends its own head's token before its
+        // pass (nothing to combine with one split, so no counters either).
+        d.q_prime = nullptr;
+        d.seq_lens = nullptr;
+        d.app = ap;
+        snprintf(what, sizeof(what), "%s fused decode launch", name);
+        return hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what);
+    }
+    snprintf(what, sizeof(what), "%s append launch", name);
+    VQKV_CHECK(hip_status(vqkv::launch_quantize_append(ap, (hipStream_t)stream), what));
     snprintf(what, sizeof(what), "%s decode launch", name);
     return hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what);
 }

@@ -32,6 +32,8 @@
 #include "attn_common.h"
 #include "device_util.h"
 #include "internal.h"
+#include "qtransform.h"
+#include "token_search.h"
 
 namespace vqkv {
 
@@ -41,9 +43,15 @@ namespace {
 // per-sequence length clamped to [0, capacity] (an out-of-range length can
 // never make a kernel read outside the cache).
 __device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int b) {
-    if (!a.seq_lens) return a.seq_len;
-    const int n = a.seq_lens[b];
-    return n < 0 ? 0 : (n > a.cap ? a.cap : n);
+    if (a.seq_lens) {
+        const int n = a.seq_lens[b];
+        return n < 0 ? 0 : (n > a.cap ? a.cap : n);
+    }
+    if (a.app.positions) {                                  // fused append: through the new token
+        const int64_t p = a.app.positions[b];
+        return p < 0 ? 0 : (p >= a.cap ? a.cap : (int)p + 1);
+    }
+    return a.seq_len;
 }
 
 // Bytes of the per-(b, h) code stream per token.
@@ -353,6 +361,79 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
 constexpr int kBookStride = 256;
 constexpr int kBookBytes = 256 * kBookStride;
 
+// Fused append of the one-split decode step (2-bit).  The work-group of
+// (b, h) writes q' = H (q * s) of its G query heads into qr (waves 4..3+G,
+// the query transform's own butterflies), then codes the new key and value of
+// (b, h) with the exact fp64 search of the one-token append kernel (the same
+// functions, so the codes are identical) and stores them in the cache.  It
+// ends on a barrier: every code the work-group reads afterwards, the new
+// token's included, is in place (the stores and the later loads come from one
+// work-group on one CU).  `books` holds the staged K and V books, 32 copies
+// per entry (entry e, copy c at byte kBookStride e + 8 c), staged but not yet
+// synchronized; xr is 2 x 128 doubles of LDS.
+template <int G, int NW>
+__device__ __forceinline__ void fused_append_2bit(const DecodeArgs& a, int b, int h, double* xr, float* qr,
+                                                  const unsigned char* books) {
+    static_assert(NW == 16 && 4 + G <= NW, "64 sub-vectors x 16 slices fill the 1024 threads");
+    const AppendArgs& ap = a.app;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t stream = (int64_t)b * a.hkv + h;
+    // Position of the token: uniform, or per sequence; outside the cache it is
+    // not appended (block-uniform), as in the append kernel.
+    const int64_t t = ap.positions ? (int64_t)ap.positions[b] : (int64_t)ap.start_pos;
+    const bool app = t >= 0 && t < a.cap;
+    if (wave >= 4 && wave < 4 + G) {
+        const int64_t vec = (int64_t)b * a.hq + h * G + (wave - 4);
+        transform_query_wave((const char*)ap.q + vec * kHeadDim * (ap.dtype == 0 ? 2 : 4), ap.dtype,
+                             ap.smooth + (int64_t)h * kHeadDim, qr + (wave - 4) * kHeadDim, lane);
+    }
+    if (app && threadIdx.x < 2 * kHeadDim) {
+        const int c = threadIdx.x & (kHeadDim - 1), isv = threadIdx.x >> 7;
+        // Keys, and values of the value-transform variant: divided by their scales.
+        const float* div = isv ? a.v_smooth : ap.smooth;
+        const double e = load_elem_d(isv ? ap.v_new : ap.k_new, stream * kHeadDim + c, ap.dtype);
+        xr[isv * kHeadDim + c] = div ? e / (double)div[(int64_t)h * kHeadDim + c] : e;
+    }
+    __syncthreads();
+    if (app && (wave == 0 || (wave == 1 && a.v_smooth != nullptr))) rotate_row_wave(xr + wave * kHeadDim, lane);
+    __syncthreads();
+    if (app) {
+        // Sub-vector sv = thread / 16: key j = sv for sv < 32, value j = sv - 32;
+        // slice sl = entries sl, sl + 16, ..., copy lane % 32 of the book.
+        const int sv = threadIdx.x >> 4, sl = threadIdx.x & 15;
+        const int isv = sv >> 5, j = sv & 31;
+        double xs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[i] = xr[isv * kHeadDim + 4 * j + i];
+        const unsigned char* book = books + isv * kBookBytes + (lane & 31) * 8;
+        double best = __builtin_inf();
+        int idx = sl;
+#pragma unroll 4
+        for (int k = 0; k < 16; ++k) {
+            const int e = sl + 16 * k;
+            const double d = dist_h<4>(xs, (const uint16_t*)(book + e * kBookStride));
+            if (d < best) { best = d; idx = e; }
+        }
+        group_argmin<16>(best, idx);
+        if (sl == 0) {
+            // The token's 64-token block: in the stream, or (paged) the pool
+            // block the table names, clamped to the pool.
+            int64_t blk;
+            if (ap.block_table) {
+                int pb = ap.block_table[stream * (int64_t)(a.cap >> 6) + (t >> 6)];
+                pb = pb < 0 ? 0 : (pb >= ap.num_blocks ? ap.num_blocks - 1 : pb);
+                blk = (int64_t)pb * 2048;
+            } else {
+                blk = stream * (int64_t)a.cap * 32 + (t >> 6) * 2048;
+            }
+            const int u = (int)(t & 63);
+            if (isv == 0) ap.k_codes[blk + u * 32 + j] = (uint8_t)idx;
+            else ap.v_codes[blk + v_code_offset_2bit(u, j)] = (uint8_t)idx;
+        }
+    }
+    __syncthreads();
+}
+
 template <int V> struct IntC { static constexpr int value = V; };
 
 template <int I, int N, class F>
@@ -412,7 +493,7 @@ __device__ __forceinline__ uint32_t code12_x16(const uint32_t (&w)[N], uint32_t 
 // copies (2 x 64 KB).  Key codes are 24 bytes per token; value codes come in
 // 48-byte streams, one per lane pair, 16 pairs (sub-vectors j, j + 8) in step
 // order.
-template <int FMT, int G, int NW, bool PAGED>
+template <int FMT, int G, int NW, bool PAGED, bool APPEND = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int HB = (G + 3) / 4;
     constexpr int PT_BYTES = NW * HB * 512;
@@ -452,25 +533,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             ((uint4*)(smem + kBookBytes))[i] = vb[i];
         }
     }
-    // Query operands: lane 4c + i holds head 4hb + i's dims of (virtual)
-    // sub-vector 16r + c, times sm_scale * log2(e), rounded to fp16.
-    half4_t qa[HB][2];
-    {
-        const float* qp = a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim;
-        const int c = lane >> 2, i = lane & 3;
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int g = 4 * hb + i;
-                float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                if (g < G) q = *(const float4*)(qp + g * kHeadDim + 4 * (16 * r + c));
-                qa[hb][r] = half4_t{(_Float16)(q.x * a.qscale), (_Float16)(q.y * a.qscale),
-                                    (_Float16)(q.z * a.qscale), (_Float16)(q.w * a.qscale)};
-            }
-    }
-    __syncthreads();
-
     float m[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = kNegInf;
@@ -556,10 +618,67 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             for (int i = 0; i < 3; ++i) dv[i] = *(const uint4*)(vl1 + toff(tl) + 16 * i);
         }
     };
-    if (first < t_end) {
-        load_k(first);
-        load_v(first);
+    // 2-bit: a second code set, so each tile's codes arrive two tiles ahead
+    // (which matters when a wave has few tiles: six per wave at batch 1).
+    uint4 bk0, bk1, bv0, bv1;
+    auto load_first = [&]() {
+        if (first < t_end) {
+            load_k(first);
+            load_v(first);
+            if constexpr (FMT == 0) {
+                const int second = first + kStride < t_end ? first + kStride : first;
+                const int64_t o = toff(second);
+                bk0 = *(const uint4*)(kl0 + o);
+                bk1 = *(const uint4*)(kl0 + o + 16);
+                bv0 = *(const uint4*)(vl0 + o);
+                bv1 = *(const uint4*)(vl0 + o + 16);
+            }
+        }
+    };
+    bool loaded = false;
+    const float* qp;
+    if constexpr (!APPEND) {
+        qp = a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim;
+    } else {
+        // One-split decode step: q' and the new token's codes come first.
+        static_assert(FMT == 0, "the fused append codes 2-bit tokens");
+        static_assert(2 * kHeadDim * 8 + G * kHeadDim * 4 <= PT_BYTES, "rows and q' fit the probability tiles");
+        double* xr = (double*)(smem + 2 * kBookBytes);
+        float* qr = (float*)(smem + 2 * kBookBytes + 2 * kHeadDim * 8);
+        // The wave's first two tiles are requested before the append unless
+        // one of them holds the new token: their codes then wait for it.
+        const int64_t tn = a.app.positions ? (int64_t)a.app.positions[b] : (int64_t)a.app.start_pos;
+        bool early = true;
+        if (tn >= 0 && tn < a.cap && first < t_end) {
+            const int second = first + kStride < t_end ? first + kStride : first;
+            const int64_t nb = toff((int)(tn & ~(int64_t)63));
+            early = toff(first) != nb && toff(second) != nb;
+        }
+        if (early) {
+            load_first();
+            loaded = true;
+        }
+        fused_append_2bit<G, NW>(a, b, h, xr, qr, smem);
+        qp = qr;
     }
+    // Query operands: lane 4c + i holds head 4hb + i's dims of (virtual)
+    // sub-vector 16r + c, times sm_scale * log2(e), rounded to fp16.
+    half4_t qa[HB][2];
+    {
+        const int c = lane >> 2, i = lane & 3;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int g = 4 * hb + i;
+                float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (g < G) q = *(const float4*)(qp + g * kHeadDim + 4 * (16 * r + c));
+                qa[hb][r] = half4_t{(_Float16)(q.x * a.qscale), (_Float16)(q.y * a.qscale),
+                                    (_Float16)(q.z * a.qscale), (_Float16)(q.w * a.qscale)};
+            }
+    }
+    __syncthreads();
+    if (!loaded) load_first();
 
     // One tile; the 2-bit code registers are parameters so that two sets can
     // alternate (codes loaded two tiles ahead).
@@ -713,17 +832,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         wave_lds_sync();
     };
     if constexpr (FMT == 0) {
-        // Two code sets: each tile's codes arrive two tiles ahead, which
-        // matters when a wave has few tiles (batch 1: six per wave).
-        uint4 bk0, bk1, bv0, bv1;
-        if (first < t_end) {
-            const int second = first + kStride < t_end ? first + kStride : first;
-            const int64_t o = toff(second);
-            bk0 = *(const uint4*)(kl0 + o);
-            bk1 = *(const uint4*)(kl0 + o + 16);
-            bv0 = *(const uint4*)(vl0 + o);
-            bv1 = *(const uint4*)(vl0 + o + 16);
-        }
         for (int tile = first; tile < t_end; tile += 2 * kStride) {
             step(tile, tile + 2 * kStride < t_end ? tile + 2 * kStride : tile, ck0, ck1, cv0, cv1);
             const int t2 = tile + kStride;
@@ -968,6 +1076,21 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
             case 4: hipLaunchKernelGGL((decode_table_kernel<4, NW>), grid, dim3(NW * 64), 0, stream, a); break;
             default: return hipErrorInvalidValue;
         }
+        return hipGetLastError();
+    }
+    if (a.app.k_new != nullptr) {                           // fused append: 2-bit, one split, the output written
+        if (a.fmt != 0 || a.splits != 1 || a.out == nullptr || a.path != 3 || a.seq_lens) return hipErrorInvalidValue;
+        constexpr int NW = 16;
+        const bool paged = a.block_table != nullptr;
+#define VQKV_G(GV) case GV:                                                                                          \
+            if (paged) hipLaunchKernelGGL((decode_mfma_kernel<0, GV, NW, true, true>), grid, dim3(NW * 64), 0, stream, a); \
+            else hipLaunchKernelGGL((decode_mfma_kernel<0, GV, NW, false, true>), grid, dim3(NW * 64), 0, stream, a);      \
+            break;
+        switch (G) {
+            VQKV_G(1) VQKV_G(2) VQKV_G(3) VQKV_G(4) VQKV_G(5) VQKV_G(6) VQKV_G(7) VQKV_G(8)
+            default: return hipErrorInvalidValue;
+        }
+#undef VQKV_G
         return hipGetLastError();
     }
     if (a.path != 2) {

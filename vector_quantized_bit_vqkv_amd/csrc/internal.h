@@ -98,6 +98,13 @@ struct DecodeArgs {
     float* out;             // [B][Hq][128]
     int32_t* arrivals;      // [B][Hkv]
     const float* v_smooth;  // [Hkv][128] or null: with out, the output is mapped back, s_v * (H o)
+    // Fused append (2-bit, one split, out non-null), app.k_new non-null: each
+    // work-group first computes q' of its G query heads from app.q (q_prime is
+    // not read) and codes the new token of its (b, kv-head) into app.k_codes /
+    // app.v_codes, exactly as launch_quantize_append would; with app.positions,
+    // sequence b's length is positions[b] + 1 clamped to [0, cap] (seq_lens
+    // must be null).
+    AppendArgs app;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

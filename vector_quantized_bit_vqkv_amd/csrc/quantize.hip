@@ -21,14 +21,13 @@
 #include "device_util.h"
 #include "internal.h"
 #include "qtransform.h"
+#include "token_search.h"
 
 #pragma clang fp contract(off)
 
 namespace vqkv {
 
 namespace {
-
-constexpr double kInvSqrtHeadDimD = 0x1.6a09e667f3bcdp-4;
 
 template <int FMT> struct Fmt;
 template <> struct Fmt<0> { static constexpr int E = 256, DS = 4, J = 32, W = 32; };
@@ -39,10 +38,6 @@ template <> struct Fmt<2> { static constexpr int E = 4096, DS = 4, J = 32, W = 4
 template <int FMT>
 __device__ __forceinline__ int64_t v_pair_offset(int64_t t, int j) {
     return FMT == 1 ? v_pair_offset_1p5(t, j) : v_pair_offset_3bit(t, j);
-}
-
-__device__ __forceinline__ double load_elem_d(const void* base, int64_t i, int dtype) {
-    return (double)load_elem(base, i, dtype);
 }
 
 // In-place normalized FWHT of `ntok` rows of 128 fp64 values in LDS, by the
@@ -132,19 +127,6 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 template <int ABID>
 __device__ __forceinline__ float4_t mfma_bcast(half4_t a, half4_t b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, ABID, 0);
-}
-
-// Exact distance to an fp16 book entry, pinned order.
-template <int DS>
-__device__ __forceinline__ double dist_h(const double* x, const uint16_t* c) {
-    double t = x[0] - (double)half_bits_to_float(c[0]);
-    double d = t * t;
-#pragma unroll
-    for (int i = 1; i < DS; ++i) {
-        t = x[i] - (double)half_bits_to_float(c[i]);
-        d = d + t * t;
-    }
-    return d;
 }
 
 // Lexicographic (distance, index) minimum over the wave; every lane gets it.
@@ -543,18 +525,6 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
 
 // ------------------------------------------------- append of a single token
 
-// Lexicographic (distance, index) minimum over aligned groups of L lanes
-// (L a power of two <= 64); every lane of a group gets its group's minimum.
-template <int L>
-__device__ __forceinline__ void group_argmin(double& d, int& idx) {
-#pragma unroll
-    for (int m = 1; m < L; m <<= 1) {
-        const double od = __shfl_xor(d, m, 64);
-        const int oi = __shfl_xor(idx, m, 64);
-        if (od < d || (od == d && oi < idx)) { d = od; idx = oi; }
-    }
-}
-
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // |c|^2 and x.c for one codebook entry of DS fp16 values (LDS, 8- or
@@ -652,18 +622,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         }
     }
     __syncthreads();
-    if ((ph == 0 || a.v_smooth != nullptr) && threadIdx.x < 64) {   // the rotation (block-uniform)
-        const int l = threadIdx.x;
-        double lo = x[l], hi = x[l + 64];
-        for (int st = 1; st < 64; st <<= 1) {
-            const double olo = __shfl_xor(lo, st, 64), ohi = __shfl_xor(hi, st, 64);
-            if (l & st) { lo = olo - lo; hi = ohi - hi; }
-            else { lo = lo + olo; hi = hi + ohi; }
-        }
-        const double a0 = lo + hi, a1 = lo - hi;     // stage 64, within the lane
-        x[l] = a0 * kInvSqrtHeadDimD;
-        x[l + 64] = a1 * kInvSqrtHeadDimD;
-    }
+    if ((ph == 0 || a.v_smooth != nullptr) && threadIdx.x < 64)   // the rotation (block-uniform)
+        rotate_row_wave(x, threadIdx.x);
     __syncthreads();
     {
         const int jj = threadIdx.x / ES, sl = threadIdx.x % ES;
