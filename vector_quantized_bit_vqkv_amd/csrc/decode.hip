@@ -506,16 +506,31 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ __align__(16) unsigned char smem[SMEM];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // The wave index in a scalar register: the tile loop below is then
+    // uniform control flow (the compiler cannot see that threadIdx.x / 64 is
+    // the same in every lane of a wave).
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t_begin = s * a.chunk;
     const int t_end = min(seq_len_of(a, b), t_begin + a.chunk);
 
+    // 2-bit: codebook entries are fetched into registers here and written to
+    // LDS after the first tiles' code loads have been issued (loads complete
+    // in order, so waiting for book loads issued after the code loads would
+    // also wait for the codes, and the first tiles' latency would not overlap
+    // the staging).  The 12-bit formats stage their books directly: held in
+    // registers across the code loads, their 128 bytes per lane spill.
+    constexpr int BOOK_ITERS = FMT == 0 ? 256 * 32 / (NW * 64) : 1;
+    static_assert(FMT != 0 || (256 * 32) % (NW * 64) == 0, "the block stages whole rounds");
+    uint2 kreg[BOOK_ITERS], vreg[BOOK_ITERS];
     if constexpr (FMT == 0) {
+        // Slot i holds copy i % 32 of entry i / 32 (256 bytes per entry).
         const uint2* kb = (const uint2*)(a.k_book + (int64_t)h * 256 * 4);
         const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * 256 * 4);
-        for (int i = threadIdx.x; i < 256 * 32; i += NW * 64) {
-            ((uint2*)smem)[i] = kb[i >> 5];
-            ((uint2*)(smem + kBookBytes))[i] = vb[i >> 5];
+#pragma unroll
+        for (int k = 0; k < BOOK_ITERS; ++k) {
+            const int i = threadIdx.x + k * NW * 64;
+            kreg[k] = kb[i >> 5];
+            vreg[k] = vb[i >> 5];
         }
     } else if constexpr (FMT == 2) {
         // 3-bit: single copies, 8-byte entries (4 dims).
@@ -533,6 +548,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             ((uint4*)(smem + kBookBytes))[i] = vb[i];
         }
     }
+    auto write_books = [&]() {
+        if constexpr (FMT == 0) {
+#pragma unroll
+            for (int k = 0; k < BOOK_ITERS; ++k) {
+                const int i = threadIdx.x + k * NW * 64;
+                ((uint2*)smem)[i] = kreg[k];
+                ((uint2*)(smem + kBookBytes))[i] = vreg[k];
+            }
+        }
+    };
     float m[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = kNegInf;
@@ -549,7 +574,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // the pool, so no table entry can make the kernel read outside it).
     const uint8_t* kbase = PAGED ? a.k_codes : a.k_codes + stream * (int64_t)a.cap * W;
     const uint8_t* vbase = PAGED ? a.v_codes : a.v_codes + stream * (int64_t)a.cap * W;
-    const int32_t* btab = PAGED ? a.block_table + stream * (int64_t)(a.cap >> 6) : nullptr;
+    // The table is read-only here and the tile index is wave-uniform, so a
+    // constant-address-space view lets the compiler use scalar loads: a vector
+    // load of an entry would be counted with the code loads, and waiting for
+    // it would drain every code load in flight.
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const const_i32_ptr btab = PAGED ? (const_i32_ptr)(a.block_table + stream * (int64_t)(a.cap >> 6)) : nullptr;
     auto toff = [&](int tl) -> int64_t {
         if constexpr (!PAGED) {
             return (int64_t)tl * W;
@@ -621,28 +651,60 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // 2-bit: a second code set, so each tile's codes arrive two tiles ahead
     // (which matters when a wave has few tiles: six per wave at batch 1).
     uint4 bk0, bk1, bv0, bv1;
+    // Issued on every path: a wave without tiles reads tile 0, which every
+    // stream has (capacity >= 64 tokens; paged, table entries are clamped).
+    // With a path that skips them, the waits the compiler places for the
+    // query loads above would also cover these, and the first tiles' codes
+    // would have to arrive before the loop starts.
+    // The loads go out in the loop's own order (keys, values; set A, set B),
+    // so the waits inside the loop are the same on the first pass.
     auto load_first = [&]() {
-        if (first < t_end) {
-            load_k(first);
-            load_v(first);
-            if constexpr (FMT == 0) {
-                const int second = first + kStride < t_end ? first + kStride : first;
-                const int64_t o = toff(second);
-                bk0 = *(const uint4*)(kl0 + o);
-                bk1 = *(const uint4*)(kl0 + o + 16);
-                bv0 = *(const uint4*)(vl0 + o);
-                bv1 = *(const uint4*)(vl0 + o + 16);
-            }
+        const int f = first < t_end ? first : 0;
+        load_k(f);
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(f);
+        if constexpr (FMT == 0) {
+            const int second = first + kStride < t_end ? first + kStride : f;
+            const int64_t o = toff(second);
+            __builtin_amdgcn_sched_barrier(0);
+            bk0 = *(const uint4*)(kl0 + o);
+            bk1 = *(const uint4*)(kl0 + o + 16);
+            __builtin_amdgcn_sched_barrier(0);
+            bv0 = *(const uint4*)(vl0 + o);
+            bv1 = *(const uint4*)(vl0 + o + 16);
         }
     };
     bool loaded = false;
-    const float* qp;
+    // Query operands: lane 4c + i holds head 4hb + i's dims of (virtual)
+    // sub-vector 16r + c, times sm_scale * log2(e), rounded to fp16.
+    float4 qv[HB][2];
+    auto fetch_q = [&](const float* qp) {
+        const int c = lane >> 2, i = lane & 3;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int g = 4 * hb + i;
+                qv[hb][r] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (g < G) qv[hb][r] = *(const float4*)(qp + g * kHeadDim + 4 * (16 * r + c));
+            }
+    };
     if constexpr (!APPEND) {
-        qp = a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim;
+        // 2-bit: the query, then the first tiles' codes, then the books into
+        // LDS; the waits for the books and the query leave the codes in flight.
+        fetch_q(a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim);
+        if constexpr (FMT == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_first();
+            loaded = true;
+            __builtin_amdgcn_sched_barrier(0);
+            write_books();
+        }
     } else {
         // One-split decode step: q' and the new token's codes come first.
         static_assert(FMT == 0, "the fused append codes 2-bit tokens");
         static_assert(2 * kHeadDim * 8 + G * kHeadDim * 4 <= PT_BYTES, "rows and q' fit the probability tiles");
+        write_books();
         double* xr = (double*)(smem + 2 * kBookBytes);
         float* qr = (float*)(smem + 2 * kBookBytes + 2 * kHeadDim * 8);
         // The wave's first two tiles are requested before the append unless
@@ -659,24 +721,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             loaded = true;
         }
         fused_append_2bit<G, NW>(a, b, h, xr, qr, smem);
-        qp = qr;
+        fetch_q(qr);
     }
-    // Query operands: lane 4c + i holds head 4hb + i's dims of (virtual)
-    // sub-vector 16r + c, times sm_scale * log2(e), rounded to fp16.
     half4_t qa[HB][2];
-    {
-        const int c = lane >> 2, i = lane & 3;
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int g = 4 * hb + i;
-                float4 q = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                if (g < G) q = *(const float4*)(qp + g * kHeadDim + 4 * (16 * r + c));
-                qa[hb][r] = half4_t{(_Float16)(q.x * a.qscale), (_Float16)(q.y * a.qscale),
-                                    (_Float16)(q.z * a.qscale), (_Float16)(q.w * a.qscale)};
-            }
-    }
+        for (int r = 0; r < 2; ++r) {
+            const float4 q = qv[hb][r];
+            qa[hb][r] = half4_t{(_Float16)(q.x * a.qscale), (_Float16)(q.y * a.qscale),
+                                (_Float16)(q.z * a.qscale), (_Float16)(q.w * a.qscale)};
+        }
     __syncthreads();
     if (!loaded) load_first();
 
@@ -832,11 +887,20 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         wave_lds_sync();
     };
     if constexpr (FMT == 0) {
-        for (int tile = first; tile < t_end; tile += 2 * kStride) {
+        // Whole pairs of tiles in the loop, an odd last tile after it: the
+        // loop header is reached only after set B's loads, so the wait before
+        // set A's first use lets all seven younger loads stay in flight (with
+        // a skippable second step in the loop the compiler also waited for
+        // set B's first load, i.e. codes requested half a tile earlier).
+        const int ntiles = first < t_end ? (t_end - first + kStride - 1) / kStride : 0;
+        int tile = first;
+        for (int it = 0; it < (ntiles >> 1); ++it) {
             step(tile, tile + 2 * kStride < t_end ? tile + 2 * kStride : tile, ck0, ck1, cv0, cv1);
             const int t2 = tile + kStride;
-            if (t2 < t_end) step(t2, t2 + 2 * kStride < t_end ? t2 + 2 * kStride : t2, bk0, bk1, bv0, bv1);
+            step(t2, t2 + 2 * kStride < t_end ? t2 + 2 * kStride : t2, bk0, bk1, bv0, bv1);
+            tile += 2 * kStride;
         }
+        if (ntiles & 1) step(tile, tile, ck0, ck1, cv0, cv1);
     } else {
         for (int tile = first; tile < t_end; tile += kStride)
             step(tile, tile + kStride < t_end ? tile + kStride : tile, ck0, ck1, cv0, cv1);
