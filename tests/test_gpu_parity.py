@@ -624,12 +624,15 @@ def _paged_pool(kbytes, vbytes, W, seed, spare=3):
 
 @pytest.mark.parametrize("fmt,Hq,Hkv", [(0, 8, 2), (1, 10, 2), (2, 8, 2)])
 @pytest.mark.parametrize("S", [1, 7])
-def test_decode_paged_equals_contiguous(fmt, Hq, Hkv, S):
+@pytest.mark.parametrize("lens", [(1000, 700), (20000, 13001)])
+def test_decode_paged_equals_contiguous(fmt, Hq, Hkv, S, lens):
     """A cache scattered over a shuffled block pool gives bitwise the same output
-    as the contiguous cache (same arithmetic in the same order)."""
-    lens = [1000, 700]
+    as the contiguous cache (same arithmetic in the same order).  The long case
+    gives every wave about 20 tiles (table lookups for tiles loaded ahead) and
+    ragged last tiles."""
+    lens = list(lens)
     B, T = len(lens), max(lens)
-    say(f"decode paged fmt{fmt} S{S}")
+    say(f"decode paged fmt{fmt} S{S} lens{lens}")
     q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, B, Hq, Hkv, T, 600 + fmt)
     shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
     W = vq.code_bytes_per_token(fmt)
@@ -650,7 +653,7 @@ def test_decode_paged_equals_contiguous(fmt, Hq, Hkv, S):
         vq.combine(shape, S, ws, out)
         outs.append(out.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
-    ref = oracle.attention(fmt, q[1:2], s, kb, vb, kc[1:2, :, :700], vc[1:2, :, :700])
+    ref = oracle.attention(fmt, q[1:2], s, kb, vb, kc[1:2, :, :lens[1]], vc[1:2, :, :lens[1]])
     assert rel_err(outs[1][1:2], ref) <= TOL
 
 
