@@ -371,28 +371,75 @@ constexpr int kBookBytes = 256 * kBookStride;
 // work-group on one CU).  `books` holds the staged K and V books, 32 copies
 // per entry (entry e, copy c at byte kBookStride e + 8 c), staged but not yet
 // synchronized; xr is 2 x 128 doubles of LDS.
+// What the fused append reads from global memory, fetched before the first
+// tiles' code loads are issued: loads complete in order, so any wait for
+// these would otherwise also wait for the codes.  t is the token's position
+// (uniform; scalar loads), `app` whether it lies inside the cache.
+struct AppendFetch {
+    int64_t t;
+    bool app;
+    QueryPair qv;       // waves 4 .. 3 + G: the query row's elements and scales
+    uint32_t e;         // threads < 256: the key (value) element, raw (bf16 or fp32 bits)
+    float div;          // and its divisor
+    bool has_div;
+};
+
+// Uniform reads through the constant address space become scalar loads (the
+// arrays are not written by the kernel).
+template <class T>
+__device__ __forceinline__ T scalar_read(const T* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 template <int G, int NW>
-__device__ __forceinline__ void fused_append_2bit(const DecodeArgs& a, int b, int h, double* xr, float* qr,
-                                                  const unsigned char* books) {
+__device__ __forceinline__ AppendFetch fused_append_fetch(const DecodeArgs& a, int b, int h) {
+    const AppendArgs& ap = a.app;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t stream = (int64_t)b * a.hkv + h;
+    AppendFetch f;
+    // Position of the token: uniform, or per sequence; outside the cache it is
+    // not appended (block-uniform), as in the append kernel.
+    f.t = ap.positions ? (int64_t)scalar_read(ap.positions, b) : (int64_t)ap.start_pos;
+    f.app = f.t >= 0 && f.t < a.cap;
+    f.qv = QueryPair{0u, 0u, 0.0f, 0.0f, ap.dtype};
+    if (wave >= 4 && wave < 4 + G) {
+        const int64_t vec = (int64_t)b * a.hq + h * G + (wave - 4);
+        f.qv = load_query_pair((const char*)ap.q + vec * kHeadDim * (ap.dtype == 0 ? 2 : 4), ap.dtype,
+                               ap.smooth + (int64_t)h * kHeadDim, lane);
+    }
+    {
+        // Threads < 256: the key (value) element c and its divisor.  Every
+        // thread loads (the others element 0 and scale 0, always present), so
+        // no branch joins a loaded value with a constant: the compiler would
+        // convert right after the load and wait for it there.
+        const bool mine = f.app && threadIdx.x < 2 * kHeadDim;
+        const int c = threadIdx.x & (kHeadDim - 1), isv = (threadIdx.x >> 7) & 1;
+        // Keys, and values of the value-transform variant: divided by their scales.
+        const float* div = isv ? a.v_smooth : ap.smooth;
+        const void* row = isv ? ap.v_new : ap.k_new;
+        const int64_t i = mine ? stream * kHeadDim + c : 0;
+        f.e = ap.dtype == 0 ? (uint32_t)((const uint16_t*)row)[i] : ((const uint32_t*)row)[i];
+        f.has_div = div != nullptr;
+        f.div = (div ? div : ap.smooth)[mine ? (int64_t)h * kHeadDim + c : 0];
+    }
+    return f;
+}
+
+template <int G, int NW>
+__device__ __forceinline__ void fused_append_2bit(const DecodeArgs& a, int b, int h, const AppendFetch& f,
+                                                  double* xr, float* qr, const unsigned char* books) {
     static_assert(NW == 16 && 4 + G <= NW, "64 sub-vectors x 16 slices fill the 1024 threads");
     const AppendArgs& ap = a.app;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t stream = (int64_t)b * a.hkv + h;
-    // Position of the token: uniform, or per sequence; outside the cache it is
-    // not appended (block-uniform), as in the append kernel.
-    const int64_t t = ap.positions ? (int64_t)ap.positions[b] : (int64_t)ap.start_pos;
-    const bool app = t >= 0 && t < a.cap;
-    if (wave >= 4 && wave < 4 + G) {
-        const int64_t vec = (int64_t)b * a.hq + h * G + (wave - 4);
-        transform_query_wave((const char*)ap.q + vec * kHeadDim * (ap.dtype == 0 ? 2 : 4), ap.dtype,
-                             ap.smooth + (int64_t)h * kHeadDim, qr + (wave - 4) * kHeadDim, lane);
-    }
+    const int64_t t = f.t;
+    const bool app = f.app;
+    if (wave >= 4 && wave < 4 + G) transform_query_pair(f.qv, qr + (wave - 4) * kHeadDim, lane);
     if (app && threadIdx.x < 2 * kHeadDim) {
         const int c = threadIdx.x & (kHeadDim - 1), isv = threadIdx.x >> 7;
-        // Keys, and values of the value-transform variant: divided by their scales.
-        const float* div = isv ? a.v_smooth : ap.smooth;
-        const double e = load_elem_d(isv ? ap.v_new : ap.k_new, stream * kHeadDim + c, ap.dtype);
-        xr[isv * kHeadDim + c] = div ? e / (double)div[(int64_t)h * kHeadDim + c] : e;
+        // bf16 bits widen exactly (a select, so the conversion stays here).
+        const double e = (double)__builtin_bit_cast(float, ap.dtype == 0 ? f.e << 16 : f.e);
+        xr[isv * kHeadDim + c] = f.has_div ? e / (double)f.div : e;
     }
     __syncthreads();
     if (app && (wave == 0 || (wave == 1 && a.v_smooth != nullptr))) rotate_row_wave(xr + wave * kHeadDim, lane);
@@ -415,17 +462,17 @@ __device__ __forceinline__ void fused_append_2bit(const DecodeArgs& a, int b, in
             if (d < best) { best = d; idx = e; }
         }
         group_argmin<16>(best, idx);
+        // The token's 64-token block: in the stream, or (paged) the pool block
+        // the table names, clamped to the pool (a uniform, scalar read).
+        int64_t blk;
+        if (ap.block_table) {
+            int pb = scalar_read(ap.block_table, stream * (int64_t)(a.cap >> 6) + (t >> 6));
+            pb = pb < 0 ? 0 : (pb >= ap.num_blocks ? ap.num_blocks - 1 : pb);
+            blk = (int64_t)pb * 2048;
+        } else {
+            blk = stream * (int64_t)a.cap * 32 + (t >> 6) * 2048;
+        }
         if (sl == 0) {
-            // The token's 64-token block: in the stream, or (paged) the pool
-            // block the table names, clamped to the pool.
-            int64_t blk;
-            if (ap.block_table) {
-                int pb = ap.block_table[stream * (int64_t)(a.cap >> 6) + (t >> 6)];
-                pb = pb < 0 ? 0 : (pb >= ap.num_blocks ? ap.num_blocks - 1 : pb);
-                blk = (int64_t)pb * 2048;
-            } else {
-                blk = stream * (int64_t)a.cap * 32 + (t >> 6) * 2048;
-            }
             const int u = (int)(t & 63);
             if (isv == 0) ap.k_codes[blk + u * 32 + j] = (uint8_t)idx;
             else ap.v_codes[blk + v_code_offset_2bit(u, j)] = (uint8_t)idx;
@@ -704,23 +751,25 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         // One-split decode step: q' and the new token's codes come first.
         static_assert(FMT == 0, "the fused append codes 2-bit tokens");
         static_assert(2 * kHeadDim * 8 + G * kHeadDim * 4 <= PT_BYTES, "rows and q' fit the probability tiles");
-        write_books();
         double* xr = (double*)(smem + 2 * kBookBytes);
         float* qr = (float*)(smem + 2 * kBookBytes + 2 * kHeadDim * 8);
-        // The wave's first two tiles are requested before the append unless
-        // one of them holds the new token: their codes then wait for it.
-        const int64_t tn = a.app.positions ? (int64_t)a.app.positions[b] : (int64_t)a.app.start_pos;
-        bool early = true;
-        if (tn >= 0 && tn < a.cap && first < t_end) {
+        // The append's own loads, then the wave's first two tiles, then the
+        // books into LDS: the append's waits leave the code loads in flight.
+        // If one of the two tiles holds the new token its codes are requested
+        // again after the append (the first loads read the old bytes).
+        const AppendFetch af = fused_append_fetch<G, NW>(a, b, h);
+        bool stale = false;
+        if (af.app && first < t_end) {
             const int second = first + kStride < t_end ? first + kStride : first;
-            const int64_t nb = toff((int)(tn & ~(int64_t)63));
-            early = toff(first) != nb && toff(second) != nb;
+            const int64_t nb = toff((int)(af.t & ~(int64_t)63));
+            stale = toff(first) == nb || toff(second) == nb;
         }
-        if (early) {
-            load_first();
-            loaded = true;
-        }
-        fused_append_2bit<G, NW>(a, b, h, xr, qr, smem);
+        __builtin_amdgcn_sched_barrier(0);
+        load_first();
+        loaded = !stale;
+        __builtin_amdgcn_sched_barrier(0);
+        write_books();
+        fused_append_2bit<G, NW>(a, b, h, af, xr, qr, smem);
         fetch_q(qr);
     }
     half4_t qa[HB][2];
