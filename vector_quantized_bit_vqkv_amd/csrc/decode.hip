@@ -942,12 +942,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         // a skippable second step in the loop the compiler also waited for
         // set B's first load, i.e. codes requested half a tile earlier).
         const int ntiles = first < t_end ? (t_end - first + kStride - 1) / kStride : 0;
+        // The waves of a work-group are kept in step: the instruction arbiter
+        // favours the oldest wave of each SIMD, and left alone the four age
+        // groups drift apart (at 192 tiles per wave the youngest finished
+        // ~40% of the pass after the oldest, leaving fewer waves with loads
+        // in flight).  A bare s_barrier (no memory fence, so no wait for the
+        // code loads) every kSyncTiles tiles, up to the tile count of the last
+        // wave, which has the fewest: every wave executes the same barriers.
+        constexpr int kSyncTiles = 16;
+        const int last_first = t_begin + (NW - 1) * 64;
+        const int nmin = last_first < t_end ? (t_end - last_first + kStride - 1) / kStride : 0;
         int tile = first;
         for (int it = 0; it < (ntiles >> 1); ++it) {
             step(tile, tile + 2 * kStride < t_end ? tile + 2 * kStride : tile, ck0, ck1, cv0, cv1);
             const int t2 = tile + kStride;
             step(t2, t2 + 2 * kStride < t_end ? t2 + 2 * kStride : t2, bk0, bk1, bv0, bv1);
             tile += 2 * kStride;
+            if ((2 * (it + 1)) % kSyncTiles == 0 && 2 * (it + 1) <= nmin) __builtin_amdgcn_s_barrier();
         }
         if (ntiles & 1) step(tile, tile, ck0, ck1, cv0, cv1);
     } else {
