@@ -700,6 +700,8 @@ STEP_CASES = [
     (0, 3, 8, 8, 2000, 1, "fp32"),        # G = 1
     (0, 2, 12, 4, 63, 1, "bf16"),         # G = 3, the last position of a block
     (0, 1, 40, 8, 64, 1, "bf16"),         # G = 5, the first position of a block
+    (0, 1, 8, 2, 20000, 1, "bf16"),       # ~20 tiles per wave: the waves' in-step barriers
+    (0, 2, 8, 2, 17000, 3, "fp32"),       # two launches, three splits of ~5.7k tokens
 ]
 
 
