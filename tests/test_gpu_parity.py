@@ -462,6 +462,48 @@ def test_quantize_fallbacks_match_oracle(fmt):
         assert np.array_equal(oracle.unpack_v(fmt, vcodes[0, 0].cpu().numpy(), n), vc_ref), mode
 
 
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantize_degenerate_scales_match_oracle(fmt):
+    """Smoothing scales are device data the library does not inspect (that would
+    need a synchronizing copy).  A negative and an infinite scale (that channel
+    becomes 0), a tiny one (rotated coordinates near 1e5: past the fp16 range of
+    the screen, so the exact scan decides), and a zero one (infinite or NaN
+    coordinates: every key code is 0, the lowest index) give the oracle's codes
+    in the bulk and in the one-token path; values are not divided and keep
+    ordinary codes."""
+    say(f"quantize degenerate scales fmt{fmt}")
+    E, dsub = oracle.FORMATS[fmt]
+    rng = np.random.default_rng(31 + fmt)
+    n = 24
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    k[4, 5] = 0.0                     # 0 / 0 = NaN in the second set
+    base = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    s1, s2, s3 = base.copy(), base.copy(), base.copy()
+    s1[9], s1[20] = -1.5, np.inf
+    s2[33] = 1e-6
+    s3[5] = 0.0
+    kb = synth.random_fp16_book(41, (1, E, dsub), 0.8)
+    vb = synth.random_fp16_book(42, (1, E, dsub), 1.0)
+    shape = vq.make_shape(1, 1, 1, 64, fmt)
+    W = vq.code_bytes_per_token(fmt)
+    for s_ in (s1, s2, s3):
+        kc_ref, vc_ref = oracle.quantize(fmt, k, v, s_, kb[0], vb[0])
+        for mode in ("bulk", "one-token"):
+            kcodes = torch.zeros((1, 1, 64 * W), dtype=torch.uint8, device=DEV)
+            vcodes = torch.zeros_like(kcodes)
+            if mode == "bulk":
+                vq.quantize_append(shape, dev(k[None, None]), dev(v[None, None]), 0, dev(s_[None]), book_dev(kb),
+                                   book_dev(vb), kcodes, vcodes)
+            else:
+                for t in range(n):
+                    vq.quantize_append(shape, dev(k[None, None, t:t + 1]), dev(v[None, None, t:t + 1]), t,
+                                       dev(s_[None]), book_dev(kb), book_dev(vb), kcodes, vcodes)
+            torch.cuda.synchronize()
+            assert np.array_equal(oracle.unpack_k(fmt, kcodes[0, 0].cpu().numpy(), n), kc_ref), mode
+            assert np.array_equal(oracle.unpack_v(fmt, vcodes[0, 0].cpu().numpy(), n), vc_ref), mode
+
+
 # ---------------------------------------------------------------------- attention
 
 def _attn_inputs(fmt, B, Hq, Hkv, T, seed, cap=None):
