@@ -261,20 +261,24 @@ vqkv_status vqkv_quantize_append_paged(const vqkv_shape* shape, const void* k_ne
 vqkv_status vqkv_combine(const vqkv_shape* shape, int32_t num_splits, const void* workspace,
                          float* out, void* stream);
 
-/* One decode step: the append of one new token per sequence at `position`
- * (with the query transform in the same launch), then the attention of every
- * query over tokens [0, position] with the split combine fused into it; for
- * the 2-bit format with num_splits = 1 the attention kernel does the append
- * and the query transform itself (one launch).  The result is bit-identical
- * to the four calls
+/* One decode step: the append of one new token per sequence at `position`,
+ * the query transform, the attention of every query over tokens
+ * [0, position] and the split combine.  The result is bit-identical to the
+ * four calls
  *   vqkv_quantize_append(n_new = 1, start_pos = position), vqkv_transform_query,
  *   vqkv_decode_attention(seq_len = position + 1), vqkv_combine
- * on the same arguments (the same kernels' arithmetic).  With one split the
- * attention kernel writes `out` itself; with more, the last split of each
- * (b, KV head) to finish combines that head's splits (a per-head arrival
- * counter in the workspace, cleared by the first launch of every step, so the
- * workspace needs no initialization; one split needs no counter).  Runs on
- * the matrix-core kernel.
+ * on the same arguments (the same kernels' arithmetic).  Runs on the
+ * matrix-core kernel, in one or two launches:
+ *   - 2-bit without VQKV_FMT_VALUE_TRANSFORM: the attention kernel appends
+ *     the token (in the work-group whose split holds `position`) and
+ *     transforms its queries itself; with one split it writes `out` directly
+ *     (one launch), with more it writes the splits' partials to the
+ *     workspace and vqkv_combine's kernel merges them (two launches);
+ *   - the other formats: an append launch that also transforms the query,
+ *     then the attention, where the last split of each (b, KV head) to finish
+ *     combines that head's splits (a per-head arrival counter in the
+ *     workspace, cleared by the append launch of every step, so the
+ *     workspace needs no initialization; one split needs no counter). */
  *   q                 device, [B][Hq][128], dtype (the same dtype as k_new)
  *   k_new, v_new      device, [B][Hkv][1][128], dtype
  *   position          host, 0 <= position < max_tokens
@@ -298,7 +302,8 @@ vqkv_status vqkv_decode_step(const vqkv_shape* shape, const void* q, const void*
  * max_seq_len) and vqkv_combine; a position outside [0, max_tokens) leaves the
  * cache untouched and its length is clamped to [0, max_tokens] as in the
  * varlen decode (a negative position gives a zero output).  The lengths are
- * computed on the device into the workspace.
+ * derived from positions on the device (into the workspace when an append
+ * launch runs first).
  *   positions     device, int32 [B], 4-byte aligned
  *   max_seq_len   host, 1 <= max_seq_len <= max_tokens, >= every positions[b] + 1
  *   num_splits    host, 1 <= num_splits <= ceil(max_seq_len / 64)

@@ -417,6 +417,21 @@ vqkv_status decode_step_impl(const vqkv_shape* s, const void* q, const void* k_n
         snprintf(what, sizeof(what), "%s fused decode launch", name);
         return hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what);
     }
+    if (base_fmt(s->fmt) == 0 && ap.v_smooth == nullptr) {
+        // Two launches: the attention kernel appends the token in the work-group
+        // whose split holds it (every work-group transforms its query heads) and
+        // writes the splits' partials, then the combine kernel merges them (no
+        // arrival counters).
+        d.q_prime = nullptr;
+        d.seq_lens = nullptr;
+        d.app = ap;
+        d.out = nullptr;
+        snprintf(what, sizeof(what), "%s fused decode launch", name);
+        VQKV_CHECK(hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what));
+        vqkv::CombineArgs c{part_o, part_lse, out, s->batch, s->num_q_heads, num_splits};
+        snprintf(what, sizeof(what), "%s combine launch", name);
+        return hip_status(vqkv::launch_combine(c, (hipStream_t)stream), what);
+    }
     snprintf(what, sizeof(what), "%s append launch", name);
     VQKV_CHECK(hip_status(vqkv::launch_quantize_append(ap, (hipStream_t)stream), what));
     snprintf(what, sizeof(what), "%s decode launch", name);

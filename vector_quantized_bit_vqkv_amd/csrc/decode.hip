@@ -398,9 +398,12 @@ __device__ __forceinline__ AppendFetch fused_append_fetch(const DecodeArgs& a, i
     const int64_t stream = (int64_t)b * a.hkv + h;
     AppendFetch f;
     // Position of the token: uniform, or per sequence; outside the cache it is
-    // not appended (block-uniform), as in the append kernel.
+    // not appended (block-uniform), as in the append kernel.  With several
+    // splits only the work-group whose token range holds it appends it (the
+    // others never read that tile); every work-group transforms the query.
     f.t = ap.positions ? (int64_t)scalar_read(ap.positions, b) : (int64_t)ap.start_pos;
-    f.app = f.t >= 0 && f.t < a.cap;
+    const int64_t t_begin = (int64_t)blockIdx.x * a.chunk;
+    f.app = f.t >= 0 && f.t < a.cap && f.t >= t_begin && f.t < t_begin + a.chunk;
     f.qv = QueryPair{0u, 0u, 0.0f, 0.0f, ap.dtype};
     if (wave >= 4 && wave < 4 + G) {
         const int64_t vec = (int64_t)b * a.hq + h * G + (wave - 4);
@@ -1202,8 +1205,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         }
         return hipGetLastError();
     }
-    if (a.app.k_new != nullptr) {                           // fused append: 2-bit, one split, the output written
-        if (a.fmt != 0 || a.splits != 1 || a.out == nullptr || a.path != 3 || a.seq_lens) return hipErrorInvalidValue;
+    if (a.app.k_new != nullptr) {
+        // Fused append, 2-bit: one split writes the output itself, several write
+        // the splits' partials for the combine kernel.
+        if (a.fmt != 0 || a.path != 3 || a.seq_lens || (a.splits == 1) != (a.out != nullptr)) return hipErrorInvalidValue;
         constexpr int NW = 16;
         const bool paged = a.block_table != nullptr;
 #define VQKV_G(GV) case GV:                                                                                          \
