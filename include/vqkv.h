@@ -278,7 +278,7 @@ vqkv_status vqkv_combine(const vqkv_shape* shape, int32_t num_splits, const void
  *     then the attention, where the last split of each (b, KV head) to finish
  *     combines that head's splits (a per-head arrival counter in the
  *     workspace, cleared by the append launch of every step, so the
- *     workspace needs no initialization; one split needs no counter). */
+ *     workspace needs no initialization; one split needs no counter).
  *   q                 device, [B][Hq][128], dtype (the same dtype as k_new)
  *   k_new, v_new      device, [B][Hkv][1][128], dtype
  *   position          host, 0 <= position < max_tokens
@@ -318,7 +318,11 @@ vqkv_status vqkv_decode_step_varlen(const vqkv_shape* shape, const void* q, cons
 /* The fused step for paged caches: as vqkv_decode_step_varlen, with the codes
  * in a pool of 64-token blocks named by block_table (pool and table as for
  * vqkv_decode_attention_paged); bit-identical to vqkv_quantize_append_paged,
- * vqkv_transform_query, vqkv_decode_attention_paged and vqkv_combine. */
+ * vqkv_transform_query, vqkv_decode_attention_paged and vqkv_combine,
+ * provided that the pool block receiving a sequence's new token is named by no
+ * other table entry the step reads (another logical block below some
+ * sequence's length): for 2-bit the append and the attention share one launch,
+ * so a work-group reading such a block may see it before or after the write. */
 vqkv_status vqkv_decode_step_paged(const vqkv_shape* shape, const void* q, const void* k_new,
                                    const void* v_new, int32_t dtype, const int32_t* positions,
                                    int32_t max_seq_len, const float* smooth, const uint16_t* k_book,

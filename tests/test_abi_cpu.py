@@ -27,6 +27,20 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+@pytest.mark.parametrize("header", ["vqkv.h", "vqkv_baseline.h"])
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_headers_compile_standalone(header, lang):
+    """Each public header compiles on its own, as C and as C++, warning-free."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no host compiler")
+    r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", "-x", lang, os.path.join(ROOT, "include", header)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_size_queries():
     assert vq.code_bytes_per_token(vq.FMT_2BIT) == 32
     assert vq.code_bytes_per_token(vq.FMT_1P5BIT) == 24
