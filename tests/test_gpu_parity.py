@@ -795,6 +795,107 @@ def test_decode_step_equals_the_four_calls(fmt, B, Hq, Hkv, pos, S, dtype):
     assert err <= TOL
 
 
+def _hadamard():
+    H = np.array([[1.0]])
+    while H.shape[0] < D:
+        H = np.block([[H, H], [H, -H]])
+    return H / math.sqrt(D)
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_fused_step_append_hard_cases_match_oracle(S):
+    """The 2-bit step appends inside the attention kernel (one split: every
+    work-group, three: the one whose split holds the token) with an fp32
+    distance screen and the pinned fp64 distance for the survivors.  Tokens
+    appended one step at a time must get the oracle's codes on: a duplicated
+    entry (the lower index wins), midpoints of fp16 neighbours one ulp apart
+    (below fp32 resolution), exact value midpoints, a negative, an infinite and
+    a tiny scale (coordinates near 1e5), a zero scale (infinite or NaN
+    coordinates), NaN elements, and values past the fp32 range of squares."""
+    say(f"fused step append hard cases S{S}")
+    fmt, B, Hq, Hkv, cap, p0, n = 0, 1, 8, 2, 256, 192, 16
+    E, dsub = oracle.FORMATS[fmt]
+    J = D // dsub
+    H = _hadamard()
+    rng = np.random.default_rng(77 + S)
+
+    def near_tie_book(seed):
+        r = np.random.default_rng(seed)
+        base = (r.standard_normal((E // 2, dsub)) * 0.5).astype(np.float16)
+        base[:, 0] = np.abs(base[:, 0]) + np.float16(0.25)
+        up = base.copy()
+        up[:, 0] = np.nextafter(base[:, 0], np.float16(np.inf))
+        return base, up, np.concatenate([base, up]).view(np.uint16)
+
+    scenarios = []
+    # 1. Head 0: near ties one fp16 ulp apart; head 1: a duplicated entry hit exactly.
+    base, up, ntb = near_tie_book(5)
+    kb = np.stack([ntb, synth.random_fp16_book(6, (1, E, dsub), 0.5)[0]])
+    kb[1, 200] = kb[1, 17]
+    s = rng.uniform(0.5, 2.0, (Hkv, D)).astype(np.float32)
+    pick = rng.integers(0, E // 2, (n, J))
+    xt = base[pick].astype(np.float64)
+    xt[:, :, 0] = 0.5 * (base[pick, 0].astype(np.float64) + up[pick, 0].astype(np.float64))
+    k = np.empty((n, Hkv, D), np.float32)
+    k[:, 0] = (xt.reshape(n, D) @ H) * s[0]
+    c17 = kb[1, 17].view(np.float16).astype(np.float64)
+    k[:, 1] = (np.tile(c17, J)[None] @ H) * s[1]
+    vb = np.zeros((Hkv, E, dsub), np.float16)
+    vb[:, :, 0] = np.arange(E, dtype=np.float64) * 0.25
+    vb[:, E - 1] = vb[:, 5]
+    v = np.zeros((n, Hkv, D), np.float32)
+    v[:, :, ::dsub] = (rng.integers(0, 200, (n, Hkv, J)) * 0.25 + 0.125).astype(np.float32)
+    v[:3, :, 0] = 1.25                                           # entries 5 and E - 1: 5 wins
+    scenarios.append(("ties", k, v, s, kb, vb.view(np.uint16)))
+    # 2. Degenerate scales: negative and infinite (head 0), tiny (head 1).
+    s = rng.uniform(0.5, 2.0, (Hkv, D)).astype(np.float32)
+    s[0, 9], s[0, 20], s[1, 33] = -1.5, np.inf, 1e-6
+    k = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    scenarios.append(("scales", k, v, s, synth.random_fp16_book(8, (Hkv, E, dsub), 0.8),
+                      synth.random_fp16_book(9, (Hkv, E, dsub), 1.0)))
+    # 3. Fallbacks: a zero scale (0 / 0 = NaN and x / 0 = inf), NaN elements,
+    #    huge keys and values (squares past the fp32 range).
+    s = rng.uniform(0.5, 2.0, (Hkv, D)).astype(np.float32)
+    s[0, 5] = 0.0
+    k = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    k[::2, 0, 5] = 0.0
+    k[1, 1] *= 3.0e5
+    k[3, 1] *= 1.0e19
+    k[5, 1, 7] = np.nan
+    v[2, 0, 9] = np.nan
+    v[4, 1, :dsub] = 2.0e19
+    v[6, 0] *= 1.0e25
+    scenarios.append(("fallbacks", k, v, s, synth.random_fp16_book(10, (Hkv, E, dsub), 0.8),
+                      synth.random_fp16_book(11, (Hkv, E, dsub), 1.0)))
+
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    for name, k, v, s, kb, vb in scenarios:
+        kc0 = synth.random_codes(12, (B, Hkv, cap, J), E)
+        vc0 = synth.random_codes(13, (B, Hkv, cap, J), E)
+        kbytes, vbytes = oracle.pack_stream(fmt, kc0, vc0, cap)
+        kcodes, vcodes = dev(kbytes), dev(vbytes)
+        books, sm = (book_dev(kb), book_dev(vb)), dev(s)
+        ws = torch.empty(vq.step_workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+        qd = dev(rng.standard_normal((B, Hq, D)).astype(np.float32))
+        for t in range(n):
+            vq.decode_step(shape, qd, dev(k[None, t, :, None]), dev(v[None, t, :, None]), p0 + t, sm, books[0],
+                           books[1], kcodes, vcodes, S, ws, out)
+        torch.cuda.synchronize()
+        for h in range(Hkv):
+            kc_ref, vc_ref = oracle.quantize(fmt, k[:, h], v[:, h], s[h], kb[h], vb[h])
+            gk = oracle.unpack_k(fmt, kcodes[0, h].cpu().numpy(), p0 + n)[p0:]
+            gv = oracle.unpack_v(fmt, vcodes[0, h].cpu().numpy(), p0 + n)[p0:]
+            assert np.array_equal(gk, kc_ref), (name, h, np.argwhere(gk != kc_ref)[:5])
+            assert np.array_equal(gv, vc_ref), (name, h, np.argwhere(gv != vc_ref)[:5])
+            if name == "ties" and h == 1:
+                assert np.all(gk == 17)
+            # The cache outside the appended rows is untouched.
+            assert np.array_equal(oracle.unpack_k(fmt, kcodes[0, h].cpu().numpy(), p0), kc0[0, h, :p0])
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_step_captured_in_a_graph_replays_exactly(fmt):
     """One decode step (append of one token per sequence, query transform,
