@@ -32,6 +32,27 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 
 _head = {}
+RUNS = 5                      # timed runs per figure: the median is reported, with p10 and p90
+
+
+def pct(xs, p):
+    """Nearest-rank p-quantile of xs (p in [0, 1])."""
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(p * (len(xs) - 1)))))]
+
+
+def host_cpu():
+    """The host CPU's model name and the number of CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
 
 # HBM traffic of the decode kernel comes from rocprofv3 counters recorded in
 # this file, valid only while the kernel sources still hash to the recorded value.
@@ -82,19 +103,20 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_b32_t196k")
-    ap.add_argument("--also", default="llama8b_b1_t196k,llama8b_b1_t32k",
+    ap.add_argument("--also", default="llama8b_b1_t196k,llama8b_b1_t32k,qwen14b_b8_t128k_1p5,llama8b_b8_t196k_3bit",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
-    ap.add_argument("--decode-path", default="", help="force 'table' or 'gather' (measurement)")
+    ap.add_argument("--decode-path", default="", choices=["", "table", "gather", "mfma"],
+                    help="time the decode on another kernel (measurement; the four separate calls)")
     return ap.parse_args()
 
 
 class Workload:
     """Device-resident state of one workload: calibration, codebooks, codes, step inputs."""
 
-    def __init__(self, name, dev, keep_bf16):
+    def __init__(self, name, dev, keep_bf16, keep_inputs=False):
         import torch
 
         import synth
@@ -147,7 +169,12 @@ class Workload:
         self.caches = [(k_codes, v_codes)] + [(k_codes.clone(), v_codes.clone()) for _ in range(R - 1)]
         self.k_bf16 = case["k"] if keep_bf16 else None
         self.v_bf16 = case["v"] if keep_bf16 else None
+        # The drawn inputs (calibration rows, keys, values, queries), kept for
+        # checking against the oracle; the benchmark itself drops them.
+        self.case = case if keep_inputs else None
+        self.seed = seed
         del case
+        self.decode_path = ""
         self.S = vq.suggest_splits(self.shape, T)
         self.q_prime = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
@@ -162,6 +189,18 @@ class Workload:
                            + B * Hq * 128 * 4                                           # out (fp32)
                            + 2 * B * Hkv * 128 * 2 + 2 * B * Hkv * W)                   # new k, v; new codes
 
+    def decode(self, kc, vc):
+        """The attention pass as vqkv_decode_attention launches it (or, for
+        measurement, on the kernel named by decode_path)."""
+        import vector_quantized_bit_vqkv_amd as vq
+        T = self.wl.seq_len
+        if self.decode_path:
+            vq.measure_decode_attention(self.shape, self.q_prime, self.k_book, self.v_book, kc, vc, T, self.S,
+                                        self.workspace, self.decode_path)
+        else:
+            vq.decode_attention(self.shape, self.q_prime, self.k_book, self.v_book, kc, vc, T, self.S,
+                                self.workspace)
+
     def step(self, i, ev=None):
         import vector_quantized_bit_vqkv_amd as vq
         kc, vc = self.caches[i % len(self.caches)]
@@ -170,7 +209,7 @@ class Workload:
         vq.transform_query(self.shape, self.q, self.smooth, self.q_prime)
         if ev is not None:
             ev[0].record()
-        vq.decode_attention(self.shape, self.q_prime, self.k_book, self.v_book, kc, vc, T, self.S, self.workspace)
+        self.decode(kc, vc)
         if ev is not None:
             ev[1].record()
         vq.combine(self.shape, self.S, self.workspace, self.out)
@@ -182,41 +221,47 @@ class Workload:
         vq.decode_step(self.shape, self.q, self.k_new, self.v_new, T - 1, self.smooth, self.k_book, self.v_book,
                        kc, vc, self.S, self.step_workspace, self.out)
 
-    def time_fused_steps(self, steps, warmup):
+    def time_fused_steps(self, steps, warmup, runs=RUNS):
         """The same step through decode_step: the combine fused into the decode, and with one
-        2-bit split the append too (one launch; else the append is a launch of its own)."""
+        2-bit split the append too (one launch; else the append is a launch of its own).
+        Returns the mean ms per step of each of `runs` timed runs of exactly `steps` steps."""
         import torch
         for i in range(warmup):
             self.fused_step(i)
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        head_start(self.q.device)
-        start.record()
-        for i in range(steps):
-            self.fused_step(warmup + i)
-        end.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / steps
+        per_run = []
+        for r in range(runs):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            head_start(self.q.device)
+            start.record()
+            for i in range(steps):
+                self.fused_step(warmup + r * steps + i)
+            end.record()
+            torch.cuda.synchronize()
+            per_run.append(start.elapsed_time(end) / steps)
+        return per_run
 
-    def time_steps(self, steps, warmup):
+    def time_steps(self, steps, warmup, runs=RUNS):
+        """The step as four separate calls, with events around every decode launch.
+        Returns the mean ms per step of each run and every decode launch's ms."""
         import torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        head_start(self.q.device)
-        start.record()
-        for i in range(steps):
-            self.step(warmup + i, evs[i])
-        end.record()
-        torch.cuda.synchronize()
-        step_ms = start.elapsed_time(end) / steps
-        dec = sorted(a.elapsed_time(b) for a, b in evs)
-        self.decode_p10 = dec[int(0.1 * (len(dec) - 1))]
-        self.decode_p90 = dec[int(0.9 * (len(dec) - 1))]
-        return step_ms, sum(dec) / len(dec), dec[len(dec) // 2]
+        per_run, dec = [], []
+        for r in range(runs):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            head_start(self.q.device)
+            start.record()
+            for i in range(steps):
+                self.step(warmup + r * steps + i, evs[i])
+            end.record()
+            torch.cuda.synchronize()
+            per_run.append(start.elapsed_time(end) / steps)
+            dec.extend(a.elapsed_time(b) for a, b in evs)
+        return per_run, dec
 
     def time_attention_only(self, steps, warmup):
         """decode + combine only (what the bf16 comparison times)."""
@@ -226,7 +271,7 @@ class Workload:
 
         def once(i):
             kc, vc = self.caches[i % len(self.caches)]
-            vq.decode_attention(self.shape, self.q_prime, self.k_book, self.v_book, kc, vc, T, self.S, self.workspace)
+            self.decode(kc, vc)
             vq.combine(self.shape, self.S, self.workspace, self.out)
         for i in range(warmup):
             once(i)
@@ -278,13 +323,16 @@ class Workload:
     def cpu_baseline(self, budget_s):
         """The CPU oracle on a bounded sample of this step: whole sequences (all
         query heads, full context), attention plus the append's quantization,
-        timed until the budget is spent, then scaled to the full batch."""
+        timed until the budget is spent, then scaled to the full batch; first on
+        every CPU this process may use, then on one thread (a quarter of the
+        budget, at least one sequence)."""
         import numpy as np
 
         import oracle
         wl = self.wl
         B, Hq, Hkv, T, fmt = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.seq_len, wl.fmt
         threads = oracle.default_threads()
+        model, affinity = host_cpu()
         kb = self.k_book.cpu().numpy().view(np.uint16)
         vb = self.v_book.cpu().numpy().view(np.uint16)
         s = self.smooth.cpu().numpy()
@@ -292,31 +340,45 @@ class Workload:
         kn = self.k_new.float().cpu().numpy()
         vn = self.v_new.float().cpu().numpy()
         kc_dev, vc_dev = self.caches[0]
-        # Sequences in order, each unpacked once (outside the timing); when the
-        # batch is done before the budget, the first few are timed again.
-        kept, spent, done = [], 0.0, 0
-        while spent < budget_s:
-            if done < B:
-                b = done
-                kc = np.stack([oracle.unpack_k(fmt, kc_dev[b, h].cpu().numpy(), T) for h in range(Hkv)])[None]
-                vc = np.stack([oracle.unpack_v(fmt, vc_dev[b, h].cpu().numpy(), T) for h in range(Hkv)])[None]
+        kept = []
+
+        def sequence(i):
+            # Sequences in order, each unpacked once (outside the timing); past
+            # the batch, the first few are timed again.
+            if i < B:
+                kc = np.stack([oracle.unpack_k(fmt, kc_dev[i, h].cpu().numpy(), T) for h in range(Hkv)])[None]
+                vc = np.stack([oracle.unpack_v(fmt, vc_dev[i, h].cpu().numpy(), T) for h in range(Hkv)])[None]
                 if len(kept) < 4:
-                    kept.append((b, kc, vc))
-            else:
-                b, kc, vc = kept[(done - B) % len(kept)]
-            t0 = time.perf_counter()
-            for h in range(Hkv):
-                oracle.quantize(fmt, kn[b, h], vn[b, h], s[h], kb[h], vb[h], nthreads=threads)
-            oracle.attention(fmt, q[b:b + 1], s, kb, vb, kc, vc, nthreads=threads)
-            spent += time.perf_counter() - t0
-            done += 1
+                    kept.append((i, kc, vc))
+                return i, kc, vc
+            return kept[(i - B) % len(kept)]
+
+        def timed(nthreads, budget):
+            spent, done = 0.0, 0
+            while spent < budget or done == 0:
+                b, kc, vc = sequence(done)
+                t0 = time.perf_counter()
+                for h in range(Hkv):
+                    oracle.quantize(fmt, kn[b, h], vn[b, h], s[h], kb[h], vb[h], nthreads=nthreads)
+                oracle.attention(fmt, q[b:b + 1], s, kb, vb, kc, vc, nthreads=nthreads)
+                spent += time.perf_counter() - t0
+                done += 1
+            return spent, done
+
+        spent, done = timed(threads, budget_s)
         full_s = spent / done * B
+        spent1, done1 = timed(1, budget_s / 4)
+        full1 = spent1 / done1 * B
+        what = (f"sequence computations (all {Hq} q-heads, {T} tokens each: fp64 oracle attention plus "
+                f"quantization of the appended token), scaled to the batch of {B}")
         return {"value": round(self.step_bytes / full_s / 1e9, 3), "unit": "GB/s", "cores": threads,
                 "kind": "oracle",
-                "sample": f"{done} sequence computations over {min(done, B)} of {B} sequences (all {Hq} q-heads, "
-                          f"{T} tokens each): fp64 oracle attention plus quantization of the appended token, "
-                          f"{spent:.1f} s, scaled to the batch",
-                "us_per_step": round(full_s * 1e6, 1)}
+                "sample": f"{done} {what}, {spent:.1f} s on {threads} threads",
+                "us_per_step": round(full_s * 1e6, 1),
+                "cpu_model": model, "cpus_available": affinity,
+                "one_thread": {"value": round(self.step_bytes / full1 / 1e9, 4), "unit": "GB/s",
+                               "us_per_step": round(full1 * 1e6, 1),
+                               "sample": f"{done1} {what}, {spent1:.1f} s on 1 thread"}}
 
 
 def read_stream_peak(dev):
@@ -343,22 +405,29 @@ def read_stream_peak(dev):
 def measure(name, args, dev, with_bf16, with_cpu):
     import torch
     wk = Workload(name, dev, keep_bf16=with_bf16)
-    four_ms, dec_ms, dec_med = wk.time_steps(args.steps, args.warmup)
+    wk.decode_path = args.decode_path
+    four_runs, dec = wk.time_steps(args.steps, args.warmup)
     # The product step is decode_step; a measurement override of the decode
     # kernel applies to the four separate calls only, so it times those.
-    step_ms = four_ms if args.decode_path else wk.time_fused_steps(args.steps, args.warmup)
+    step_runs = four_runs if args.decode_path else wk.time_fused_steps(args.steps, args.warmup)
+    step_ms, four_ms = pct(step_runs, 0.5), pct(four_runs, 0.5)
+    dec_ms = sum(dec) / len(dec)
     attn_ms = wk.time_attention_only(args.steps, args.warmup)
     res = {
         "workload": name,
         "us_per_step": round(step_ms * 1e3, 2),
+        "us_per_step_p10": round(pct(step_runs, 0.1) * 1e3, 2),
+        "us_per_step_p90": round(pct(step_runs, 0.9) * 1e3, 2),
+        "us_per_step_runs": [round(x * 1e3, 2) for x in step_runs],
         "us_per_step_four_calls": round(four_ms * 1e3, 2),
         "step_call": "four calls" if args.decode_path else "decode_step",
         "GBps": round(wk.step_bytes / (step_ms * 1e-3) / 1e9, 1),
         "pct_hbm_peak": round(100 * wk.step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
         "decode_us": round(dec_ms * 1e3, 2),
-        "decode_us_median": round(dec_med * 1e3, 2),
-        "decode_us_p10": round(wk.decode_p10 * 1e3, 2),
-        "decode_us_p90": round(wk.decode_p90 * 1e3, 2),
+        "decode_us_median": round(pct(dec, 0.5) * 1e3, 2),
+        "decode_us_p10": round(pct(dec, 0.1) * 1e3, 2),
+        "decode_us_p90": round(pct(dec, 0.9) * 1e3, 2),
+        "decode_launches": len(dec),
         "decode_GBps": round(wk.decode_bytes / (dec_ms * 1e-3) / 1e9, 1),
         "attention_us": round(attn_ms * 1e3, 2),
         "num_splits": wk.S,
@@ -389,8 +458,6 @@ def main():
               "has no multi-GPU mode; shard by KV head or context across GPUs as described in the design notes.",
               file=sys.stderr)
         sys.exit(2)
-    if args.decode_path:
-        os.environ["VQKV_DECODE_PATH"] = args.decode_path
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -108,8 +108,9 @@ typedef struct {
 
 /* ------------------------------------------------------------- size queries */
 
-/* Bytes per token per KV head for one of K or V: 32 (2-bit) or 24 (1.5-bit);
- * 0 for an unknown format.  VecInfer card, "Key points" (codebook size). */
+/* Bytes per token per KV head for one of K or V: 32 (2-bit), 24 (1.5-bit) or
+ * 48 (3-bit), with or without VQKV_FMT_VALUE_TRANSFORM; 0 for an unknown
+ * format.  VecInfer card, "Key points" (codebook size). */
 size_t vqkv_code_bytes_per_token(int32_t fmt);
 
 /* Bytes of one code cache (keys or values): B * Hkv * max_tokens * W.
@@ -125,8 +126,10 @@ size_t vqkv_workspace_bytes(const vqkv_shape* shape, int32_t num_splits);
  * per sequence); 0 if the arguments are invalid. */
 size_t vqkv_step_workspace_bytes(const vqkv_shape* shape, int32_t num_splits);
 
-/* A split count that fills the GPU for this shape and context length
- * (>= 1).  Any value in [1, ceil(seq_len / 64)] is valid for the decode. */
+/* A split count that fills the GPU for this shape and context length (>= 1):
+ * about one work-group per compute unit of the current device (256 when no
+ * device answers), at least 1024 tokens per split.  Any value in
+ * [1, ceil(seq_len / 64)] is valid for the decode. */
 int32_t vqkv_suggest_splits(const vqkv_shape* shape, int32_t seq_len);
 
 /* Static text for a status code. */
@@ -251,8 +254,14 @@ vqkv_status vqkv_quantize_append_paged(const vqkv_shape* shape, const void* k_ne
                                        uint8_t* v_pool, int32_t num_blocks, const int32_t* block_table,
                                        void* stream);
 
-/* Log-sum-exp merge of the splits (split-context flash decoding):
- * out[b][g] = sum_i exp(lse_i - L) o_i, L = log sum_i exp(lse_i).
+/* Log-sum-exp merge of the splits.  VecInfer card, "Summary": the attention
+ * kernel tiles the context; its "References" name the decoding scheme this
+ * finishes, a context cut into independent splits whose partial softmax
+ * results are merged afterwards (FlashDecoding++, reference 15), with the
+ * online normalizer of reference 26.  Split i contributes (o_i, lse_i), its
+ * normalized output and the log-sum-exp of its scores:
+ * out[b][g] = sum_i exp(lse_i - L) o_i, L = log sum_i exp(lse_i); a split
+ * with no token (lse_i = -inf) weighs 0, and a row with no token gives 0.
  *   workspace   device, as written by vqkv_decode_attention with the same
  *               shape and num_splits
  *   out         device, fp32 [B][Hq][128] (output; with VQKV_FMT_VALUE_TRANSFORM
@@ -306,6 +315,8 @@ vqkv_status vqkv_decode_step(const vqkv_shape* shape, const void* q, const void*
  * launch runs first).
  *   positions     device, int32 [B], 4-byte aligned
  *   max_seq_len   host, 1 <= max_seq_len <= max_tokens, >= every positions[b] + 1
+ *                 (a position past the last split's tokens is still appended,
+ *                 but no split attends to it, as with the separate calls)
  *   num_splits    host, 1 <= num_splits <= ceil(max_seq_len / 64)
  *   other arguments as for vqkv_decode_step. */
 vqkv_status vqkv_decode_step_varlen(const vqkv_shape* shape, const void* q, const void* k_new,

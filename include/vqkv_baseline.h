@@ -44,6 +44,25 @@ vqkv_status vqkv_baseline_bf16_decode(const vqkv_shape* shape, const void* q, co
 vqkv_status vqkv_baseline_read_stream(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
                                       void* stream);
 
+/* vqkv_decode_attention on a kernel chosen for measurement instead of the
+ * default one, so that the design choices stay measurable side by side:
+ *   path 0  the default (the matrix-core kernel, every format)
+ *   path 1  the score-lookup-table kernel (2-bit, Hq / Hkv <= 4): per
+ *           work-group table of q'-by-centroid scores in LDS
+ *   path 2  the gather kernel (2-bit and 1.5-bit): centroids gathered from
+ *           the LDS codebooks, fp32 score products
+ *   path 3  the matrix-core kernel, named explicitly
+ * Same arguments, results (within the tolerance of each kernel's arithmetic)
+ * and workspace format as vqkv_decode_attention; errors as in vqkv.h, with
+ * the text from vqkv_last_error().  A path outside [0, 3] returns
+ * VQKV_ERR_INVALID_ARG, a path that does not take the shape's format or
+ * group size VQKV_ERR_UNSUPPORTED. */
+vqkv_status vqkv_measure_decode_attention(const vqkv_shape* shape, const float* q_prime,
+                                          const uint16_t* k_book, const uint16_t* v_book,
+                                          const uint8_t* k_codes, const uint8_t* v_codes,
+                                          int32_t seq_len, float sm_scale, int32_t num_splits,
+                                          void* workspace, int32_t path, void* stream);
+
 /* Message for the last failed baseline call on the calling thread. */
 const char* vqkv_baseline_last_error(void);
 

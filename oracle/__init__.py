@@ -77,7 +77,20 @@ def lib():
 
 
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Threads for the oracle's parallel loops: the CPUs this process may run
+    on, capped by a cgroup CPU quota and by OMP_NUM_THREADS when they are set."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, -(-int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
 
 def _p(a: np.ndarray):

@@ -6,8 +6,11 @@
 
 int g_launches = 0;
 
-// The C-ABI layer only asks the runtime for error text.
+// The C-ABI layer asks the runtime for error text and, for the split count it
+// suggests, the current device's compute units (none here: it falls back).
 const char* hipGetErrorString(hipError_t) { return "stubbed HIP runtime"; }
+hipError_t hipGetDevice(int*) { return hipErrorNoDevice; }
+hipError_t hipDeviceGetAttribute(int*, hipDeviceAttribute_t, int) { return hipErrorNoDevice; }
 
 namespace vqkv {
 hipError_t launch_transform_query(const TransformQueryArgs&, hipStream_t) { ++g_launches; return hipSuccess; }

@@ -98,6 +98,21 @@ def test_decode_argument_checks():
     assert call(100, 0.088, 1, q=None) == INVALID
 
 
+def test_measurement_decode_path_checks():
+    """The measurement entry point names its kernel explicitly: unknown paths and
+    paths that do not take the format or group size are refused on the host."""
+    L = vq.lib()
+
+    def call(fmt, hq, path):
+        sh = ctypes.byref(vq.make_shape(1, hq, 8, 1024, fmt))
+        return L.vqkv_measure_decode_attention(sh, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 0.088, 1, FAKE, path, None)
+    assert call(vq.FMT_2BIT, 32, -1) == INVALID
+    assert call(vq.FMT_2BIT, 32, 4) == INVALID
+    assert call(vq.FMT_2BIT, 40, 1) == UNSUPPORTED          # score table holds four heads
+    assert call(vq.FMT_1P5BIT, 32, 1) == UNSUPPORTED        # score table: 2-bit only
+    assert call(vq.FMT_3BIT, 32, 2) == UNSUPPORTED          # gather: 2-bit and 1.5-bit
+
+
 def test_append_argument_checks():
     L = vq.lib()
     sh = ctypes.byref(vq.make_shape(2, 8, 2, 128, vq.FMT_1P5BIT))

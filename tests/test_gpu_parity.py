@@ -49,21 +49,39 @@ def rel_err(got, ref):
 def run_decode(shape, q_prime, kb, vb, kc, vc, T, S, path=None):
     ws = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
     out = torch.empty((shape.batch, shape.num_q_heads, D), dtype=torch.float32, device=DEV)
-    old = os.environ.get("VQKV_DECODE_PATH")
-    try:
-        if path:
-            os.environ["VQKV_DECODE_PATH"] = path
-        else:
-            os.environ.pop("VQKV_DECODE_PATH", None)
+    if path:
+        vq.measure_decode_attention(shape, q_prime, kb, vb, kc, vc, T, S, ws, path)
+    else:
         vq.decode_attention(shape, q_prime, kb, vb, kc, vc, T, S, ws)
-    finally:
-        if old is None:
-            os.environ.pop("VQKV_DECODE_PATH", None)
-        else:
-            os.environ["VQKV_DECODE_PATH"] = old
     vq.combine(shape, S, ws, out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+
+def _oracle_step_codes(fmt, kc, vc, pos, k_new, v_new, s, kb, vb, sv=None):
+    """The oracle's codes of each sequence's appended token (k_new, v_new
+    [B][Hkv][1][128] device tensors, the drawn inputs), written into the
+    oracle-side code arrays kc, vc [B][Hkv][T][J] at position pos[b]; a
+    position outside [0, T) is skipped."""
+    kn, vn = k_new.float().cpu().numpy(), v_new.float().cpu().numpy()
+    for b, p in enumerate(pos):
+        if p < 0 or p >= kc.shape[2]:
+            continue
+        for h in range(kn.shape[1]):
+            a, c = oracle.quantize(fmt, kn[b, h], vn[b, h], s[h], kb[h], vb[h], sv=None if sv is None else sv[h])
+            kc[b, h, p], vc[b, h, p] = a[0], c[0]
+
+
+def _assert_cache_codes(fmt, gk, gv, kc, vc, lens):
+    """The cache bytes gk, gv [B][Hkv][cap * W] (host) hold the oracle's codes
+    kc, vc for tokens [0, lens[b]) of every sequence."""
+    for b, T in enumerate(lens):
+        for h in range(kc.shape[1]):
+            if T <= 0:
+                continue
+            assert np.array_equal(oracle.unpack_k(fmt, gk[b, h], T), kc[b, h, :T]), f"key codes b={b} h={h}"
+            assert np.array_equal(oracle.unpack_v(fmt, gv[b, h], T), vc[b, h, :T]), f"value codes b={b} h={h}"
 
 
 # ------------------------------------------------------------------ query transform
@@ -310,12 +328,13 @@ def test_value_transform_step_equals_the_calls(fmt, S, paged):
                        for b in range(B)])
         gv = np.stack([np.stack([np.concatenate([gv[table[b, h, i]] for i in range(nb)]) for h in range(Hkv)])
                        for b in range(B)])
+    # The oracle codes the appended tokens itself; the cache must hold its codes.
+    _oracle_step_codes(fmt, kc, vc, pos, k_new, v_new, s, kb, vb, sv)
+    _assert_cache_codes(fmt, gk, gv, kc, vc, [p + 1 for p in pos])
     qf = qd.float().cpu().numpy()
     for b, p in enumerate(pos):
         T = p + 1
-        kcb = np.stack([oracle.unpack_k(fmt, gk[b, h], T) for h in range(Hkv)])[None]
-        vcb = np.stack([oracle.unpack_v(fmt, gv[b, h], T) for h in range(Hkv)])[None]
-        ref = oracle.attention(fmt, qf[b:b + 1], s, kb, vb, kcb, vcb, sv=sv)
+        ref = oracle.attention(fmt, qf[b:b + 1], s, kb, vb, kc[b:b + 1, :, :T], vc[b:b + 1, :, :T], sv=sv)
         err = rel_err(g[b:b + 1], ref)
         print(f"  b={b} T={T} max relative error {err:.3e}", flush=True)
         assert err <= TOL
@@ -783,13 +802,12 @@ def test_decode_step_equals_the_four_calls(fmt, B, Hq, Hkv, pos, S, dtype):
         g, w = got.cpu().numpy(), want.cpu().numpy()
         assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), f"position {p}: max diff {np.abs(g - w).max()}"
         assert torch.equal(got_k, ref_k) and torch.equal(got_v, ref_v)
-    # The oracle on the codes the cache holds after the second step.
+        _oracle_step_codes(fmt, kc, vc, [p] * B, k_new, v_new, s, kb, vb)
+    # The cache after the second step holds the oracle's codes; the oracle's
+    # attention over them.
     T = pos + 2
-    kc_all = np.stack([np.stack([oracle.unpack_k(fmt, got_k[b, h].cpu().numpy(), T) for h in range(Hkv)])
-                       for b in range(B)])
-    vc_all = np.stack([np.stack([oracle.unpack_v(fmt, got_v[b, h].cpu().numpy(), T) for h in range(Hkv)])
-                       for b in range(B)])
-    ref = oracle.attention(fmt, qd.float().cpu().numpy(), s, kb, vb, kc_all, vc_all)
+    _assert_cache_codes(fmt, got_k.cpu().numpy(), got_v.cpu().numpy(), kc, vc, [T] * B)
+    ref = oracle.attention(fmt, qd.float().cpu().numpy(), s, kb, vb, kc, vc)
     err = rel_err(got.cpu().numpy(), ref)
     print(f"  max relative error {err:.3e}", flush=True)
     assert err <= TOL
@@ -1009,7 +1027,9 @@ def test_decode_step_ragged_equals_the_four_calls(fmt, Hq, Hkv, S, paged):
         assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), f"step {step}: max diff {np.abs(g - w).max()}"
         assert torch.equal(got_k, ref_k) and torch.equal(got_v, ref_v)
         assert np.all(g[3] == 0.0)
-    # The oracle per sequence on the codes the cache holds after the second step.
+        _oracle_step_codes(fmt, kc, vc, pos, k_new, v_new, s, kb, vb)
+    # The cache after the second step holds the oracle's codes; the oracle's
+    # attention per sequence over them.
     gk, gv = got_k.cpu().numpy(), got_v.cpu().numpy()
     if paged:
         nb = cap // 64
@@ -1017,17 +1037,55 @@ def test_decode_step_ragged_equals_the_four_calls(fmt, Hq, Hkv, S, paged):
                        for b in range(B)])
         gv = np.stack([np.stack([np.concatenate([gv[table[b, h, i]] for i in range(nb)]) for h in range(Hkv)])
                        for b in range(B)])
+    _assert_cache_codes(fmt, gk, gv, kc, vc, [p + 1 for p in pos])
     qf = qd.float().cpu().numpy()
     for b, p in enumerate(pos):
         if p < 0:
             continue
         T = p + 1
-        kcb = np.stack([oracle.unpack_k(fmt, gk[b, h], T) for h in range(Hkv)])[None]
-        vcb = np.stack([oracle.unpack_v(fmt, gv[b, h], T) for h in range(Hkv)])[None]
-        ref = oracle.attention(fmt, qf[b:b + 1], s, kb, vb, kcb, vcb)
+        ref = oracle.attention(fmt, qf[b:b + 1], s, kb, vb, kc[b:b + 1, :, :T], vc[b:b + 1, :, :T])
         err = rel_err(g[b:b + 1], ref)
         print(f"  b={b} T={T} max relative error {err:.3e}", flush=True)
         assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt,S", [(0, 1), (0, 3), (1, 3)])
+def test_decode_step_varlen_appends_past_max_seq_len(fmt, S):
+    """A ragged step whose max_seq_len is below positions[b] + 1: the token is
+    still appended (by the last split's work-group in the one-launch 2-bit
+    step) and no split attends to it, exactly as the separate calls do; the
+    cache then holds the oracle's codes for it."""
+    say(f"decode_step_varlen with a position past max_seq_len, fmt{fmt} S{S}")
+    B, Hq, Hkv = 2, 8, 2
+    pos, mx = [100, 3000], 1000
+    cap = 3072
+    q, s, kb, vb, kc, vc, _ = _attn_inputs(fmt, B, Hq, Hkv, cap, 8100 + S + fmt, cap)
+    shape = vq.make_shape(B, Hq, Hkv, cap, fmt)
+    kbytes, vbytes = oracle.pack_stream(fmt, kc, vc, cap)
+    ref_k, ref_v, got_k, got_v = dev(kbytes), dev(vbytes), dev(kbytes), dev(vbytes)
+    rng = np.random.default_rng(31 + S)
+    books, sm = (book_dev(kb), book_dev(vb)), dev(s)
+    qd = dev(rng.standard_normal((B, Hq, D)).astype(np.float32), torch.bfloat16)
+    k_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), torch.bfloat16)
+    v_new = dev(rng.standard_normal((B, Hkv, 1, D)).astype(np.float32), torch.bfloat16)
+    pos_d = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    lens_d = torch.tensor([p + 1 for p in pos], dtype=torch.int32, device=DEV)
+    qp = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    ws_ref = torch.empty(vq.workspace_bytes(shape, S), dtype=torch.uint8, device=DEV)
+    ws = torch.full((vq.step_workspace_bytes(shape, S),), 0xFF, dtype=torch.uint8, device=DEV)
+    want = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    got = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+    vq.quantize_append_varlen(shape, k_new, v_new, pos_d, sm, books[0], books[1], ref_k, ref_v)
+    vq.transform_query(shape, qd, sm, qp)
+    vq.decode_attention_varlen(shape, qp, books[0], books[1], ref_k, ref_v, lens_d, mx, S, ws_ref)
+    vq.combine(shape, S, ws_ref, want)
+    vq.decode_step_varlen(shape, qd, k_new, v_new, pos_d, mx, sm, books[0], books[1], got_k, got_v, S, ws, got)
+    torch.cuda.synchronize()
+    g, w = got.cpu().numpy(), want.cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), f"max diff {np.abs(g - w).max()}"
+    assert torch.equal(got_k, ref_k) and torch.equal(got_v, ref_v)
+    _oracle_step_codes(fmt, kc, vc, pos, k_new, v_new, s, kb, vb)
+    _assert_cache_codes(fmt, got_k.cpu().numpy(), got_v.cpu().numpy(), kc, vc, [p + 1 for p in pos])
 
 
 @pytest.mark.parametrize("fmt,S", [(0, 3), (1, 4), (0, 1), (2, 2)])

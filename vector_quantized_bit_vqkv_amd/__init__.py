@@ -28,8 +28,10 @@ FMT_VALUE_TRANSFORM = 0x100      # OR'ed into a format: values smoothed and rota
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 HEAD_DIM = 128
-ENTRIES = {FMT_2BIT: 256, FMT_1P5BIT: 4096}
-DSUB = {FMT_2BIT: 4, FMT_1P5BIT: 8}
+ENTRIES = {FMT_2BIT: 256, FMT_1P5BIT: 4096, FMT_3BIT: 4096}
+DSUB = {FMT_2BIT: 4, FMT_1P5BIT: 8, FMT_3BIT: 4}
+# Kernels selectable for measurement (measure_decode_attention).
+DECODE_PATHS = {"default": 0, "table": 1, "gather": 2, "mfma": 3}
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP runtime error"}
 
@@ -86,6 +88,7 @@ def lib() -> ctypes.CDLL:
         "vqkv_smooth_scales": (I32, [I32, I32, P, I32, P, P]),
         "vqkv_train_workspace_bytes": (SZ, [I32, I32]),
         "vqkv_train_codebook": (I32, [I32, I32, P, I32, I32, P, P, I32, P, P, P, P]),
+        "vqkv_measure_decode_attention": (I32, [SP, P, P, P, P, P, I32, F32, I32, P, I32, P]),
         "vqkv_baseline_bf16_decode": (I32, [SP, P, P, P, I32, F32, I32, P, P]),
         "vqkv_baseline_read_stream": (I32, [P, SZ, P, I32, P]),
         "vqkv_baseline_last_error": (ctypes.c_char_p, []),
@@ -175,6 +178,18 @@ def decode_attention(shape: Shape, q_prime, k_book, v_book, k_codes, v_codes, se
     _check(lib().vqkv_decode_attention(ctypes.byref(shape), _ptr(q_prime), _ptr(k_book), _ptr(v_book),
                                        _ptr(k_codes), _ptr(v_codes), seq_len, sm_scale, num_splits,
                                        _ptr(workspace), _stream(q_prime)))
+
+
+def measure_decode_attention(shape: Shape, q_prime, k_book, v_book, k_codes, v_codes, seq_len: int,
+                             num_splits: int, workspace, path: str, sm_scale: float | None = None) -> None:
+    """decode_attention on a kernel chosen for measurement: 'default', 'table', 'gather' or 'mfma'."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if path not in DECODE_PATHS:
+        raise ValueError(f"unknown decode path {path!r}")
+    _check(lib().vqkv_measure_decode_attention(ctypes.byref(shape), _ptr(q_prime), _ptr(k_book), _ptr(v_book),
+                                               _ptr(k_codes), _ptr(v_codes), seq_len, sm_scale, num_splits,
+                                               _ptr(workspace), DECODE_PATHS[path], _stream(q_prime)))
 
 
 def decode_attention_varlen(shape: Shape, q_prime, k_book, v_book, k_codes, v_codes, seq_lens, max_seq_len: int,

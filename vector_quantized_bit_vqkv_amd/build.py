@@ -42,14 +42,19 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+
+    def compile_one(src):
         path = os.path.join(CSRC, src)
         obj = os.path.join(BUILD, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), *lang, "-c", path, "-o", obj]
-        out = _run(cmd)
+        return obj, _run([HIPCC, *COMMON, *PER_FILE.get(src, []), *lang, "-c", path, "-o", obj])
+    # The sources compile independently (a few at a time: each hipcc is one process).
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), max(1, (os.cpu_count() or 1) // 2))) as pool:
+        results = list(pool.map(compile_one, SOURCES))
+    objs = []
+    for obj, out in results:
         if verbose and out:
             print(out)
         objs.append(obj)

@@ -6,10 +6,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
-#include <cstring>
 
 #include "../../include/vqkv.h"
+#include "../../include/vqkv_baseline.h"
 #include "internal.h"
 
 namespace {
@@ -98,15 +97,15 @@ int split_chunk(int seq_len, int splits) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Decode path override for measurement: VQKV_DECODE_PATH = "table" | "gather" | "mfma".
-int decode_path_from_env() {
-    const char* v = getenv("VQKV_DECODE_PATH");
-    if (!v || !*v) return 0;
-    if (!strcmp(v, "table")) return 1;
-    if (!strcmp(v, "gather")) return 2;
-    if (!strcmp(v, "mfma")) return 3;
-    return 0;
+// Compute units of the current device (the decode kernels keep one
+// work-group per CU); 256, an MI355X's count, when no device answers.
+int compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+    return n;
 }
+
 
 }  // namespace
 
@@ -142,7 +141,7 @@ size_t vqkv_step_workspace_bytes(const vqkv_shape* s, int32_t num_splits) {
 int32_t vqkv_suggest_splits(const vqkv_shape* s, int32_t seq_len) {
     if (check_shape(s, false) != VQKV_OK || seq_len < 1) return 1;
     const int64_t streams = (int64_t)s->batch * s->num_kv_heads;
-    const int64_t want = ceil_div(256, streams);              // one work-group per CU on 256 CUs
+    const int64_t want = ceil_div(compute_units(), streams);  // one work-group per CU
     const int64_t cap = ceil_div(seq_len, 1024);              // keep >= 1024 tokens per split
     int64_t S = want < cap ? want : cap;
     if (S < 1) S = 1;
@@ -239,10 +238,16 @@ vqkv_status vqkv_quantize_append_paged(const vqkv_shape* s, const void* k_new, c
     return hip_status(vqkv::launch_quantize_append(a, (hipStream_t)stream), "quantize_append_paged launch");
 }
 
-vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
+}  // extern "C"
+
+namespace {
+
+// vqkv_decode_attention on a chosen kernel: 0 the default (matrix cores),
+// 1 score table, 2 gather, 3 matrix cores named explicitly.
+vqkv_status decode_attention_impl(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
                                   const uint16_t* v_book, const uint8_t* k_codes, const uint8_t* v_codes,
                                   int32_t seq_len, float sm_scale, int32_t num_splits, void* workspace,
-                                  void* stream) {
+                                  int path, void* stream) {
     VQKV_CHECK(check_shape(s, true));
     if (seq_len < 1 || seq_len > s->max_tokens)
         return fail(VQKV_ERR_INVALID_ARG, "seq_len %d outside [1, max_tokens = %d]", seq_len, s->max_tokens);
@@ -259,8 +264,8 @@ vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, con
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     float* part_o = (float*)workspace;
     float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
-    const int path = decode_path_from_env();
     const int G = s->num_q_heads / s->num_kv_heads;
+    if (path < 0 || path > 3) return fail(VQKV_ERR_INVALID_ARG, "unknown decode path %d", path);
     if (path == 1 && !(base_fmt(s->fmt) == VQKV_FMT_2BIT && G <= 4))
         return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
     if (path == 2 && base_fmt(s->fmt) == VQKV_FMT_3BIT)
@@ -270,6 +275,26 @@ vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, con
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), path};
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+vqkv_status vqkv_decode_attention(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
+                                  const uint16_t* v_book, const uint8_t* k_codes, const uint8_t* v_codes,
+                                  int32_t seq_len, float sm_scale, int32_t num_splits, void* workspace,
+                                  void* stream) {
+    return decode_attention_impl(s, q_prime, k_book, v_book, k_codes, v_codes, seq_len, sm_scale, num_splits,
+                                 workspace, 0, stream);
+}
+
+vqkv_status vqkv_measure_decode_attention(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
+                                          const uint16_t* v_book, const uint8_t* k_codes, const uint8_t* v_codes,
+                                          int32_t seq_len, float sm_scale, int32_t num_splits, void* workspace,
+                                          int32_t path, void* stream) {
+    return decode_attention_impl(s, q_prime, k_book, v_book, k_codes, v_codes, seq_len, sm_scale, num_splits,
+                                 workspace, path, stream);
 }
 
 vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* s, const float* q_prime, const uint16_t* k_book,
@@ -294,16 +319,10 @@ vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* s, const float* q_pri
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     float* part_o = (float*)workspace;
     float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
-    const int path = decode_path_from_env();
-    const int G = s->num_q_heads / s->num_kv_heads;
-    if (path == 1 && !(base_fmt(s->fmt) == VQKV_FMT_2BIT && G <= 4))
-        return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
-    if (path == 2 && base_fmt(s->fmt) == VQKV_FMT_3BIT)
-        return fail(VQKV_ERR_UNSUPPORTED, "the gather path takes the 2-bit and 1.5-bit formats");
     vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
-                       (float)((double)sm_scale * 1.4426950408889634), path, seq_lens};
+                       (float)((double)sm_scale * 1.4426950408889634), 0, seq_lens};
     return hip_status(vqkv::launch_decode(a, (hipStream_t)stream), "decode_attention_varlen launch");
 }
 
@@ -330,8 +349,6 @@ vqkv_status vqkv_decode_attention_paged(const vqkv_shape* s, const float* q_prim
     VQKV_CHECK(check_ptr(k_pool, "k_pool"));
     VQKV_CHECK(check_ptr(v_pool, "v_pool"));
     VQKV_CHECK(check_ptr(workspace, "workspace"));
-    if (decode_path_from_env() != 0)
-        return fail(VQKV_ERR_UNSUPPORTED, "paged caches run on the matrix-core kernel only");
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     float* part_o = (float*)workspace;
     float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));

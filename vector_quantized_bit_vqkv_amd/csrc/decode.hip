@@ -400,10 +400,14 @@ __device__ __forceinline__ AppendFetch fused_append_fetch(const DecodeArgs& a, i
     // Position of the token: uniform, or per sequence; outside the cache it is
     // not appended (block-uniform), as in the append kernel.  With several
     // splits only the work-group whose token range holds it appends it (the
-    // others never read that tile); every work-group transforms the query.
+    // others never read that tile); every work-group transforms the query.  A
+    // position past the last split's range (a ragged step whose max_seq_len
+    // is below positions[b] + 1: no split attends to it) is appended by the
+    // last split, so the cache still receives it as the append call would.
     f.t = ap.positions ? (int64_t)scalar_read(ap.positions, b) : (int64_t)ap.start_pos;
     const int64_t t_begin = (int64_t)blockIdx.x * a.chunk;
-    f.app = f.t >= 0 && f.t < a.cap && f.t >= t_begin && f.t < t_begin + a.chunk;
+    f.app = f.t >= 0 && f.t < a.cap && f.t >= t_begin &&
+            (f.t < t_begin + a.chunk || blockIdx.x == gridDim.x - 1);
     f.qv = QueryPair{0u, 0u, 0.0f, 0.0f, ap.dtype};
     if (wave >= 4 && wave < 4 + G) {
         const int64_t vec = (int64_t)b * a.hq + h * G + (wave - 4);
