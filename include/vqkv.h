@@ -304,6 +304,30 @@ vqkv_status vqkv_decode_step(const vqkv_shape* shape, const void* q, const void*
                              const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, float sm_scale,
                              int32_t num_splits, void* workspace, float* out, void* stream);
 
+/* Bytes of the static scratch behind vqkv_decode_step_static, on each GPU. */
+#define VQKV_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* vqkv_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same computation, kernels and result bits as vqkv_decode_step (same
+ * arguments, checks and errors, minus `workspace`); the step's workspace is
+ * a static device array of VQKV_STATIC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends.  Neither the call nor the
+ * library allocates or frees memory.
+ * - A shape and split count whose vqkv_step_workspace_bytes exceeds
+ *   VQKV_STATIC_SCRATCH_BYTES return VQKV_ERR_UNSUPPORTED, with no device work
+ *   (for example batch 32 x 32 query heads fits up to 14 splits).
+ * - Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents; the step needs none of them (its arrival counters are
+ *   cleared by its own append launch, as with a caller's workspace).
+ * - Calls that overlap in time on one GPU (other streams, other threads)
+ *   race on the array: the caller must serialize them. */
+vqkv_status vqkv_decode_step_static(const vqkv_shape* shape, const void* q, const void* k_new,
+                                    const void* v_new, int32_t dtype, int32_t position, const float* smooth,
+                                    const uint16_t* k_book, const uint16_t* v_book, uint8_t* k_codes,
+                                    uint8_t* v_codes, float sm_scale, int32_t num_splits, float* out,
+                                    void* stream);
+
 /* The fused step for ragged batches: sequence b's new token lands at
  * positions[b] and its queries attend to tokens [0, positions[b]].  The result
  * is bit-identical to vqkv_quantize_append_varlen(positions),

@@ -39,9 +39,10 @@ int main() {
         CHECK(vqkv_decode_step(&s, F, F, F, 0, 4098, Ff, Fb, Fb, Fc, Fc, 0.088f, 9, F, Ff, nullptr) == VQKV_OK);
         CHECK(vqkv_decode_step_varlen(&s, F, F, F, 0, Fi, 4099, Ff, Fb, Fb, Fc, Fc, 0.088f, 9, F, Ff, nullptr) == VQKV_OK);
         CHECK(vqkv_decode_step_paged(&s, F, F, F, 0, Fi, 4099, Ff, Fb, Fb, Fc, Fc, 7, Fi, 0.088f, 9, F, Ff, nullptr) == VQKV_OK);
+        CHECK(vqkv_decode_step_static(&s, F, F, F, 0, 4098, Ff, Fb, Fb, Fc, Fc, 0.088f, 1, Ff, nullptr) == VQKV_OK);
         const int vt = (fmt & VQKV_FMT_VALUE_TRANSFORM) != 0;
         CHECK(vqkv_value_output_transform(&s, Ff, Ff, nullptr) == (vt ? VQKV_OK : VQKV_ERR_INVALID_ARG));
-        CHECK(g_launches - before == 8 + 2 * 3 + vt);
+        CHECK(g_launches - before == 8 + 2 * 3 + (fmt == VQKV_FMT_2BIT ? 1 : 2) + vt);
     }
     // Rejections: no launch may happen.
     const int before = g_launches;
@@ -70,6 +71,11 @@ int main() {
     CHECK(vqkv_decode_step_paged(&good, F, F, F, 0, Fi, 100, Ff, Fb, Fb, Fc, Fc, 0, Fi, 0.088f, 1, F, Ff, nullptr) == VQKV_ERR_INVALID_ARG);
     CHECK(vqkv_decode_step_varlen(&good, F, F, F, 0, nullptr, 100, Ff, Fb, Fb, Fc, Fc, 0.088f, 1, F, Ff, nullptr) == VQKV_ERR_INVALID_ARG);
     CHECK(vqkv_combine(&good, 0, F, Ff, nullptr) == VQKV_ERR_INVALID_ARG);
+    // The allocation-free step: a workspace beyond the static scratch is refused.
+    CHECK(vqkv_step_workspace_bytes(&good, 64) > VQKV_STATIC_SCRATCH_BYTES);
+    CHECK(vqkv_decode_step_static(&good, F, F, F, 0, 196607, Ff, Fb, Fb, Fc, Fc, 0.088f, 64, Ff, nullptr) == VQKV_ERR_UNSUPPORTED);
+    CHECK(vqkv_decode_step_static(&good, F, F, F, 0, 196607, Ff, Fb, Fb, Fc, Fc, 0.088f, 0, Ff, nullptr) == VQKV_ERR_INVALID_ARG);
+    CHECK(vqkv_decode_step_static(&good, F, F, F, 0, -1, Ff, Fb, Fb, Fc, Fc, 0.088f, 1, Ff, nullptr) == VQKV_ERR_INVALID_ARG);
     CHECK(vqkv_train_codebook(1, 255, F, 0, 0, nullptr, static_cast<const int64_t*>(F), 20, static_cast<uint16_t*>(F), nullptr, F, nullptr) == VQKV_ERR_INVALID_ARG);
     CHECK(vqkv_smooth_scales(0, 10, F, 0, Ff, nullptr) == VQKV_ERR_INVALID_ARG);
     CHECK(g_launches == before);

@@ -20,4 +20,10 @@ hipError_t launch_combine(const CombineArgs&, hipStream_t) { ++g_launches; retur
 hipError_t launch_value_output_transform(const ValueOutputArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_smooth_scales(int, int, const void*, int, float*, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_train_codebook(const TrainArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
+// The static scratch's address: an aligned dummy (nothing dereferences it).
+hipError_t static_scratch(void** addr, int* device) {
+    *addr = reinterpret_cast<void*>(0x20000);
+    if (device) *device = 0;
+    return hipSuccess;
+}
 }  // namespace vqkv

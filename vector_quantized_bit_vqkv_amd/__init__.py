@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
         "vqkv_step_workspace_bytes": (SZ, [SP, I32]),
         "vqkv_value_output_transform": (I32, [SP, P, P, P]),
         "vqkv_decode_step": (I32, [SP, P, P, P, I32, I32, P, P, P, P, P, F32, I32, P, P, P]),
+        "vqkv_decode_step_static": (I32, [SP, P, P, P, I32, I32, P, P, P, P, P, F32, I32, P, P]),
         "vqkv_decode_step_varlen": (I32, [SP, P, P, P, I32, P, I32, P, P, P, P, P, F32, I32, P, P, P]),
         "vqkv_decode_step_paged": (I32, [SP, P, P, P, I32, P, I32, P, P, P, P, P, I32, P, F32, I32, P, P, P]),
         "vqkv_decode_attention_varlen": (I32, [SP, P, P, P, P, P, P, I32, F32, I32, P, P]),
@@ -270,6 +271,22 @@ def decode_step(shape: Shape, q, k_new, v_new, position: int, smooth, k_book, v_
     _check(lib().vqkv_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
                                   position, _ptr(smooth), _ptr(k_book), _ptr(v_book), _ptr(k_codes),
                                   _ptr(v_codes), sm_scale, num_splits, _ptr(workspace), _ptr(out), _stream(q)))
+
+
+# Bytes of the static device workspace behind decode_step_static, on each GPU.
+STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def decode_step_static(shape: Shape, q, k_new, v_new, position: int, smooth, k_book, v_book, k_codes, v_codes,
+                       num_splits: int, out, sm_scale: float | None = None) -> None:
+    """decode_step without a workspace argument: the library's static per-GPU scratch serves as
+    the workspace, so nothing is allocated (calls overlapping on one GPU race on it)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    _step_inputs(q, k_new, v_new)
+    _check(lib().vqkv_decode_step_static(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                         position, _ptr(smooth), _ptr(k_book), _ptr(v_book), _ptr(k_codes),
+                                         _ptr(v_codes), sm_scale, num_splits, _ptr(out), _stream(q)))
 
 
 def torch_int32():

@@ -28,7 +28,7 @@ COMMON = [
 # Files whose floating point decides integers (codes, K-Means assignments):
 # no fused multiply-add anywhere.
 PER_FILE = {"quantize.hip": ["-ffp-contract=off"]}
-SOURCES = ["capi.cpp", "transform_query.hip", "quantize.hip", "decode.hip", "baseline.hip"]
+SOURCES = ["capi.cpp", "transform_query.hip", "quantize.hip", "decode.hip", "baseline.hip", "static_scratch.hip"]
 
 
 def _run(cmd):

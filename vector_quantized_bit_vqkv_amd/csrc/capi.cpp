@@ -467,6 +467,23 @@ vqkv_status vqkv_decode_step(const vqkv_shape* s, const void* q, const void* k_n
                             v_codes, 0, nullptr, sm_scale, num_splits, workspace, out, stream, "decode_step");
 }
 
+vqkv_status vqkv_decode_step_static(const vqkv_shape* s, const void* q, const void* k_new, const void* v_new,
+                                    int32_t dtype, int32_t position, const float* smooth, const uint16_t* k_book,
+                                    const uint16_t* v_book, uint8_t* k_codes, uint8_t* v_codes, float sm_scale,
+                                    int32_t num_splits, float* out, void* stream) {
+    static_assert(VQKV_STATIC_SCRATCH_BYTES == vqkv::kStaticScratchBytes, "one size in the header and the library");
+    VQKV_CHECK(check_shape(s, true));
+    if (num_splits < 1) return fail(VQKV_ERR_INVALID_ARG, "num_splits %d < 1", num_splits);
+    const size_t need = vqkv_step_workspace_bytes(s, num_splits);
+    if (need > vqkv::kStaticScratchBytes)
+        return fail(VQKV_ERR_UNSUPPORTED, "the step needs %zu bytes of workspace, more than the %zu bytes of the "
+                    "static scratch (use vqkv_decode_step with a workspace)", need, vqkv::kStaticScratchBytes);
+    void* ws = nullptr;
+    VQKV_CHECK(hip_status(vqkv::static_scratch(&ws, nullptr), "static scratch address"));
+    return decode_step_impl(s, q, k_new, v_new, dtype, position, nullptr, 0, smooth, k_book, v_book, k_codes,
+                            v_codes, 0, nullptr, sm_scale, num_splits, ws, out, stream, "decode_step_static");
+}
+
 vqkv_status vqkv_decode_step_varlen(const vqkv_shape* s, const void* q, const void* k_new, const void* v_new,
                                     int32_t dtype, const int32_t* positions, int32_t max_seq_len,
                                     const float* smooth, const uint16_t* k_book, const uint16_t* v_book,

@@ -124,6 +124,13 @@ struct ValueOutputArgs {
 };
 hipError_t launch_value_output_transform(const ValueOutputArgs& a, hipStream_t stream);
 
+// Workspace of the allocation-free decode step: a file-scope device array of
+// kStaticScratchBytes (static_scratch.hip), one copy per GPU.  Returns the
+// current device's copy's address (taken once per device with
+// hipGetSymbolAddress, then kept) and, if `device` is not null, the device.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+hipError_t static_scratch(void** addr, int* device);
+
 // Offline calibration.
 hipError_t launch_smooth_scales(int hkv, int n_cal, const void* k_cal, int dtype, float* smooth,
                                 hipStream_t stream);
