@@ -21,8 +21,9 @@
  *     so q'.k' == q.k ([card] Summary; [abstract]);
  *   - nearest-centroid codes under squared L2 over contiguous sub-vectors,
  *     ties to the lowest index, with codebooks of 2^8 x 4 (2-bit) or
- *     2^12 x 8 (1.5-bit) fp16 entries ([card] Key points, codebook size), and
- *     a third width inside the pages' 1.25-4 bit range, 2^12 x 4 (3-bit);
+ *     2^12 x 8 (1.5-bit) fp16 entries ([card] Key points, codebook size),
+ *     and two more widths inside the pages' 1.25-4 bit range ([card] Summary):
+ *     2^12 x 4 (3-bit) and 2^10 x 8 (1.25-bit);
  *   - offline K-Means (Lloyd) codebooks ([card] Summary, "trained offline");
  *   - exact softmax attention over the dequantized cache, one query head at a
  *     time (the definition the fused kernel must reproduce; [abstract]).
@@ -68,11 +69,16 @@ int vqo_format(int fmt, int* entries, int* dsub)
      * span it; the shape is not printed): 2^12 entries x 4 dims, 3 bits per
      * element. */
     if (fmt == 2) { *entries = 4096; *dsub = 4; return 0; }
+    /* The low end of that range, 1.25 bits per element ([card] Summary: the
+     * results start at 1.25 bits; the shape is not printed): the 1.5-bit
+     * setting's 8-dim sub-vectors with 2^10 entries, 10-bit codes. */
+    if (fmt == 3) { *entries = 1024; *dsub = 8; return 0; }
     return -1;
 }
 
-/* Bytes of one token's codes per (b, KV head): 32 (2-bit), 24 (1.5-bit), 48 (3-bit). */
-static int code_bytes(int fmt) { return fmt == 0 ? 32 : (fmt == 1 ? 24 : 48); }
+/* Bytes of one token's codes per (b, KV head): 32 (2-bit), 24 (1.5-bit),
+ * 48 (3-bit), 20 (1.25-bit). */
+static int code_bytes(int fmt) { return fmt == 0 ? 32 : (fmt == 1 ? 24 : (fmt == 2 ? 48 : 20)); }
 
 /* ------------------------------------------------------------------ fp16 */
 
@@ -388,8 +394,9 @@ int vqo_attention_fp(int B, int Hq, int Hkv, int64_t T, const double* q, const d
 /* The library's code layout for one (batch, KV head) stream of capacity
  * `cap` tokens (a multiple of 64), restated from its header:
  *
- * Keys, token-major: token t occupies bytes [t*W, (t+1)*W), W = 32 (2-bit) or
- * 24 (1.5-bit).  2-bit: byte j = code of sub-vector j.  1.5-bit: sub-vectors
+ * Keys, token-major: token t occupies bytes [t*W, (t+1)*W), W = 32 (2-bit),
+ * 24 (1.5-bit), 48 (3-bit) or 20 (1.25-bit: 10-bit codes as bit fields, see
+ * put_bits below).  2-bit: byte j = code of sub-vector j.  1.5-bit: sub-vectors
  * (2i, 2i+1) share bytes 3i..3i+2 as b0 = c0 & 0xFF, b1 = (c0 >> 8) | ((c1 & 0xF) << 4),
  * b2 = c1 >> 4 (12-bit codes, 3 bytes per 2 sub-vectors).
  *
@@ -416,6 +423,31 @@ static uint16_t get12(const uint8_t* p, int which)
     return (uint16_t)((p[1] >> 4) | (p[2] << 4));
 }
 
+/* 10-bit codes (1.25-bit format) as little-endian bit fields: bit i of the
+ * field is bit (pos + i) % 8 of byte (pos + i) / 8, one bit at a time.  Four
+ * codes fill five bytes; the 12-bit pair rule above is the same convention. */
+static void put_bits(uint8_t* p, int64_t pos, int width, uint32_t v)
+{
+    for (int i = 0; i < width; ++i) {
+        int64_t b = pos + i;
+        uint8_t m = (uint8_t)(1u << (b % 8));
+        if ((v >> i) & 1u) p[b / 8] = (uint8_t)(p[b / 8] | m);
+        else p[b / 8] = (uint8_t)(p[b / 8] & ~m);
+    }
+}
+
+static uint32_t get_bits(const uint8_t* p, int64_t pos, int width)
+{
+    uint32_t v = 0;
+    for (int i = 0; i < width; ++i) {
+        int64_t b = pos + i;
+        v |= (uint32_t)((p[b / 8] >> (b % 8)) & 1u) << i;
+    }
+    return v;
+}
+
+/* Keys of the 1.25-bit format: token-major, 20 bytes per token, the code of
+ * sub-vector j in bits [10 j, 10 j + 10) of the token's bytes. */
 int vqo_pack_k(int fmt, int64_t T, const uint16_t* codes, uint8_t* out)
 {
     int E, dsub;
@@ -425,6 +457,7 @@ int vqo_pack_k(int fmt, int64_t T, const uint16_t* codes, uint8_t* out)
         for (int j = 0; j < J; ++j) {
             uint16_t c = codes[t * J + j];
             if (fmt == 0) out[t * 32 + j] = (uint8_t)c;
+            else if (fmt == 3) put_bits(out + t * 20, 10 * j, 10, c);
             else put12(out + t * code_bytes(fmt) + 3 * (j / 2), j & 1, c);
         }
     return 0;
@@ -436,9 +469,25 @@ int vqo_unpack_k(int fmt, int64_t T, const uint8_t* in, uint16_t* codes)
     if (vqo_format(fmt, &E, &dsub)) return -1;
     int J = HD / dsub;
     for (int64_t t = 0; t < T; ++t)
-        for (int j = 0; j < J; ++j)
-            codes[t * J + j] = fmt == 0 ? in[t * 32 + j] : get12(in + t * code_bytes(fmt) + 3 * (j / 2), j & 1);
+        for (int j = 0; j < J; ++j) {
+            if (fmt == 0) codes[t * J + j] = in[t * 32 + j];
+            else if (fmt == 3) codes[t * J + j] = (uint16_t)get_bits(in + t * 20, 10 * j, 10);
+            else codes[t * J + j] = get12(in + t * code_bytes(fmt) + 3 * (j / 2), j & 1);
+        }
     return 0;
+}
+
+/* Values of the 1.25-bit format: 64-token blocks of 1280 bytes, 32 streams of
+ * 40 bytes.  As in the 1.5-bit layout, stream 8*((j%8)/2) + 2*(u%4) + j%2
+ * (u = t % 64) holds the pairs (sub-vector j%8, sub-vector j%8 + 8) of the
+ * tokens with that u % 4, pair u/4 in bits [20 (u/4), 20 (u/4) + 20) of the
+ * stream's bytes, sub-vector j in the pair's 10-bit half j / 8.  Returns the
+ * bit position of (t, j) from the start of the cache. */
+static int64_t v_bit_1p25(int64_t t, int j)
+{
+    int64_t u = t % 64;
+    int64_t stream = 8 * ((j % 8) / 2) + 2 * (u % 4) + (j % 2);
+    return ((t / 64) * 1280 + 40 * stream) * 8 + 20 * (u / 4) + 10 * (j / 8);
 }
 
 static int64_t v_offset(int fmt, int64_t t, int j, int* which)
@@ -479,6 +528,11 @@ int vqo_pack_v(int fmt, int64_t T, const uint16_t* codes, uint8_t* out)
     int E, dsub;
     if (vqo_format(fmt, &E, &dsub)) return -1;
     int J = HD / dsub;
+    if (fmt == 3) {
+        for (int64_t t = 0; t < T; ++t)
+            for (int j = 0; j < J; ++j) put_bits(out, v_bit_1p25(t, j), 10, codes[t * J + j]);
+        return 0;
+    }
     for (int64_t t = 0; t < T; ++t)
         for (int j = 0; j < J; ++j) {
             int which;
@@ -494,6 +548,11 @@ int vqo_unpack_v(int fmt, int64_t T, const uint8_t* in, uint16_t* codes)
     int E, dsub;
     if (vqo_format(fmt, &E, &dsub)) return -1;
     int J = HD / dsub;
+    if (fmt == 3) {
+        for (int64_t t = 0; t < T; ++t)
+            for (int j = 0; j < J; ++j) codes[t * J + j] = (uint16_t)get_bits(in, v_bit_1p25(t, j), 10);
+        return 0;
+    }
     for (int64_t t = 0; t < T; ++t)
         for (int j = 0; j < J; ++j) {
             int which;

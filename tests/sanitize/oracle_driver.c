@@ -67,11 +67,11 @@ int main(void) {
         vqo_smooth_scales(cal, 64, sc);
         for (int i = 0; i < HD; ++i) CHECK(sc[i] > 0.0f);
     }
-    for (int fmt = 0; fmt < 3; ++fmt) {
+    for (int fmt = 0; fmt < 4; ++fmt) {
         int E, dsub;
         CHECK(vqo_format(fmt, &E, &dsub) == 0);
         const int J = HD / dsub, n = 5, T = 70, cap = 128;
-        const int W = fmt == 0 ? 32 : (fmt == 1 ? 24 : 48);
+        const int W = fmt == 0 ? 32 : (fmt == 1 ? 24 : (fmt == 2 ? 48 : 20));
         uint16_t* kb = malloc(sizeof(uint16_t) * E * dsub);
         uint16_t* vb = malloc(sizeof(uint16_t) * E * dsub);
         double* bookd = malloc(sizeof(double) * E * dsub);

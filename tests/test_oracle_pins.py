@@ -215,7 +215,7 @@ def test_nearest_duplicate_centroid_goes_to_first():
     assert oracle.nearest(book[3] + 1e-3, book) == 3
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 3])
 def test_quantize_recovers_codes_of_keys_built_from_centroids(fmt):
     """Keys built as k = s * H(concat C_K[codes]) (scipy's H, numpy arithmetic)
     quantize back to the generating codes; values built from C_V likewise."""
@@ -281,7 +281,8 @@ def _numpy_attention(fmt, q, s, kbook, vbook, kc, vc, sm_scale):
     return out
 
 
-@pytest.mark.parametrize("fmt,Hq,Hkv,T", [(0, 4, 1, 300), (0, 8, 2, 129), (1, 5, 1, 77), (1, 4, 2, 1)])
+@pytest.mark.parametrize("fmt,Hq,Hkv,T", [(0, 4, 1, 300), (0, 8, 2, 129), (1, 5, 1, 77), (1, 4, 2, 1),
+                                          (3, 5, 1, 131), (3, 8, 2, 64)])
 def test_attention_matches_numpy_scipy(fmt, Hq, Hkv, T):
     E, dsub = oracle.FORMATS[fmt]
     J = D // dsub
@@ -344,7 +345,7 @@ def test_fp_attention_matches_scipy():
             assert np.abs(got[b, g] - p @ v[b, h]).max() < 1e-13
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 3])
 def test_vq_attention_equals_full_precision_on_exact_cache(fmt):
     """Keys and values built exactly from centroids: VQ attention over the codes
     equals full-precision attention over the raw cache (the transform changes
@@ -372,7 +373,7 @@ def test_vq_attention_equals_full_precision_on_exact_cache(fmt):
     assert np.abs(vq - fp).max() < 1e-12
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 3])
 def test_value_transform_quantize_recovers_codes(fmt):
     """Value-transform variant: values built as v = sv * H(concat C_V[codes])
     (scipy's H) quantize back to the generating codes when the quantizer is
@@ -406,7 +407,7 @@ def test_value_output_transform_undoes_the_value_transform():
         assert np.abs(back - v).max() <= 1e-13 * np.abs(v).max()
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 3])
 def test_vq_attention_with_value_transform_equals_full_precision(fmt):
     """Keys and values built exactly from centroids in the transformed spaces
     (k = s * H k', v = sv * H v'): VQ attention with the value transform equals
@@ -558,6 +559,91 @@ def test_3bit_format_is_twelve_bits_per_four_dims():
     gk, _ = oracle.quantize(2, k, rng.standard_normal((30, D)), s, kbook, vbook)
     kmap = np.array([np.flatnonzero((kf == kf[e]).all(axis=1))[0] for e in range(E)])
     assert np.array_equal(gk, kmap[kc])
+
+
+def _bits(buf, pos, width):
+    """Little-endian bit field [pos, pos + width) of a byte array (Python ints)."""
+    return (int.from_bytes(bytes(buf), "little") >> pos) & ((1 << width) - 1)
+
+
+def test_pack10_golden_examples():
+    """Hand-derived bytes of four 10-bit codes, in the key layout (sub-vectors
+    4..7 of token 0: bytes 5..9) and in the value layout (sub-vectors 5 and
+    13 of tokens 0 and 4, pairs 0 and 1 of stream 8*2 + 0 + 1 = 17: bytes
+    17*40 .. 17*40 + 4)."""
+    for row in _golden_rows("pack10_examples.txt"):
+        c = [int(x, 16) for x in row[:4]]
+        want = [int(x, 16) for x in row[4:]]
+        codes = np.zeros((1, 16), dtype=np.uint16)
+        codes[0, 4:8] = c
+        kb = oracle.pack_k(3, codes, 64)
+        assert list(kb[5:10]) == want and not kb[:5].any() and not kb[10:20].any()
+        vcodes = np.zeros((5, 16), dtype=np.uint16)
+        vcodes[0, 5], vcodes[0, 13], vcodes[4, 5], vcodes[4, 13] = c
+        vb = oracle.pack_v(3, vcodes, 64)
+        assert list(vb[17 * 40:17 * 40 + 5]) == want
+        assert np.count_nonzero(vb) == np.count_nonzero(want)
+
+
+def test_pack10_round_trip_exhaustive():
+    """All 2^20 pairs of 10-bit codes survive pack/unpack in both layouts, at
+    every position of a token (keys) and of a stream (values)."""
+    pairs = np.arange(1 << 20, dtype=np.uint32)
+    c = np.stack([(pairs & 0x3FF), (pairs >> 10)], axis=1).astype(np.uint16).reshape(-1, 16)
+    T = c.shape[0]
+    kb = oracle.pack_k(3, c, T)
+    assert kb.size == T * 20
+    assert np.array_equal(oracle.unpack_k(3, kb, T), c)
+    vb = oracle.pack_v(3, c, T)
+    assert np.array_equal(oracle.unpack_v(3, vb, T), c)
+
+
+def test_pack_1p25bit_positions():
+    """Hand-computed positions of the 1.25-bit layouts (read with Python's own
+    little-endian integers): key code j of token t in bits [160 t + 10 j, +10);
+    value code (t, j), u = t % 64, in block t // 64 of 1280 bytes, stream
+    8*((j%8)//2) + 2*(u%4) + j%2 of 40 bytes, bits 20*(u//4) + 10*(j//8).."""
+    T = 130
+    c = synth.random_codes(6, (T, 16), 1024)
+    kb = oracle.pack_k(3, c, 192)
+    vb = oracle.pack_v(3, c, 192)
+    assert kb.size == vb.size == 192 * 20
+    for t, j in [(0, 0), (0, 15), (1, 3), (77, 9), (129, 15)]:
+        assert _bits(kb[20 * t:20 * t + 20], 10 * j, 10) == c[t, j]
+    assert _bits(vb[0:40], 0, 10) == c[0, 0]                       # stream 0, pair 0, half 0
+    assert _bits(vb[0:40], 10, 10) == c[0, 8]                      # half 1: sub-vector 8
+    assert _bits(vb[40 * 1:40 * 2], 0, 10) == c[0, 1]              # j = 1 -> stream 1
+    assert _bits(vb[40 * 3:40 * 4], 0, 10) == c[1, 1]              # t = 1, j = 1 -> 2 + 1
+    assert _bits(vb[40 * 28:40 * 29], 20 * 15, 10) == c[62, 6]     # u = 62: 8*3 + 2*2 + 0, pair 15
+    assert _bits(vb[40 * 28:40 * 29], 20 * 15 + 10, 10) == c[62, 14]
+    assert _bits(vb[1280 + 40 * 31:1280 + 40 * 32], 0, 10) == c[67, 7]   # block 1, u = 3: 24 + 6 + 1
+    assert _bits(vb[2 * 1280 + 40 * 8:2 * 1280 + 40 * 9], 10, 10) == c[128, 10]  # block 2, u = 0, j = 10
+    assert np.array_equal(oracle.unpack_k(3, kb, T), c)
+    assert np.array_equal(oracle.unpack_v(3, vb, T), c)
+
+
+def test_pack10_leaves_other_tokens_bits_alone():
+    """Tokens share bytes in the value layout (two 20-bit pairs per 5 bytes):
+    packing one token over a filled stream changes only that token's codes."""
+    T = 64
+    c = synth.random_codes(7, (T, 16), 1024)
+    vb = oracle.pack_v(3, c, T)
+    for t in (0, 4, 5, 63):
+        one = c.copy()
+        one[t] = synth.random_codes(8 + t, (1, 16), 1024)[0]
+        vb2 = vb.copy()
+        oracle.pack_v(3, one[:t + 1], T, vb2)      # re-pack tokens 0..t (t's codes new)
+        got = oracle.unpack_v(3, vb2, T)
+        assert np.array_equal(got[t], one[t])
+        assert np.array_equal(np.delete(got, t, axis=0), np.delete(c, t, axis=0))
+
+
+def test_1p25bit_format_is_ten_bits_per_eight_dims():
+    """The 1.25-bit width: 1024 entries of 8 dims, 10 bits per 8 elements, 16
+    codes and 20 bytes per token."""
+    E, dsub = oracle.FORMATS[3]
+    assert (E, dsub) == (1024, 8)
+    assert math.log2(E) / dsub == 1.25 and oracle.code_bytes_per_token(3) * 8 == 10 * 16
 
 
 # ------------------------------------------------------------------------ K-Means
