@@ -40,7 +40,9 @@
  *   12-bit codes of sub-vectors 2i and 2i+1 (dims 8*2i.. and 8*(2i+1)..) share
  *   bytes 3i..3i+2 as b0 = c0 & 0xFF, b1 = (c0 >> 8) | ((c1 & 0xF) << 4),
  *   b2 = c1 >> 4.  3-bit: the same 12-bit pairs for sub-vectors 2i and 2i+1
- *   (dims 4*2i..), 48 bytes per token.
+ *   (dims 4*2i..), 48 bytes per token.  1.25-bit: 10-bit codes as
+ *   little-endian bit fields (the same convention), sub-vector j in bits
+ *   [10j, 10j + 10) of the token's 20 bytes.
  * - Value codes, blocked by tokens and arranged so that every lane of the
  *   decode kernel reads its codes for a block with one wide load.  2-bit:
  *   blocks of 64 tokens, 2048 bytes each, cut into 64 chunks of 32 bytes;
@@ -53,6 +55,10 @@
  *   tokens, 3072 bytes each, cut into 64 chunks of 48 bytes; the codes of
  *   sub-vectors j and j + 16 (j < 16) of token t form one 12-bit pair in chunk
  *   16*(j/4) + 4*(u%4) + j%4 (as in the 2-bit layout), bytes 3*(u/4)..+2.
+ *   1.25-bit: blocks of 64 tokens, 1280 bytes each, cut into 32 streams of 40
+ *   bytes in the 1.5-bit stream order (stream 8*(j/2) + 2*(u%4) + j%2 for the
+ *   pair (j, j + 8), j < 8), the pair of token group u/4 in bits
+ *   [20*(u/4), 20*(u/4) + 20) of the stream, sub-vector j in its low 10 bits.
  * - Codebooks: fp16 [Hkv][E][dsub], one for keys and one for values per KV
  *   head, shared by every sub-vector position.  Key codebooks live in the
  *   rotated space.
@@ -83,6 +89,9 @@ typedef enum {
      * range but print only the two shapes above): 4096 entries x 4 dims,
      * 12-bit codes, 3 bits per element, 48 B per token. */
     VQKV_FMT_3BIT = 2,
+    /* The low end of that range: 1024 entries x 8 dims, 10-bit codes, 1.25 bits
+     * per element, 20 B per token. */
+    VQKV_FMT_1P25BIT = 3,
     /* Flag OR'ed into either format: the value-transform variant.  The pages'
      * technical-framework paragraph quantizes the "preprocessed KV cache"; read
      * that way, values get their own per-channel scales s_v and the keys'
@@ -108,9 +117,9 @@ typedef struct {
 
 /* ------------------------------------------------------------- size queries */
 
-/* Bytes per token per KV head for one of K or V: 32 (2-bit), 24 (1.5-bit) or
- * 48 (3-bit), with or without VQKV_FMT_VALUE_TRANSFORM; 0 for an unknown
- * format.  VecInfer card, "Key points" (codebook size). */
+/* Bytes per token per KV head for one of K or V: 32 (2-bit), 24 (1.5-bit),
+ * 48 (3-bit) or 20 (1.25-bit), with or without VQKV_FMT_VALUE_TRANSFORM; 0 for
+ * an unknown format.  VecInfer card, "Key points" (codebook size). */
 size_t vqkv_code_bytes_per_token(int32_t fmt);
 
 /* Bytes of one code cache (keys or values): B * Hkv * max_tokens * W.

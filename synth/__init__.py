@@ -32,8 +32,9 @@ HEAD_DIM = 128
 FMT_2BIT = 0      # 2^8 entries x 4 dims  -> 2 bits per element
 FMT_1P5BIT = 1    # 2^12 entries x 8 dims -> 1.5 bits per element
 FMT_3BIT = 2      # 2^12 entries x 4 dims -> 3 bits per element
+FMT_1P25BIT = 3   # 2^10 entries x 8 dims -> 1.25 bits per element
 FORMATS = {FMT_2BIT: dict(entries=256, dsub=4), FMT_1P5BIT: dict(entries=4096, dsub=8),
-           FMT_3BIT: dict(entries=4096, dsub=4)}
+           FMT_3BIT: dict(entries=4096, dsub=4), FMT_1P25BIT: dict(entries=1024, dsub=8)}
 
 N_OUTLIER = 4
 OUTLIER_SCALE = 15.0
@@ -77,6 +78,8 @@ WORKLOADS = {
     "qwen14b_b8_t128k_1p5": Workload("qwen14b_b8_t128k_1p5", 8, 40, 8, 131072, FMT_1P5BIT, "bf16"),
     # The added 3-bit width (2^12 x 4) on the Llama-3.1-8B attention shape.
     "llama8b_b8_t196k_3bit": Workload("llama8b_b8_t196k_3bit", 8, 32, 8, 196608, FMT_3BIT, "bf16"),
+    # The 1.25-bit width (2^10 x 8) on the Qwen2.5-14B attention shape of the 1.5-bit workload.
+    "qwen14b_b8_t128k_1p25": Workload("qwen14b_b8_t128k_1p25", 8, 40, 8, 131072, FMT_1P25BIT, "bf16"),
 }
 
 

@@ -24,12 +24,13 @@ LIB_PATH = os.path.join(_HERE, "libvqkv.so")
 FMT_2BIT = 0
 FMT_1P5BIT = 1
 FMT_3BIT = 2                      # 4096 x 4: a third width inside the pages' 1.25-4 bit range
+FMT_1P25BIT = 3                   # 1024 x 8: the low end of that range
 FMT_VALUE_TRANSFORM = 0x100      # OR'ed into a format: values smoothed and rotated too
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 HEAD_DIM = 128
-ENTRIES = {FMT_2BIT: 256, FMT_1P5BIT: 4096, FMT_3BIT: 4096}
-DSUB = {FMT_2BIT: 4, FMT_1P5BIT: 8, FMT_3BIT: 4}
+ENTRIES = {FMT_2BIT: 256, FMT_1P5BIT: 4096, FMT_3BIT: 4096, FMT_1P25BIT: 1024}
+DSUB = {FMT_2BIT: 4, FMT_1P5BIT: 8, FMT_3BIT: 4, FMT_1P25BIT: 8}
 # Kernels selectable for measurement (measure_decode_attention).
 DECODE_PATHS = {"default": 0, "table": 1, "gather": 2, "mfma": 3}
 

@@ -18,7 +18,8 @@
 // Kernels (the matrix-core one chosen by measurement; the others stay
 // selectable for measurement):
 //   * decode_mfma_kernel (default, every format: 2-bit 2^8 x 4, 1.5-bit
-//     2^12 x 8, 3-bit 2^12 x 4): scores and values both on the matrix cores,
+//     2^12 x 8, 3-bit 2^12 x 4, 1.25-bit 2^10 x 8): scores and values both on
+//     the matrix cores,
 //     v_mfma_f32_4x4x4f16, with the centroids gathered from LDS codebooks
 //     (details at the kernel).  For the fused decode step it also finishes
 //     the output: with one split the work-group writes it directly, with more
@@ -519,25 +520,25 @@ __device__ __forceinline__ uint32_t bytes3_at(const uint32_t (&w)[N]) {
     return __builtin_amdgcn_perm(w[d1], w[d], s0 | (s1 << 8) | (s2 << 16) | (0x0cu << 24));
 }
 
-// 2^SH x the 12-bit code at bits [12 C, 12 C + 12) of the little-endian words
-// w, OR base (whose bits SH..SH+11 are clear): a shift or a funnel shift that
-// puts the code at bit SH, then one AND-OR.
-template <int C, int SH, int N>
-__device__ __forceinline__ uint32_t code12_addr(const uint32_t (&w)[N], uint32_t base) {
-    constexpr int S = 12 * C - SH;
-    static_assert(S + SH + 12 <= 32 * N, "code inside the words");
+// 2^SH x the BITS-bit code at bits [BITS C, BITS C + BITS) of the
+// little-endian words w, OR base (whose bits SH..SH+BITS-1 are clear): a shift
+// or a funnel shift that puts the code at bit SH, then one AND-OR.
+template <int BITS, int C, int SH, int N>
+__device__ __forceinline__ uint32_t code_addr(const uint32_t (&w)[N], uint32_t base) {
+    constexpr int S = BITS * C - SH;
+    static_assert(S + SH + BITS <= 32 * N, "code inside the words");
     uint32_t win;
     if constexpr (S < 0) win = w[0] << SH;
-    else if constexpr (S % 32 + SH + 12 <= 32) win = w[S / 32] >> (S % 32);
+    else if constexpr (S % 32 + SH + BITS <= 32) win = w[S / 32] >> (S % 32);
     else win = __builtin_amdgcn_alignbit(w[S / 32 + 1], w[S / 32], S % 32);
     uint32_t r;
     // One v_and_or_b32 (left to itself the compiler splits it into an AND and an ADD).
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(win), "s"(0xfffu << SH), "v"(base));
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(win), "s"(((1u << BITS) - 1u) << SH), "v"(base));
     return r;
 }
-template <int C, int N>
-__device__ __forceinline__ uint32_t code12_x16(const uint32_t (&w)[N], uint32_t base) {
-    return code12_addr<C, 4>(w, base);
+template <int C, int SH, int N>
+__device__ __forceinline__ uint32_t code12_addr(const uint32_t (&w)[N], uint32_t base) {
+    return code_addr<12, C, SH>(w, base);
 }
 
 // 1.5-bit: an 8-dim centroid is two 4-dim halves, so the same products run on
@@ -547,6 +548,13 @@ __device__ __forceinline__ uint32_t code12_x16(const uint32_t (&w)[N], uint32_t 
 // copies (2 x 64 KB).  Key codes are 24 bytes per token; value codes come in
 // 48-byte streams, one per lane pair, 16 pairs (sub-vectors j, j + 8) in step
 // order.
+// 1.25-bit (2^10 x 8): the 1.5-bit products with 10-bit codes (keys 20 bytes
+// per token, value streams of 40 bytes).  A 16 KB book leaves room for four
+// copies in each 64 KB book region, copy c of entry e at 64 e + 16 c: score
+// lookups take copy lane % 4 (the 16 lanes of a 16-byte read pass spread over
+// four copies), value lookups copy (lane / 2) % 4 (a lane pair reads the two
+// halves of one copy), which about halves the bank conflicts of random
+// lookups into a single copy.
 template <int FMT, int G, int NW, bool PAGED, bool APPEND = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int HB = (G + 3) / 4;
@@ -554,8 +562,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int MERGE_BYTES = NW * G * (kHeadDim + 2) * 4;
     constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES;
     constexpr int SMEM = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
-    constexpr int W = FMT == 0 ? 32 : (FMT == 1 ? 24 : 48);
+    constexpr int W = FMT == 0 ? 32 : (FMT == 1 ? 24 : (FMT == 2 ? 48 : 20));
     static_assert(FMT != 1 || 4096 * 16 == kBookBytes, "a 1.5-bit book fills one book region");
+    static_assert(FMT != 3 || 1024 * 16 * 4 == kBookBytes, "four copies of a 1.25-bit book fill one region");
     static_assert(FMT != 2 || 4096 * 8 <= kBookBytes, "a 3-bit book fits one book region");
     __shared__ __align__(16) unsigned char smem[SMEM];
 
@@ -575,8 +584,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // registers across the code loads, their 128 bytes per lane spill.
     constexpr int BOOK_ITERS = FMT == 0 ? 256 * 32 / (NW * 64) : 1;
     static_assert(FMT != 0 || (256 * 32) % (NW * 64) == 0, "the block stages whole rounds");
+    static_assert(FMT != 3 || NW * 64 == 1024, "1.25-bit: one thread per book entry");
     uint2 kreg[BOOK_ITERS], vreg[BOOK_ITERS];
-    if constexpr (FMT == 0) {
+    uint4 kq3, vq3;                                         // 1.25-bit: entry threadIdx.x of each book
+    if constexpr (FMT == 3) {
+        kq3 = ((const uint4*)(a.k_book + (int64_t)h * 1024 * 8))[threadIdx.x];
+        vq3 = ((const uint4*)(a.v_book + (int64_t)h * 1024 * 8))[threadIdx.x];
+    } else if constexpr (FMT == 0) {
         // Slot i holds copy i % 32 of entry i / 32 (256 bytes per entry).
         const uint2* kb = (const uint2*)(a.k_book + (int64_t)h * 256 * 4);
         const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * 256 * 4);
@@ -609,6 +623,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 const int i = threadIdx.x + k * NW * 64;
                 ((uint2*)smem)[i] = kreg[k];
                 ((uint2*)(smem + kBookBytes))[i] = vreg[k];
+            }
+        } else if constexpr (FMT == 3) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ((uint4*)smem)[threadIdx.x * 4 + c] = kq3;
+                ((uint4*)(smem + kBookBytes))[threadIdx.x * 4 + c] = vq3;
             }
         }
     };
@@ -645,8 +665,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     };
     // 2-bit: 32 copies, lane l reads copy l % 32; the value book starts at 64 KB.
     // 1.5-bit: value lookups read half e = lane % 2 of the entry.
-    const uint32_t kofs = FMT == 0 ? (uint32_t)(lane & 31) * 8 : 0u;
+    // 1.25-bit: score lookups copy lane % 4, value lookups copy (lane / 2) % 4, half lane % 2.
+    const uint32_t kofs = FMT == 0 ? (uint32_t)(lane & 31) * 8 : (FMT == 3 ? (uint32_t)(lane & 3) * 16 : 0u);
     const uint32_t vofs = FMT == 0   ? (kofs | (1u << 16))
+                          : FMT == 3 ? (((uint32_t)(lane >> 1) & 3u) * 16 | ((uint32_t)(lane & 1) << 3) | (1u << 16))
                           : FMT == 1 ? (((uint32_t)(lane & 1) << 3) | (1u << 16))
                                      : (1u << 16);
     unsigned char* pt = smem + 2 * kBookBytes + wave * (HB * 512);
@@ -672,10 +694,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // values (chunk = lane of the block).
     const uint8_t* kl2 = kbase + lane * 48;
     const uint8_t* vl2 = vbase + lane * 48;
+    // 1.25-bit: 20 bytes (5 dwords) of the lane's token, 40 bytes (5 x 8) of its
+    // lane pair's value stream (the 1.5-bit stream index).
+    const uint8_t* kl3 = kbase + lane * 20;
+    const uint8_t* vl3 = vbase + vstream * 40;
     uint4 ck0, ck1, cv0, cv1;                               // 2-bit
     uint2 dk[3];                                            // 1.5-bit
     uint4 dv[3];
     uint4 ek[3], ev[3];                                     // 3-bit
+    uint32_t fk[5];                                         // 1.25-bit
+    uint2 fv[5];
     auto load_k = [&](int tl) {
         if constexpr (FMT == 0) {
             const int64_t o = toff(tl);
@@ -684,6 +712,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         } else if constexpr (FMT == 2) {
 #pragma unroll
             for (int i = 0; i < 3; ++i) ek[i] = *(const uint4*)(kl2 + toff(tl) + 16 * i);
+        } else if constexpr (FMT == 3) {
+#pragma unroll
+            for (int i = 0; i < 5; ++i) fk[i] = *(const uint32_t*)(kl3 + toff(tl) + 4 * i);
         } else {
 #pragma unroll
             for (int i = 0; i < 3; ++i) dk[i] = *(const uint2*)(kl1 + toff(tl) + 8 * i);
@@ -697,6 +728,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         } else if constexpr (FMT == 2) {
 #pragma unroll
             for (int i = 0; i < 3; ++i) ev[i] = *(const uint4*)(vl2 + toff(tl) + 16 * i);
+        } else if constexpr (FMT == 3) {
+#pragma unroll
+            for (int i = 0; i < 5; ++i) fv[i] = *(const uint2*)(vl3 + toff(tl) + 8 * i);
         } else {
 #pragma unroll
             for (int i = 0; i < 3; ++i) dv[i] = *(const uint4*)(vl1 + toff(tl) + 16 * i);
@@ -747,7 +781,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         // 2-bit: the query, then the first tiles' codes, then the books into
         // LDS; the waits for the books and the query leave the codes in flight.
         fetch_q(a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim);
-        if constexpr (FMT == 0) {
+        if constexpr (FMT == 0 || FMT == 3) {
             __builtin_amdgcn_sched_barrier(0);
             load_first();
             loaded = true;
@@ -831,13 +865,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             load_k(nxt);
         } else {
             // Scores: 16 sub-vectors in 8 pairs; each 16-byte entry feeds the
-            // products of virtual sub-vectors 2j and 2j + 1.
-            const uint32_t kw[6] = {dk[0].x, dk[0].y, dk[1].x, dk[1].y, dk[2].x, dk[2].y};
+            // products of virtual sub-vectors 2j and 2j + 1.  12-bit codes of
+            // 24 bytes (1.5-bit), or 10-bit codes of 20 bytes at 64-byte entry
+            // strides (1.25-bit, four copies).
+            constexpr int CB = FMT == 3 ? 10 : 12, CSH = FMT == 3 ? 6 : 4, NKW = FMT == 3 ? 5 : 6;
+            uint32_t kw[NKW];
+            if constexpr (FMT == 3) {
+#pragma unroll
+                for (int i = 0; i < 5; ++i) kw[i] = fk[i];
+            } else {
+                kw[0] = dk[0].x; kw[1] = dk[0].y; kw[2] = dk[1].x; kw[3] = dk[1].y; kw[4] = dk[2].x; kw[5] = dk[2].y;
+            }
             static_for<0, 8>([&](auto mc) {
                 constexpr int mp = decltype(mc)::value;
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const uint32_t addr = u == 0 ? code12_x16<2 * mp>(kw, 0u) : code12_x16<2 * mp + 1>(kw, 0u);
+                    const uint32_t addr = u == 0 ? code_addr<CB, 2 * mp, CSH>(kw, kofs)
+                                                 : code_addr<CB, 2 * mp + 1, CSH>(kw, kofs);
                     const uint4 ent = *(const uint4*)(smem + addr);
                     const half4_t lo = __builtin_bit_cast(half4_t, make_uint2(ent.x, ent.y));
                     const half4_t hi = __builtin_bit_cast(half4_t, make_uint2(ent.z, ent.w));
@@ -924,14 +968,25 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             load_v(nxt);
         } else {
-            // Values: step st takes pair st of the lane's stream (bytes 3 st..).
-            const uint32_t vw[12] = {dv[0].x, dv[0].y, dv[0].z, dv[0].w, dv[1].x, dv[1].y,
-                                     dv[1].z, dv[1].w, dv[2].x, dv[2].y, dv[2].z, dv[2].w};
+            // Values: step st takes pair st of the lane's stream (bits 24 st..,
+            // 1.5-bit; bits 20 st.., 1.25-bit).
+            constexpr int CB = FMT == 3 ? 10 : 12, CSH = FMT == 3 ? 6 : 4, NVW = FMT == 3 ? 10 : 12;
+            uint32_t vw[NVW];
+            if constexpr (FMT == 3) {
+#pragma unroll
+                for (int i = 0; i < 5; ++i) { vw[2 * i] = fv[i].x; vw[2 * i + 1] = fv[i].y; }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    vw[4 * i] = dv[i].x; vw[4 * i + 1] = dv[i].y; vw[4 * i + 2] = dv[i].z; vw[4 * i + 3] = dv[i].w;
+                }
+            }
             static_for<0, 16>([&](auto sc16) {
                 constexpr int st = decltype(sc16)::value;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const uint32_t addr = hh == 0 ? code12_x16<2 * st>(vw, vofs) : code12_x16<2 * st + 1>(vw, vofs);
+                    const uint32_t addr = hh == 0 ? code_addr<CB, 2 * st, CSH>(vw, vofs)
+                                                  : code_addr<CB, 2 * st + 1, CSH>(vw, vofs);
                     const half4_t vv = lds_read_tr16((const lds_char*)(smem + addr));
 #pragma unroll
                     for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_bcast<st>(pt_op[hb], vv, o[hb][hh]);
@@ -1243,16 +1298,21 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                 VQKV_G(1, 1) VQKV_G(1, 2) VQKV_G(1, 3) VQKV_G(1, 4) VQKV_G(1, 5) VQKV_G(1, 6) VQKV_G(1, 7) VQKV_G(1, 8)
                 default: return hipErrorInvalidValue;
             }
-        } else {
+        } else if (a.fmt == 2) {
             switch (G) {
                 VQKV_G(2, 1) VQKV_G(2, 2) VQKV_G(2, 3) VQKV_G(2, 4) VQKV_G(2, 5) VQKV_G(2, 6) VQKV_G(2, 7) VQKV_G(2, 8)
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (G) {
+                VQKV_G(3, 1) VQKV_G(3, 2) VQKV_G(3, 3) VQKV_G(3, 4) VQKV_G(3, 5) VQKV_G(3, 6) VQKV_G(3, 7) VQKV_G(3, 8)
                 default: return hipErrorInvalidValue;
             }
         }
 #undef VQKV_G
         return hipGetLastError();
     }
-    if (a.block_table || a.fmt == 2) return hipErrorInvalidValue;   // matrix-core kernel only
+    if (a.block_table || a.fmt >= 2) return hipErrorInvalidValue;   // matrix-core kernel only
     if (a.fmt == 0) return launch_gather<0, 8>(a, grid, stream);
     return launch_gather<1, 8>(a, grid, stream);
 }

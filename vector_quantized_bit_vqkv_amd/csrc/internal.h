@@ -40,6 +40,20 @@ __host__ __device__ __forceinline__ int64_t v_pair_offset_3bit(int64_t t, int j)
     return (t >> 6) * 3072 + 48 * chunk + 3 * (u >> 2);
 }
 
+// Bit position, from the start of a 1.25-bit value stream (b, h), of the
+// 10-bit value code of (token t, sub-vector j), j < 16.  Blocks of 64 tokens x
+// 16 sub-vectors = 1280 bytes, cut into 32 streams of 40 bytes in the 1.5-bit
+// stream order: stream 8*((j%8)/2) + 2*(t%4) + j%2 holds the pairs (sub-vector
+// j%8, sub-vector j%8 + 8) of its 16 tokens, pair (t%64)/4 in bits
+// [20 ((t%64)/4), +20), sub-vector j in the pair's 10-bit half j / 8.  Two
+// consecutive pairs (tokens u and u + 4 of one 8-token group) share five
+// bytes: a writer of one token's pair keeps the other's bits.
+__host__ __device__ __forceinline__ int64_t v_bit_1p25(int64_t t, int j) {
+    const int u = (int)(t & 63);
+    const int stream = 8 * ((j & 7) >> 1) + 2 * (u & 3) + (j & 1);
+    return ((t >> 6) * 1280 + 40 * stream) * 8 + 20 * (u >> 2) + 10 * (j >> 3);
+}
+
 struct TransformQueryArgs {
     const void* q;          // [B][Hq][128], bf16 or fp32
     int dtype;              // 0 bf16, 1 fp32

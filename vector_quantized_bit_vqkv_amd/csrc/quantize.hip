@@ -5,8 +5,8 @@
 // "technical framework" paragraph: keys are smoothed per channel and rotated
 // by a Hadamard transform, then keys and values are vector-quantized against
 // codebooks trained offline with K-Means ("Key points": 2^8 x 4 entries for
-// 2-bit, 2^12 x 8 for 1.5-bit; a third width inside the pages' 1.25-4 bit
-// range, 2^12 x 4 at 3 bits, takes the same steps).  In the value-transform
+// 2-bit, 2^12 x 8 for 1.5-bit; two more widths inside the pages' 1.25-4 bit
+// range, 2^12 x 4 at 3 bits and 2^10 x 8 at 1.25 bits, take the same steps).  In the value-transform
 // variant the values take the keys' steps with their own scales s_v.
 //
 // Every decision that turns floating point into an integer (a code, a K-Means
@@ -33,6 +33,27 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<0> { static constexpr int E = 256, DS = 4, J = 32, W = 32; };
 template <> struct Fmt<1> { static constexpr int E = 4096, DS = 8, J = 16, W = 24; };
 template <> struct Fmt<2> { static constexpr int E = 4096, DS = 4, J = 32, W = 48; };
+template <> struct Fmt<3> { static constexpr int E = 1024, DS = 8, J = 16, W = 20; };
+
+// Writes the `width`-bit field v (width <= 56) at bit `bit` of the little-endian
+// byte string p, keeping every bit outside the field (1.25-bit codes: 10-bit
+// fields that do not start on byte boundaries).
+__device__ __forceinline__ void put_field(uint8_t* p, int64_t bit, int width, uint64_t v) {
+    uint8_t* q = p + (bit >> 3);
+    const int sh = (int)(bit & 7), nb = (sh + width + 7) >> 3;
+    uint64_t w = 0;
+    for (int i = 0; i < nb; ++i) w |= (uint64_t)q[i] << (8 * i);
+    const uint64_t mask = ((1ull << width) - 1ull) << sh;
+    w = (w & ~mask) | ((v << sh) & mask);
+    for (int i = 0; i < nb; ++i) q[i] = (uint8_t)(w >> (8 * i));
+}
+
+// 1.25-bit keys: the token's four 10-bit codes c[0..3] of sub-vectors 4i..4i+3
+// fill bytes 5i..5i+4 of its 20 bytes.
+__device__ __forceinline__ void put_key_group_1p25(uint8_t* tok, int i, const uint16_t* c) {
+    const uint64_t v = (uint64_t)c[0] | ((uint64_t)c[1] << 10) | ((uint64_t)c[2] << 20) | ((uint64_t)c[3] << 30);
+    put_field(tok, 40 * i, 40, v);
+}
 
 // Byte offset of the value pair (j, j + J/2) of token t, 12-bit formats.
 template <int FMT>
@@ -242,7 +263,9 @@ __device__ __forceinline__ double screen_operands(const double* x, int np, half4
 
 // -------------------------------------------------------------- append kernel
 
-template <int FMT> struct AppendTile { static constexpr int TT = FMT == 0 ? 32 : 16; };   // 1.5- and 3-bit: 16
+// Tiles are TT-aligned; 1.25-bit value pairs of tokens u, u + 4 (u % 8 < 4) share
+// bytes, so its tiles must hold whole 8-token groups (TT a multiple of 8).
+template <int FMT> struct AppendTile { static constexpr int TT = FMT == 0 ? 32 : 16; };   // 12- and 10-bit: 16
 
 // The screen's bound for a point of norm xn against a book with
 // (max |c|^2, max |c|_1) = cb.
@@ -273,6 +296,31 @@ __device__ __forceinline__ int refine_point(const double* xp, const uint16_t* bo
     }
     wave_argmin(d, idx);
     return idx;
+}
+
+// Writes the 1.25-bit codes of tile rows [off, off + nt) (positions
+// tile_base + row; kcodes / vcodes [TT][16]): keys in whole 5-byte groups of
+// their token; values per 5-byte group of a stream, which holds the pairs
+// (j, j + 8) of the tokens u and u + 4 of one 8-token group (u % 8 < 4) --
+// both in the tile, since tiles are 8-aligned -- a token outside [off, off +
+// nt) keeping its bits.  One thread per group: no two threads share a byte.
+template <int TT>
+__device__ void write_tile_1p25(uint8_t* kc, uint8_t* vc, int64_t tile_base, int off, int nt,
+                                const uint16_t* kcodes, const uint16_t* vcodes) {
+    static_assert(TT % 8 == 0, "whole 8-token groups per tile");
+    constexpr int J = 16, W = 20;
+    for (int idx = threadIdx.x; idx < nt * 4; idx += blockDim.x) {
+        const int r = off + idx / 4, i = idx % 4;
+        put_key_group_1p25(kc + (tile_base + r) * W, i, kcodes + r * J + 4 * i);
+    }
+    for (int idx = threadIdx.x; idx < (TT / 8) * 4 * 8; idx += blockDim.x) {
+        const int ra = (idx / 32) * 8 + (idx / 8) % 4, rb = ra + 4, j = idx % 8;
+        const bool ina = ra >= off && ra < off + nt, inb = rb >= off && rb < off + nt;
+        if (!ina && !inb) continue;
+        const int64_t bit = v_bit_1p25(tile_base + ra, j);          // a multiple of 40: five whole bytes
+        if (ina) put_field(vc, bit, 20, (uint64_t)vcodes[ra * J + j] | ((uint64_t)vcodes[ra * J + j + 8] << 10));
+        if (inb) put_field(vc, bit + 20, 20, (uint64_t)vcodes[rb * J + j] | ((uint64_t)vcodes[rb * J + j + 8] << 10));
+    }
 }
 
 // Bulk quantization of a tile of TT positions of one (b, KV head) by the
@@ -380,6 +428,8 @@ __global__ __launch_bounds__(1024) void quantize_screen_kernel(AppendArgs a) {
             kc[t * W + j] = (uint8_t)codes[0][r * J + j];
             vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[1][r * J + j];
         }
+    } else if (FMT == 3) {
+        write_tile_1p25<TT>(kc, vc, tile_base, off, nt, codes[0], codes[1]);
     } else {
         // Keys: sub-vectors (2i, 2i+1) of a token share 3 bytes.
         for (int idx = threadIdx.x; idx < nt * (J / 2); idx += blockDim.x) {
@@ -499,6 +549,8 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
             kc[t * W + j] = (uint8_t)codes[0][r * J + j];
             vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[1][r * J + j];
         }
+    } else if (FMT == 3) {
+        write_tile_1p25<TT>(kc, vc, tile_base, off, nt, codes[0], codes[1]);
     } else {
         // Keys: sub-vectors (2i, 2i+1) of a token share 3 bytes.
         for (int idx = threadIdx.x; idx < nt * (J / 2); idx += blockDim.x) {
@@ -553,7 +605,7 @@ __device__ __forceinline__ void screen_dot(const uint16_t* c, const half2_t (&xh
 
 // Blocks per key (and per value) of the one-token append: a 4096-entry search
 // is split over 4 blocks of 4 sub-vectors each, so the grid fills the GPU.
-template <int FMT> struct TokenSplit { static constexpr int P = FMT == 0 ? 1 : 4; };   // 4096 entries: 4
+template <int FMT> struct TokenSplit { static constexpr int P = FMT == 0 ? 1 : (FMT == 3 ? 2 : 4); };   // 1024: 2, 4096: 4
 
 // The per-step append (one new token per sequence), latency-bound: grid
 // (2P, Hkv, B), block x / P = 0 codes the key, 1 the value, x % P = part p
@@ -753,6 +805,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
             if (ph == 0) kblk[u * W + j] = (uint8_t)codes[threadIdx.x];
             else vblk[v_code_offset_2bit(u, j)] = (uint8_t)codes[threadIdx.x];
         }
+    } else if (FMT == 3) {
+        // Keys: the block's JB consecutive sub-vectors, whole 5-byte groups of
+        // the token.  Values: the pairs (j, j + 8), 20 bits each, sharing a
+        // byte with token u +- 4, whose bits are kept (one token per stream
+        // per call: no other writer of that byte).
+        if (ph == 0 && threadIdx.x < JB / 4)
+            put_key_group_1p25(kblk + u * W, (part * JB) / 4 + (int)threadIdx.x, codes + 4 * threadIdx.x);
+        if (ph == 1 && threadIdx.x < JB / 2) {
+            const int m = threadIdx.x;
+            put_field(vblk, v_bit_1p25(u, sub_of(m)), 20, (uint64_t)codes[m] | ((uint64_t)codes[m + JB / 2] << 10));
+        }
     } else if (threadIdx.x < JB / 2) {
         // Keys: sub-vectors (2i, 2i+1) share 3 bytes (the block's jj = 2m, 2m+1);
         // values: (i, i + J/2) (the block's jj = m, m + JB/2).
@@ -926,20 +989,24 @@ hipError_t train_codebook(const TrainArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
-    const int TT = a.fmt == 0 ? AppendTile<0>::TT : (a.fmt == 1 ? AppendTile<1>::TT : AppendTile<2>::TT);
+    const int TT = a.fmt == 0 ? AppendTile<0>::TT
+                 : (a.fmt == 1 ? AppendTile<1>::TT : (a.fmt == 2 ? AppendTile<2>::TT : AppendTile<3>::TT));
     const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
     const dim3 grid(last - first + 1, a.hkv, a.batch);
     if (a.n_new == 1 || a.positions) {
-        const dim3 g1(2 * (a.fmt == 0 ? TokenSplit<0>::P : (a.fmt == 1 ? TokenSplit<1>::P : TokenSplit<2>::P)),
-                      a.hkv, a.batch);
+        const int P = a.fmt == 0 ? TokenSplit<0>::P
+                    : (a.fmt == 1 ? TokenSplit<1>::P : (a.fmt == 2 ? TokenSplit<2>::P : TokenSplit<3>::P));
+        const dim3 g1(2 * P, a.hkv, a.batch);
         if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(1024), 0, stream, a);
         else if (a.fmt == 1) hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
-        else hipLaunchKernelGGL(quantize_token_kernel<2>, g1, dim3(1024), 0, stream, a);
+        else if (a.fmt == 2) hipLaunchKernelGGL(quantize_token_kernel<2>, g1, dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL(quantize_token_kernel<3>, g1, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     if (a.fmt == 0) hipLaunchKernelGGL(quantize_exact_kernel<0>, grid, dim3(256), 0, stream, a);
     else if (a.fmt == 1) hipLaunchKernelGGL(quantize_screen_kernel<1>, grid, dim3(1024), 0, stream, a);
-    else hipLaunchKernelGGL(quantize_screen_kernel<2>, grid, dim3(1024), 0, stream, a);
+    else if (a.fmt == 2) hipLaunchKernelGGL(quantize_screen_kernel<2>, grid, dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL(quantize_screen_kernel<3>, grid, dim3(1024), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -950,6 +1017,7 @@ hipError_t launch_smooth_scales(int hkv, int n_cal, const void* k_cal, int dtype
 
 hipError_t launch_train_codebook(const TrainArgs& a, hipStream_t stream) {
     if (a.fmt == 0) return train_codebook<0>(a, stream);
+    if (a.fmt == 3) return train_codebook<3>(a, stream);
     return a.fmt == 1 ? train_codebook<1>(a, stream) : train_codebook<2>(a, stream);
 }
 
