@@ -21,8 +21,8 @@ the attention of the step's queries over the whole context (within 2e-3 of the
 step's output).  No oracle input comes from the library: the GPU's scales and
 books are compared with the oracle's, and the oracle then runs on its own.
 
-Runtime: about 10 s of GPU work and 1-2 minutes of oracle time on 16 host
-threads for the whole file, most of it the 1.5-bit codebooks and codes.
+Runtime on the GPU machine (16 host threads for the oracle): about 20 s for the
+whole file, most of it the oracle's 1.5-bit codebooks and codes.
 """
 import os
 import time
@@ -55,13 +55,16 @@ def rel_err(got, ref):
     return float((num / den).max())
 
 
-def last_token_value_bytes(fmt, E, J):
-    """Byte positions, inside a 64-token value block, of the block's last token:
-    the bytes the oracle's packing fills when only that token has a nonzero
-    code (E - 1 sets every bit of every one of its codes)."""
+def last_token_value_bits(fmt, E, J):
+    """Bytes, inside a 64-token value block, that hold bits of the block's last
+    token, and the mask of its bits in each: what the oracle's packing sets
+    when only that token has nonzero codes (E - 1 sets every bit of each of
+    its codes).  In the 1.25-bit layout a byte can hold bits of two tokens."""
     probe = np.zeros((64, J), dtype=np.uint16)
     probe[63] = E - 1
-    return np.nonzero(oracle.pack_v(fmt, probe, 64))[0]
+    packed = oracle.pack_v(fmt, probe, 64)
+    pos = np.nonzero(packed)[0]
+    return pos, packed[pos]
 
 
 # (workload, number of sampled (b, KV head) slices)
@@ -82,10 +85,13 @@ def test_product_step_at_full_size(name, nsamp):
     W = vq.code_bytes_per_token(fmt)
     kc_dev, vc_dev = wk.caches[0]
 
-    # The step must write the new token's codes itself: overwrite its bytes.
+    # The step must write the new token's codes itself: overwrite its bits
+    # (only its own: other tokens' bits sharing a byte keep their values).
     kc_dev[:, :, (T - 1) * W:] = PATTERN
-    vpos = torch.from_numpy(last_token_value_bytes(fmt, E, J) + (T - 64) * W).to(DEV)
-    vc_dev[:, :, vpos] = PATTERN
+    pos, bits = last_token_value_bits(fmt, E, J)
+    vpos = torch.from_numpy(pos + (T - 64) * W).to(DEV)
+    mask = torch.from_numpy(bits).to(DEV)
+    vc_dev[:, :, vpos] = (vc_dev[:, :, vpos] & ~mask) | (PATTERN & mask)
     torch.cuda.synchronize()
     wk.fused_step(0)                 # decode_step on caches[0], as the timed loop calls it
     torch.cuda.synchronize()

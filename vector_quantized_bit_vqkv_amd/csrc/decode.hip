@@ -576,29 +576,32 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int t_begin = s * a.chunk;
     const int t_end = min(seq_len_of(a, b), t_begin + a.chunk);
 
-    // 2-bit: codebook entries are fetched into registers here and written to
-    // LDS after the first tiles' code loads have been issued (loads complete
-    // in order, so waiting for book loads issued after the code loads would
-    // also wait for the codes, and the first tiles' latency would not overlap
-    // the staging).  The 12-bit formats stage their books directly: held in
-    // registers across the code loads, their 128 bytes per lane spill.
-    constexpr int BOOK_ITERS = FMT == 0 ? 256 * 32 / (NW * 64) : 1;
-    static_assert(FMT != 0 || (256 * 32) % (NW * 64) == 0, "the block stages whole rounds");
+    // 2-bit and 1.25-bit: codebook entries are fetched into registers here and
+    // written to LDS after the first tiles' code loads have been issued (loads
+    // complete in order, so waiting for book loads issued after the code loads
+    // would also wait for the codes, and the first tiles' latency would not
+    // overlap the staging).  The 2-bit books come through the scalar path: wave
+    // w reads entries [16 w, 16 w + 16) of each book (128 bytes, four 64-byte
+    // scalar loads in all) into SGPRs, so they are not queued in the vector
+    // memory pipeline behind the other waves' first code requests (batch-1
+    // decode over 32k tokens 11.3 -> 9.8 us).  The 12-bit formats stage their
+    // books directly: held in registers across the code loads, their 128 bytes
+    // per lane spill.
+    static_assert(FMT != 0 || NW == 16, "2-bit: 16 waves stage 16 entries each");
     static_assert(FMT != 3 || NW * 64 == 1024, "1.25-bit: one thread per book entry");
-    uint2 kreg[BOOK_ITERS], vreg[BOOK_ITERS];
+    uint32_t kd[FMT == 0 ? 32 : 1], vd[FMT == 0 ? 32 : 1];  // 2-bit: the wave's 16 entries (SGPRs)
     uint4 kq3, vq3;                                         // 1.25-bit: entry threadIdx.x of each book
     if constexpr (FMT == 3) {
         kq3 = ((const uint4*)(a.k_book + (int64_t)h * 1024 * 8))[threadIdx.x];
         vq3 = ((const uint4*)(a.v_book + (int64_t)h * 1024 * 8))[threadIdx.x];
     } else if constexpr (FMT == 0) {
-        // Slot i holds copy i % 32 of entry i / 32 (256 bytes per entry).
-        const uint2* kb = (const uint2*)(a.k_book + (int64_t)h * 256 * 4);
-        const uint2* vb = (const uint2*)(a.v_book + (int64_t)h * 256 * 4);
+        typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+        const const_u32_ptr kbs = (const_u32_ptr)(a.k_book + (int64_t)h * 256 * 4) + wave * 32;
+        const const_u32_ptr vbs = (const_u32_ptr)(a.v_book + (int64_t)h * 256 * 4) + wave * 32;
 #pragma unroll
-        for (int k = 0; k < BOOK_ITERS; ++k) {
-            const int i = threadIdx.x + k * NW * 64;
-            kreg[k] = kb[i >> 5];
-            vreg[k] = vb[i >> 5];
+        for (int i = 0; i < 32; ++i) {
+            kd[i] = kbs[i];
+            vd[i] = vbs[i];
         }
     } else if constexpr (FMT == 2) {
         // 3-bit: single copies, 8-byte entries (4 dims).
@@ -618,11 +621,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
     auto write_books = [&]() {
         if constexpr (FMT == 0) {
+            // Slot 32 e + c holds copy c of entry e (256 bytes per entry): wave w
+            // writes entries 16 w + 2 k (lanes 0..31, copy = lane) and 16 w + 2 k + 1
+            // (lanes 32..63, copy = lane - 32).
 #pragma unroll
-            for (int k = 0; k < BOOK_ITERS; ++k) {
-                const int i = threadIdx.x + k * NW * 64;
-                ((uint2*)smem)[i] = kreg[k];
-                ((uint2*)(smem + kBookBytes))[i] = vreg[k];
+            for (int k = 0; k < 8; ++k) {
+                const bool lo = lane < 32;
+                const int slot = (16 * wave + 2 * k) * 32 + lane;
+                ((uint2*)smem)[slot] = make_uint2(lo ? kd[4 * k] : kd[4 * k + 2], lo ? kd[4 * k + 1] : kd[4 * k + 3]);
+                ((uint2*)(smem + kBookBytes))[slot] =
+                    make_uint2(lo ? vd[4 * k] : vd[4 * k + 2], lo ? vd[4 * k + 1] : vd[4 * k + 3]);
             }
         } else if constexpr (FMT == 3) {
 #pragma unroll
