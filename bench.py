@@ -57,7 +57,7 @@ def host_cpu():
 # HBM traffic of the decode kernel comes from rocprofv3 counters recorded in
 # this file, valid only while the kernel sources still hash to the recorded value.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_kernel__llama8b_b32_t196k__hbm_traffic.txt")
-KERNEL_SOURCES = ["decode.hip", "attn_common.h", "device_util.h", "internal.h"]
+KERNEL_SOURCES = ["decode.hip", "attn_common.h", "device_util.h", "internal.h", "qtransform.h", "token_search.h"]
 
 
 def kernel_source_hash():
