@@ -202,17 +202,13 @@ class Workload:
             vq.decode_attention(self.shape, self.q_prime, self.k_book, self.v_book, kc, vc, T, self.S,
                                 self.workspace)
 
-    def step(self, i, ev=None):
+    def step(self, i):
         import vector_quantized_bit_vqkv_amd as vq
         kc, vc = self.caches[i % len(self.caches)]
         T = self.wl.seq_len
         vq.quantize_append(self.shape, self.k_new, self.v_new, T - 1, self.smooth, self.k_book, self.v_book, kc, vc)
         vq.transform_query(self.shape, self.q, self.smooth, self.q_prime)
-        if ev is not None:
-            ev[0].record()
         self.decode(kc, vc)
-        if ev is not None:
-            ev[1].record()
         vq.combine(self.shape, self.S, self.workspace, self.out)
 
     def fused_step(self, i):
@@ -242,27 +238,42 @@ class Workload:
             per_run.append(start.elapsed_time(end) / steps)
         return per_run
 
-    def time_steps(self, steps, warmup, runs=RUNS):
-        """The step as four separate calls, with events around every decode launch.
-        Returns the mean ms per step of each run and every decode launch's ms."""
+    def _time_runs(self, fn, steps, warmup, runs):
+        """Mean ms per call of `steps` back-to-back calls fn(i), for each of `runs`
+        runs, bracketed by HIP events on torch's current stream (the stream every
+        call launches on)."""
         import torch
         for i in range(warmup):
-            self.step(i)
+            fn(i)
         torch.cuda.synchronize()
-        per_run, dec = [], []
+        per_run = []
         for r in range(runs):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
             start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
             head_start(self.q.device)
             start.record()
             for i in range(steps):
-                self.step(warmup + r * steps + i, evs[i])
+                fn(warmup + r * steps + i)
             end.record()
             torch.cuda.synchronize()
             per_run.append(start.elapsed_time(end) / steps)
-            dec.extend(a.elapsed_time(b) for a, b in evs)
-        return per_run, dec
+        return per_run
+
+    def time_steps(self, steps, warmup, runs=RUNS):
+        """The step as four separate calls: mean ms per step of each run."""
+        return self._time_runs(self.step, steps, warmup, runs)
+
+    def time_decode(self, steps, warmup, runs=RUNS):
+        """The attention pass alone (vqkv_decode_attention), back to back over the
+        rotated cache copies: mean ms per launch of each run.  (Events around
+        single launches in a mixed stream add their own recording to each
+        launch, several us at batch 1; back-to-back launches do not.)"""
+        import vector_quantized_bit_vqkv_amd as vq
+        vq.transform_query(self.shape, self.q, self.smooth, self.q_prime)
+
+        def once(i):
+            kc, vc = self.caches[i % len(self.caches)]
+            self.decode(kc, vc)
+        return self._time_runs(once, steps, warmup, runs)
 
     def time_attention_only(self, steps, warmup):
         """decode + combine only (what the bf16 comparison times)."""
@@ -274,17 +285,7 @@ class Workload:
             kc, vc = self.caches[i % len(self.caches)]
             self.decode(kc, vc)
             vq.combine(self.shape, self.S, self.workspace, self.out)
-        for i in range(warmup):
-            once(i)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        head_start(self.q.device)
-        a.record()
-        for i in range(steps):
-            once(i)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps
+        return pct(self._time_runs(once, steps, warmup, RUNS), 0.5)
 
     def time_bf16(self, steps, warmup):
         """The same attention over the unquantized bf16 cache (bf16 decode + combine),
@@ -407,12 +408,13 @@ def measure(name, args, dev, with_bf16, with_cpu):
     import torch
     wk = Workload(name, dev, keep_bf16=with_bf16)
     wk.decode_path = args.decode_path
-    four_runs, dec = wk.time_steps(args.steps, args.warmup)
+    four_runs = wk.time_steps(args.steps, args.warmup)
     # The product step is decode_step; a measurement override of the decode
     # kernel applies to the four separate calls only, so it times those.
     step_runs = four_runs if args.decode_path else wk.time_fused_steps(args.steps, args.warmup)
     step_ms, four_ms = pct(step_runs, 0.5), pct(four_runs, 0.5)
-    dec_ms = sum(dec) / len(dec)
+    dec = wk.time_decode(args.steps, args.warmup)
+    dec_ms = sum(dec) / len(dec)                  # every run has the same number of launches
     attn_ms = wk.time_attention_only(args.steps, args.warmup)
     res = {
         "workload": name,
@@ -428,7 +430,7 @@ def measure(name, args, dev, with_bf16, with_cpu):
         "decode_us_median": round(pct(dec, 0.5) * 1e3, 2),
         "decode_us_p10": round(pct(dec, 0.1) * 1e3, 2),
         "decode_us_p90": round(pct(dec, 0.9) * 1e3, 2),
-        "decode_launches": len(dec),
+        "decode_launches": len(dec) * args.steps,
         "decode_GBps": round(wk.decode_bytes / (dec_ms * 1e-3) / 1e9, 1),
         "attention_us": round(attn_ms * 1e3, 2),
         "num_splits": wk.S,
