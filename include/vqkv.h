@@ -271,6 +271,9 @@ vqkv_status vqkv_quantize_append_paged(const vqkv_shape* shape, const void* k_ne
  * normalized output and the log-sum-exp of its scores:
  * out[b][g] = sum_i exp(lse_i - L) o_i, L = log sum_i exp(lse_i); a split
  * with no token (lse_i = -inf) weighs 0, and a row with no token gives 0.
+ * The workspace holds each lse_i as two numbers, the split's largest score
+ * and the log of its weight sum, so the weights keep full fp32 precision
+ * whatever the size of the scores.
  *   workspace   device, as written by vqkv_decode_attention with the same
  *               shape and num_splits
  *   out         device, fp32 [B][Hq][128] (output; with VQKV_FMT_VALUE_TRANSFORM

@@ -1158,6 +1158,28 @@ def test_decode_single_token_returns_its_value():
         assert np.abs(got[0, g] - v0).max() <= 1e-6 * np.abs(v0).max()
 
 
+@pytest.mark.parametrize("fmt,Hq,Hkv,S", [(0, 8, 2, 3), (1, 10, 2, 3), (2, 8, 2, 1), (3, 10, 2, 4)])
+def test_decode_query_beyond_fp16_range(fmt, Hq, Hkv, S):
+    """Queries whose elements times sm_scale * log2(e) pass the fp16 maximum
+    (65504): the matrix-core path scales such a head's query operand by a
+    power of two and takes its scores back in the exponents.  With unit
+    smoothing scales and a constant query row, q' = H q is that constant
+    times sqrt(128) on dim 0 and exactly zero elsewhere, so the softmax puts
+    equal weights on the tokens whose sub-vector-0 centroid has the largest
+    (first head) or smallest (last head) dim 0; the other heads stay normal."""
+    say(f"decode with fp16-overflowing queries, fmt {fmt} Hq{Hq} Hkv{Hkv} S{S}")
+    q, s, kb, vb, kc, vc, cap = _attn_inputs(fmt, 1, Hq, Hkv, 1000, 4242 + fmt)
+    s = np.ones_like(s)
+    q[0, 0, :] = 5.0e5          # q'_0 * sm_scale * log2(e) ~ 7.2e5
+    q[0, Hq - 1, :] = -3.0e6    # ~ -4.3e6
+    got = _gpu_attention(fmt, q, s, kb, vb, kc, vc, cap, S)
+    ref = oracle.attention(fmt, q, s, kb, vb, kc, vc)
+    assert np.isfinite(got).all()
+    err = rel_err(got, ref)
+    print(f"  max relative error {err:.3e}", flush=True)
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("fmt,path", [(0, "table"), (0, "gather"), (0, "mfma"), (1, "mfma"), (1, "gather"), (2, "mfma"),
                                       (3, "mfma")])
 def test_decode_split_invariance_and_determinism(fmt, path):

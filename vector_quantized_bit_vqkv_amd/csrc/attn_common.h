@@ -55,6 +55,31 @@ __device__ __forceinline__ void softmax_tile_lazy(float (&sc)[G], float (&m)[G],
     for (int g = 0; g < G; ++g) p[g] = __builtin_amdgcn_exp2f(sc[g] - m[g] + (float)P_LOG2);
 }
 
+// softmax_tile_lazy for scores that arrive scaled: head g's scores (and m[g],
+// kept in the same units) are its true scores times 2^-k_g, and sm[g] = 2^k_g
+// takes them back inside the exponents.  With sm[g] = 1 every result is
+// bit-identical to softmax_tile_lazy (x * 1 is exact and the fused add rounds
+// once, as the plain add does).
+template <int G, int P_LOG2, class Rescale>
+__device__ __forceinline__ void softmax_tile_lazy_scaled(float (&sc)[G], float (&m)[G], const float (&sm)[G],
+                                                         float (&p)[G], Rescale&& rescale) {
+    bool up = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) up = up || (sc[g] > m[g]);
+    if (__ballot(up)) {                                     // wave-uniform
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mn = fmaxf(m[g], wave_max(sc[g]));
+            if (mn != m[g]) {
+                rescale(g, __builtin_amdgcn_exp2f((m[g] - mn) * sm[g]));
+                m[g] = mn;
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) p[g] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[g] - m[g], sm[g], (float)P_LOG2));
+}
+
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // c + a.lo * b.lo + a.hi * b.hi, a and b holding fp16 pairs; fp32 accumulate.
@@ -68,12 +93,15 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// Merge the NW waves' states and write the split's (o, lse).  `scratch`
-// holds, per wave w and head g, the unnormalized output at
+// Merge the NW waves' states and write the split's partial: its normalized
+// output o and the pair (m, ll), m the largest score and ll = log2 of the
+// sum of 2^(z - m) over the split's tokens (log-sum-exp = m + ll, kept as two
+// numbers so the merge of splits stays exact whatever the size of m).
+// `scratch` holds, per wave w and head g, the unnormalized output at
 // scratch[(w * G + g) * 128 + d] and (m, l) at scratch[NW * G * 128 +
 // (w * G + g) * 2 + {0, 1}]; every thread of the block calls this after a
 // barrier.  l_log2_scale is a power-of-two factor carried by l and the
-// outputs (removed from lse).
+// outputs (removed from ll).
 template <int G, int NW>
 __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeArgs& a, int b, int h, int s,
                                             float l_log2_scale, float* stage = nullptr) {
@@ -84,7 +112,7 @@ __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeAr
         float M = kNegInf;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, ml[(w * G + g) * 2]);
-        float o = 0.0f, lse = kNegInf;
+        float o = 0.0f, ll = 0.0f;
         if (M != kNegInf) {
             float L = 0.0f, O = 0.0f;
 #pragma unroll
@@ -95,13 +123,16 @@ __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeAr
                 O += f * mo[(w * G + g) * kHeadDim + d];
             }
             o = O / L;
-            lse = M + (__builtin_log2f(L) - l_log2_scale);
+            ll = __builtin_log2f(L) - l_log2_scale;
         }
         if (stage != nullptr && a.out != nullptr && (a.splits > 1 || a.v_smooth != nullptr)) {
             // Fused combine (the partial waits in LDS for combine_if_last), or one
             // split of the value-transform variant (o waits for its output map).
             stage[g * kHeadDim + d] = o;
-            if (d == 0) stage[G * kHeadDim + g] = lse;
+            if (d == 0) {
+                stage[G * kHeadDim + 2 * g] = M;
+                stage[G * kHeadDim + 2 * g + 1] = ll;
+            }
         } else if (a.out != nullptr && a.splits == 1) {
             // One split: o is already the output (the combine of a single
             // split returns it unchanged, 0 for an empty row).
@@ -109,40 +140,56 @@ __device__ __forceinline__ void merge_waves(const float* scratch, const DecodeAr
         } else {
             const int64_t row = ((int64_t)b * a.hq + h * G + g) * a.splits + s;
             a.part_o[row * kHeadDim + d] = o;
-            if (d == 0) a.part_lse[row] = lse;
+            if (d == 0) {
+                a.part_ml[2 * row] = M;
+                a.part_ml[2 * row + 1] = ll;
+            }
         }
     }
 }
 
-// One (b, q-head) row of the split combine: lse = log2 sum_i 2^lse_i and
-// out = sum_i 2^(lse_i - lse) o_i (empty splits, lse_i = -inf, weigh 0; a row
-// with no token gives 0).  d = output dim in [0, 128) of the row's 128-thread
+// One (b, q-head) row of the split combine: with M the largest m_i,
+// x_i = (m_i - M) + ll_i and X the largest x_i, out = sum_i w_i o_i / sum_i
+// w_i, w_i = 2^(x_i - X) (empty splits, m_i = -inf, weigh 0; a row with no
+// token gives 0).  m_i - M is exact wherever it decides a weight (m_i within a
+// factor 2 of M), so the weights keep full precision at any score size, and
+// the heaviest split weighs exactly 1 (one split returns its o unchanged).
+// d = output dim in [0, 128) of the row's 128-thread
 // group; red = 2 floats and wts = 128 floats of LDS for the group.  Splits go
 // in chunks of 128: thread d computes the weight of split c + d into wts, then
 // every thread sums its dim over the chunk in split order, 16 partial rows in
 // flight.  It has block barriers: every thread of the block calls it, threads
 // of an inactive group only pass the barriers.
-__device__ __forceinline__ void combine_row(const float* part_o, const float* part_lse, float* out, int S,
+__device__ __forceinline__ void combine_row(const float* part_o, const float* part_ml, float* out, int S,
                                             int64_t bg, int d, bool active, float* red, float* wts,
                                             float* lds_row = nullptr) {
     const int lane = d & 63, wave = d >> 6;
-    const float* lse = part_lse + bg * S;
+    const float* ml = part_ml + bg * S * 2;
     float M = kNegInf;
     if (active)
-        for (int s = d; s < S; s += 128) M = fmaxf(M, lse[s]);
+        for (int s = d; s < S; s += 128) M = fmaxf(M, ml[2 * s]);
     M = wave_max(M);
     if (lane == 0) red[wave] = M;
     __syncthreads();
     M = fmaxf(red[0], red[1]);
     __syncthreads();
     const bool any = active && M != kNegInf;
+    float X = kNegInf;
+    if (any)
+        for (int s = d; s < S; s += 128)
+            if (ml[2 * s] != kNegInf) X = fmaxf(X, (ml[2 * s] - M) + ml[2 * s + 1]);
+    X = wave_max(X);
+    if (lane == 0) red[wave] = X;
+    __syncthreads();
+    X = fmaxf(red[0], red[1]);
+    __syncthreads();
     const float* po = part_o + bg * S * kHeadDim + d;
     float den = 0.0f, num = 0.0f;
     for (int c = 0; c < S; c += 128) {                      // the same trip count in every thread
         float w = 0.0f;
         if (any && c + d < S) {
-            const float ls = lse[c + d];
-            w = ls == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(ls - M);
+            const float ms = ml[2 * (c + d)];
+            w = ms == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(((ms - M) + ml[2 * (c + d) + 1]) - X);
         }
         den += w;
         wts[d] = w;
@@ -166,7 +213,7 @@ __device__ __forceinline__ void combine_row(const float* part_o, const float* pa
 }
 
 // Fused combine after merge_waves(..., stage), for more than one split.
-// Wave 0 writes the split's partials (G rows of o, G lse values, staged in
+// Wave 0 writes the split's partials (G rows of o, G (m, ll) pairs, staged in
 // LDS by merge_waves), makes them visible device-wide with one release fence,
 // and counts the work-group in arrivals[b][h] (lane 0, after the fence: all of
 // the wave's stores precede the count).  The last of the head's splits to
@@ -190,7 +237,8 @@ __device__ __forceinline__ void combine_if_last(unsigned char* smem, const float
             const int64_t row = ((int64_t)b * a.hq + h * G + i / kHeadDim) * a.splits + s;
             a.part_o[row * kHeadDim + i % kHeadDim] = stage[i];
         }
-        if (lane < G) a.part_lse[((int64_t)b * a.hq + h * G + lane) * a.splits + s] = stage[G * kHeadDim + lane];
+        if (lane < 2 * G)
+            a.part_ml[2 * (((int64_t)b * a.hq + h * G + lane / 2) * a.splits + s) + lane % 2] = stage[G * kHeadDim + lane];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         int prev = 0;
         if (lane == 0) prev = __hip_atomic_fetch_add(a.arrivals + stream, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -204,7 +252,7 @@ __device__ __forceinline__ void combine_if_last(unsigned char* smem, const float
     const bool active = grp < G;
     // Value-transform variant: the combined rows wait in LDS for the output map.
     float* rows = a.v_smooth != nullptr ? (float*)(smem + 4352) : nullptr;   // G x 128 floats
-    combine_row(a.part_o, a.part_lse, a.out, a.splits, (int64_t)b * a.hq + h * G + (active ? grp : 0),
+    combine_row(a.part_o, a.part_ml, a.out, a.splits, (int64_t)b * a.hq + h * G + (active ? grp : 0),
                 threadIdx.x & 127, active, red + 2 * grp, wts + 128 * grp, rows ? rows + 128 * grp : nullptr);
     if (rows != nullptr) {                                  // block-uniform
         __syncthreads();

@@ -130,7 +130,7 @@ size_t vqkv_cache_bytes(const vqkv_shape* s) {
 size_t vqkv_workspace_bytes(const vqkv_shape* s, int32_t num_splits) {
     if (check_shape(s, false) != VQKV_OK || num_splits < 1) return 0;
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
-    return align256(rows * 128 * sizeof(float)) + align256(rows * sizeof(float));
+    return align256(rows * 128 * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
 size_t vqkv_step_workspace_bytes(const vqkv_shape* s, int32_t num_splits) {
@@ -266,14 +266,14 @@ vqkv_status decode_attention_impl(const vqkv_shape* s, const float* q_prime, con
     VQKV_CHECK(check_ptr(workspace, "workspace"));
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     float* part_o = (float*)workspace;
-    float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
+    float* part_ml = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
     const int G = s->num_q_heads / s->num_kv_heads;
     if (path < 0 || path > 3) return fail(VQKV_ERR_INVALID_ARG, "unknown decode path %d", path);
     if (path == 1 && !(base_fmt(s->fmt) == VQKV_FMT_2BIT && G <= 4))
         return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
     if (path == 2 && (base_fmt(s->fmt) == VQKV_FMT_3BIT || base_fmt(s->fmt) == VQKV_FMT_1P25BIT))
         return fail(VQKV_ERR_UNSUPPORTED, "the gather path takes the 2-bit and 1.5-bit formats");
-    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
+    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_ml,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), path};
@@ -321,8 +321,8 @@ vqkv_status vqkv_decode_attention_varlen(const vqkv_shape* s, const float* q_pri
     VQKV_CHECK(check_ptr(workspace, "workspace"));
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     float* part_o = (float*)workspace;
-    float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
-    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
+    float* part_ml = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
+    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_ml,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), 0, seq_lens};
@@ -354,8 +354,8 @@ vqkv_status vqkv_decode_attention_paged(const vqkv_shape* s, const float* q_prim
     VQKV_CHECK(check_ptr(workspace, "workspace"));
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     float* part_o = (float*)workspace;
-    float* part_lse = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
-    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_pool, v_pool, part_o, part_lse,
+    float* part_ml = (float*)((char*)workspace + align256(rows * 128 * sizeof(float)));
+    vqkv::DecodeArgs a{q_prime, k_book, v_book, k_pool, v_pool, part_o, part_ml,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        max_seq_len, num_splits, split_chunk(max_seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), 0, seq_lens, block_table, num_blocks};
@@ -406,13 +406,13 @@ vqkv_status decode_step_impl(const vqkv_shape* s, const void* q, const void* k_n
     VQKV_CHECK(check_ptr(v_codes, "v_codes"));
     VQKV_CHECK(check_ptr(workspace, "workspace"));
     VQKV_CHECK(check_ptr(out, "out"));
-    // Workspace: partial o | partial lse | q' | arrival counters | sequence lengths.
+    // Workspace: partial o | partial (m, ll) pairs | q' | arrival counters | sequence lengths.
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     char* ws = (char*)workspace;
     float* part_o = (float*)ws;
     ws += align256(rows * 128 * sizeof(float));
-    float* part_lse = (float*)ws;
-    ws += align256(rows * sizeof(float));
+    float* part_ml = (float*)ws;
+    ws += align256(rows * 2 * sizeof(float));
     float* q_prime = (float*)ws;
     ws += align256((size_t)s->batch * s->num_q_heads * 128 * sizeof(float));
     int32_t* arrivals = (int32_t*)ws;
@@ -423,7 +423,7 @@ vqkv_status decode_step_impl(const vqkv_shape* s, const void* q, const void* k_n
                         num_blocks, q, q_prime, arrivals, s->num_q_heads, seq_lens};
     char what[64];
     ap.v_smooth = value_scales(s, smooth);
-    vqkv::DecodeArgs d{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_lse,
+    vqkv::DecodeArgs d{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_ml,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),
                        seq_len, num_splits, split_chunk(seq_len, num_splits),
                        (float)((double)sm_scale * 1.4426950408889634), 3, seq_lens, block_table, num_blocks,
@@ -448,7 +448,7 @@ vqkv_status decode_step_impl(const vqkv_shape* s, const void* q, const void* k_n
         d.out = nullptr;
         snprintf(what, sizeof(what), "%s fused decode launch", name);
         VQKV_CHECK(hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what));
-        vqkv::CombineArgs c{part_o, part_lse, out, s->batch, s->num_q_heads, num_splits};
+        vqkv::CombineArgs c{part_o, part_ml, out, s->batch, s->num_q_heads, num_splits};
         snprintf(what, sizeof(what), "%s combine launch", name);
         return hip_status(vqkv::launch_combine(c, (hipStream_t)stream), what);
     }
@@ -518,8 +518,8 @@ vqkv_status vqkv_combine(const vqkv_shape* s, int32_t num_splits, const void* wo
     VQKV_CHECK(check_ptr(out, "out"));
     const size_t rows = (size_t)s->batch * s->num_q_heads * num_splits;
     const float* part_o = (const float*)workspace;
-    const float* part_lse = (const float*)((const char*)workspace + align256(rows * 128 * sizeof(float)));
-    vqkv::CombineArgs a{part_o, part_lse, out, s->batch, s->num_q_heads, num_splits};
+    const float* part_ml = (const float*)((const char*)workspace + align256(rows * 128 * sizeof(float)));
+    vqkv::CombineArgs a{part_o, part_ml, out, s->batch, s->num_q_heads, num_splits};
     return hip_status(vqkv::launch_combine(a, (hipStream_t)stream), "combine launch");
 }
 

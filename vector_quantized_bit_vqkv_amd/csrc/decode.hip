@@ -12,8 +12,9 @@
 // over its codes.  Each wave takes 64-token tiles of the range in turn and
 // keeps its own online-softmax state (running max m, lane-partial sums l,
 // output accumulators); the waves are merged at the end and the split writes
-// (o normalized, lse) to the workspace.  Scores carry the factor
-// sm_scale * log2(e), so exp2 is the exponential and lse is in log2 units.
+// (o normalized, m, ll) to the workspace: m the largest score, ll the log2 of
+// the weight sum, so the log-sum-exp is m + ll.  Scores carry the factor
+// sm_scale * log2(e), so exp2 is the exponential and m, ll are in log2 units.
 //
 // Kernels (the matrix-core one chosen by measurement; the others stay
 // selectable for measurement):
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) void decode_table_kernel(DecodeArgs a) {
     const uint32_t vslot = (lane & (kVCopies - 1)) * 8;
     // p is produced as exp2(score - max + 15): the fp16 pairs then stay clear of
     // the subnormal range down to 2^-29 of the maximum.  l and acc carry the
-    // same 2^15, removed from lse at the end.
+    // same 2^15, removed from ll at the end.
     constexpr int P_LOG2 = 15;
     const char* tab = (const char*)table;
 
@@ -826,15 +827,41 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         fused_append_2bit<G, NW>(a, b, h, af, xr, qr, smem);
         fetch_q(qr);
     }
+    // The query operand in fp16 range: head g's q' * qscale is scaled by
+    // 2^-k_g, k_g >= 0 the smallest that brings every element below 2^15, and
+    // its scores are taken back by 2^k_g in the exponents and when m leaves
+    // the kernel (powers of two: exact).  k_g = 0 for queries of attention's
+    // usual size, and then every result is what it is without this step.
+    // Lanes with equal lane % 4 hold one head's elements.
     half4_t qa[HB][2];
+    float qsc[G];                                           // 2^k_g, wave-uniform
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
+    for (int hb = 0; hb < HB; ++hb) {
+        float mx = 0.0f;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const float4 q = qv[hb][r];
-            qa[hb][r] = half4_t{(_Float16)(q.x * a.qscale), (_Float16)(q.y * a.qscale),
-                                (_Float16)(q.z * a.qscale), (_Float16)(q.w * a.qscale)};
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(q.x * a.qscale), fabsf(q.y * a.qscale)),
+                                 fmaxf(fabsf(q.z * a.qscale), fabsf(q.w * a.qscale))));
         }
+        mx = fmaxf(mx, xor_lane(mx, 4));
+        mx = fmaxf(mx, xor_lane(mx, 8));
+        mx = fmaxf(mx, xor_lane(mx, 16));
+        mx = fmaxf(mx, xor_lane(mx, 32));
+        int e = 0;
+        if (__builtin_isfinite(mx)) (void)frexpf(mx, &e);  // mx < 2^e; a non-finite query keeps k = 0
+        const int k = e > 15 ? e - 15 : 0;
+        const float inv = ldexpf(1.0f, -k);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * hb + i < G) qsc[4 * hb + i] = readlane(ldexpf(1.0f, k), i);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float4 q = qv[hb][r];
+            qa[hb][r] = half4_t{(_Float16)(q.x * a.qscale * inv), (_Float16)(q.y * a.qscale * inv),
+                                (_Float16)(q.z * a.qscale * inv), (_Float16)(q.w * a.qscale * inv)};
+        }
+    }
     __syncthreads();
     if (!loaded) load_first();
 
@@ -918,7 +945,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) sc[g] = t < t_end ? sacc[g >> 2][g & 3] : kNegInf;
         float p[G];
-        softmax_tile_lazy<G, P_LOG2>(sc, m, p, [&](int g, float alpha) {
+        softmax_tile_lazy_scaled<G, P_LOG2>(sc, m, qsc, p, [&](int g, float alpha) {
             o[g >> 2][0][g & 3] *= alpha;
             o[g >> 2][1][g & 3] *= alpha;
             if ((lane & 3) == (g & 3)) lsum[g >> 2] *= alpha;
@@ -1053,6 +1080,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i)
             if (4 * hb + i < G) l[4 * hb + i] = readlane(x, i);
     }
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] *= qsc[g];             // back to true score units
     __syncthreads();
     float* scratch = (float*)smem;
 #pragma unroll
@@ -1063,7 +1092,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     stash_ml<G, NW>(scratch, m, l);
     __syncthreads();
     float* stage = scratch + NW * G * (kHeadDim + 2);       // after the merge scratch
-    static_assert(SMEM >= MERGE_BYTES + G * (kHeadDim + 1) * 4, "LDS holds the merge scratch and the stage");
+    static_assert(SMEM >= MERGE_BYTES + G * (kHeadDim + 2) * 4, "LDS holds the merge scratch and the stage");
     merge_waves<G, NW>(scratch, a, b, h, s, (float)P_LOG2, stage);
     if (a.out != nullptr && a.splits > 1) {
         combine_if_last<G, NW>(smem, stage, a, b, h);
@@ -1242,7 +1271,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gather_kernel(DecodeArgs a) {
 // One block per (b, q-head), thread d = output dim (combine_row).
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     __shared__ float red[2], wts[128];
-    combine_row(a.part_o, a.part_lse, a.out, a.splits, blockIdx.x, threadIdx.x, true, red, wts);
+    combine_row(a.part_o, a.part_ml, a.out, a.splits, blockIdx.x, threadIdx.x, true, red, wts);
 }
 
 template <int FMT, int NW>

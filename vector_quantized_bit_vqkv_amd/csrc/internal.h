@@ -97,7 +97,7 @@ struct DecodeArgs {
     const uint8_t* k_codes; // [B][Hkv][cap * W]
     const uint8_t* v_codes;
     float* part_o;          // [B][Hq][S][128]
-    float* part_lse;        // [B][Hq][S]  (log2 units)
+    float* part_ml;         // [B][Hq][S][2]: (largest score, log2 of the split's weight sum), log2 units
     int batch, hq, hkv, cap, fmt;
     int seq_len, splits, chunk;
     float qscale;           // sm_scale * log2(e)
@@ -124,7 +124,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 struct CombineArgs {
     const float* part_o;
-    const float* part_lse;
+    const float* part_ml;   // [B][Hq][S][2]
     float* out;             // [B][Hq][128]
     int batch, hq, splits;
 };
