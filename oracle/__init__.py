@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "vqkv_oracle.c")
 _LIB = os.path.join(_HERE, "libvqkv_oracle.so")
 
 HEAD_DIM = 128
-FORMATS = {0: (256, 4), 1: (4096, 8), 2: (4096, 4), 3: (1024, 8)}
+FORMATS = {0: (256, 4), 1: (4096, 8), 2: (4096, 4), 3: (1024, 8), 4: (256, 2)}
 
 
 def build(force: bool = True) -> str:
@@ -253,7 +253,7 @@ def attention_fp(q, k, v, sm_scale: float | None = None, nthreads: int | None = 
 # ------------------------------------------------------------------------- layouts
 
 def code_bytes_per_token(fmt: int) -> int:
-    return {0: 32, 1: 24, 2: 48, 3: 20}[fmt]
+    return {0: 32, 1: 24, 2: 48, 3: 20, 4: 64}[fmt]
 
 
 def pack_k(fmt: int, codes, cap: int, out: np.ndarray | None = None) -> np.ndarray:

@@ -73,12 +73,24 @@ int vqo_format(int fmt, int* entries, int* dsub)
      * results start at 1.25 bits; the shape is not printed): the 1.5-bit
      * setting's 8-dim sub-vectors with 2^10 entries, 10-bit codes. */
     if (fmt == 3) { *entries = 1024; *dsub = 8; return 0; }
+    /* The high end, 4 bits per element: 2^8 entries x 2 dims (8-bit codes on
+     * 2-dim sub-vectors; the shape is not printed either). */
+    if (fmt == 4) { *entries = 256; *dsub = 2; return 0; }
     return -1;
 }
 
 /* Bytes of one token's codes per (b, KV head): 32 (2-bit), 24 (1.5-bit),
- * 48 (3-bit), 20 (1.25-bit). */
-static int code_bytes(int fmt) { return fmt == 0 ? 32 : (fmt == 1 ? 24 : (fmt == 2 ? 48 : 20)); }
+ * 48 (3-bit), 20 (1.25-bit), 64 (4-bit). */
+static int code_bytes(int fmt)
+{
+    switch (fmt) {
+    case 0: return 32;
+    case 1: return 24;
+    case 2: return 48;
+    case 3: return 20;
+    default: return 64;
+    }
+}
 
 /* ------------------------------------------------------------------ fp16 */
 
@@ -395,8 +407,8 @@ int vqo_attention_fp(int B, int Hq, int Hkv, int64_t T, const double* q, const d
  * `cap` tokens (a multiple of 64), restated from its header:
  *
  * Keys, token-major: token t occupies bytes [t*W, (t+1)*W), W = 32 (2-bit),
- * 24 (1.5-bit), 48 (3-bit) or 20 (1.25-bit: 10-bit codes as bit fields, see
- * put_bits below).  2-bit: byte j = code of sub-vector j.  1.5-bit: sub-vectors
+ * 24 (1.5-bit), 48 (3-bit), 20 (1.25-bit: 10-bit codes as bit fields, see
+ * put_bits below) or 64 (4-bit).  2-bit and 4-bit: byte j = code of sub-vector j.  1.5-bit: sub-vectors
  * (2i, 2i+1) share bytes 3i..3i+2 as b0 = c0 & 0xFF, b1 = (c0 >> 8) | ((c1 & 0xF) << 4),
  * b2 = c1 >> 4 (12-bit codes, 3 bytes per 2 sub-vectors).
  *
@@ -456,7 +468,7 @@ int vqo_pack_k(int fmt, int64_t T, const uint16_t* codes, uint8_t* out)
     for (int64_t t = 0; t < T; ++t)
         for (int j = 0; j < J; ++j) {
             uint16_t c = codes[t * J + j];
-            if (fmt == 0) out[t * 32 + j] = (uint8_t)c;
+            if (fmt == 0 || fmt == 4) out[t * code_bytes(fmt) + j] = (uint8_t)c;
             else if (fmt == 3) put_bits(out + t * 20, 10 * j, 10, c);
             else put12(out + t * code_bytes(fmt) + 3 * (j / 2), j & 1, c);
         }
@@ -470,7 +482,7 @@ int vqo_unpack_k(int fmt, int64_t T, const uint8_t* in, uint16_t* codes)
     int J = HD / dsub;
     for (int64_t t = 0; t < T; ++t)
         for (int j = 0; j < J; ++j) {
-            if (fmt == 0) codes[t * J + j] = in[t * 32 + j];
+            if (fmt == 0 || fmt == 4) codes[t * J + j] = in[t * code_bytes(fmt) + j];
             else if (fmt == 3) codes[t * J + j] = (uint16_t)get_bits(in + t * 20, 10 * j, 10);
             else codes[t * J + j] = get12(in + t * code_bytes(fmt) + 3 * (j / 2), j & 1);
         }
@@ -500,6 +512,17 @@ static int64_t v_offset(int fmt, int64_t t, int j, int* which)
         int64_t chunk = 16 * ((j % 16) / 4) + 4 * (u % 4) + (j % 4);
         *which = 0;
         return (t / 64) * 2048 + 32 * chunk + 2 * (u / 4) + j / 16;
+    }
+    if (fmt == 4) {
+        /* 64-token blocks of 4096 bytes, 64 chunks of 64 bytes.  Sub-vectors
+           2w and 2w+1 (4 dims) are group w of the 2-bit layout's 32: chunk
+           16*((w%16)/4) + 4*(u%4) + w%4 (u = t % 64, w = j / 2) holds, at byte
+           4*(u/4) + 2*(w/16) + j%2, the code of sub-vector j of token t. */
+        int64_t u = t % 64;
+        int w = j / 2;
+        int64_t chunk = 16 * ((w % 16) / 4) + 4 * (u % 4) + (w % 4);
+        *which = 0;
+        return (t / 64) * 4096 + 64 * chunk + 4 * (u / 4) + 2 * (w / 16) + (j % 2);
     }
     if (fmt == 2) {
         /* 64-token blocks of 3072 bytes, 64 chunks of 48 bytes.  Chunk
@@ -537,7 +560,7 @@ int vqo_pack_v(int fmt, int64_t T, const uint16_t* codes, uint8_t* out)
         for (int j = 0; j < J; ++j) {
             int which;
             int64_t off = v_offset(fmt, t, j, &which);
-            if (fmt == 0) out[off] = (uint8_t)codes[t * J + j];
+            if (fmt == 0 || fmt == 4) out[off] = (uint8_t)codes[t * J + j];
             else put12(out + off, which, codes[t * J + j]);
         }
     return 0;
@@ -557,7 +580,7 @@ int vqo_unpack_v(int fmt, int64_t T, const uint8_t* in, uint16_t* codes)
         for (int j = 0; j < J; ++j) {
             int which;
             int64_t off = v_offset(fmt, t, j, &which);
-            codes[t * J + j] = fmt == 0 ? in[off] : get12(in + off, which);
+            codes[t * J + j] = (fmt == 0 || fmt == 4) ? in[off] : get12(in + off, which);
         }
     return 0;
 }

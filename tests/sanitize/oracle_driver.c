@@ -67,11 +67,11 @@ int main(void) {
         vqo_smooth_scales(cal, 64, sc);
         for (int i = 0; i < HD; ++i) CHECK(sc[i] > 0.0f);
     }
-    for (int fmt = 0; fmt < 4; ++fmt) {
+    for (int fmt = 0; fmt < 5; ++fmt) {
         int E, dsub;
         CHECK(vqo_format(fmt, &E, &dsub) == 0);
         const int J = HD / dsub, n = 5, T = 70, cap = 128;
-        const int W = fmt == 0 ? 32 : (fmt == 1 ? 24 : (fmt == 2 ? 48 : 20));
+        const int W = fmt == 0 ? 32 : (fmt == 1 ? 24 : (fmt == 2 ? 48 : (fmt == 3 ? 20 : 64)));
         uint16_t* kb = malloc(sizeof(uint16_t) * E * dsub);
         uint16_t* vb = malloc(sizeof(uint16_t) * E * dsub);
         double* bookd = malloc(sizeof(double) * E * dsub);
@@ -83,7 +83,7 @@ int main(void) {
         CHECK(vqo_nearest(x, bookd, E, dsub) >= 0);
         double k[5 * HD], v[5 * HD];
         for (int i = 0; i < n * HD; ++i) { k[i] = nrand(); v[i] = nrand(); }
-        uint16_t kc[5 * 32], vc[5 * 32];
+        uint16_t kc[5 * 64], vc[5 * 64];
         CHECK(vqo_quantize(fmt, n, k, v, s, NULL, kb, vb, kc, vc, 2) == 0);
         CHECK(vqo_quantize(fmt, n, k, v, s, sv, kb, vb, kc, vc, 2) == 0);
         /* Codes of T tokens, packed and unpacked in both layouts. */

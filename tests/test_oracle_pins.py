@@ -181,7 +181,7 @@ def test_double_to_half_round_to_nearest_even():
 
 # ---------------------------------------------------------------- nearest centroid
 
-@pytest.mark.parametrize("dsub", [4, 8])
+@pytest.mark.parametrize("dsub", [2, 4, 8])
 @pytest.mark.parametrize("E", [4, 7, 16])
 def test_nearest_brute_force(dsub, E):
     rng = np.random.default_rng(E * 10 + dsub)
@@ -192,7 +192,7 @@ def test_nearest_brute_force(dsub, E):
         assert oracle.nearest(x, book) == ref
 
 
-@pytest.mark.parametrize("dsub", [4, 8])
+@pytest.mark.parametrize("dsub", [2, 4, 8])
 def test_nearest_exact_ties_take_lowest_index(dsub):
     """Small integers make every distance exact, so ties are frequent and
     numpy's argmin (first occurrence) is the lowest-index rule."""
@@ -215,7 +215,7 @@ def test_nearest_duplicate_centroid_goes_to_first():
     assert oracle.nearest(book[3] + 1e-3, book) == 3
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 3, 4])
 def test_quantize_recovers_codes_of_keys_built_from_centroids(fmt):
     """Keys built as k = s * H(concat C_K[codes]) (scipy's H, numpy arithmetic)
     quantize back to the generating codes; values built from C_V likewise."""
@@ -282,7 +282,7 @@ def _numpy_attention(fmt, q, s, kbook, vbook, kc, vc, sm_scale):
 
 
 @pytest.mark.parametrize("fmt,Hq,Hkv,T", [(0, 4, 1, 300), (0, 8, 2, 129), (1, 5, 1, 77), (1, 4, 2, 1),
-                                          (3, 5, 1, 131), (3, 8, 2, 64)])
+                                          (3, 5, 1, 131), (3, 8, 2, 64), (4, 4, 1, 100), (4, 8, 2, 65)])
 def test_attention_matches_numpy_scipy(fmt, Hq, Hkv, T):
     E, dsub = oracle.FORMATS[fmt]
     J = D // dsub
@@ -345,7 +345,7 @@ def test_fp_attention_matches_scipy():
             assert np.abs(got[b, g] - p @ v[b, h]).max() < 1e-13
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 3, 4])
 def test_vq_attention_equals_full_precision_on_exact_cache(fmt):
     """Keys and values built exactly from centroids: VQ attention over the codes
     equals full-precision attention over the raw cache (the transform changes
@@ -373,7 +373,7 @@ def test_vq_attention_equals_full_precision_on_exact_cache(fmt):
     assert np.abs(vq - fp).max() < 1e-12
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 3, 4])
 def test_value_transform_quantize_recovers_codes(fmt):
     """Value-transform variant: values built as v = sv * H(concat C_V[codes])
     (scipy's H) quantize back to the generating codes when the quantizer is
@@ -407,7 +407,7 @@ def test_value_output_transform_undoes_the_value_transform():
         assert np.abs(back - v).max() <= 1e-13 * np.abs(v).max()
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 3, 4])
 def test_vq_attention_with_value_transform_equals_full_precision(fmt):
     """Keys and values built exactly from centroids in the transformed spaces
     (k = s * H k', v = sv * H v'): VQ attention with the value transform equals
@@ -646,6 +646,56 @@ def test_1p25bit_format_is_ten_bits_per_eight_dims():
     assert math.log2(E) / dsub == 1.25 and oracle.code_bytes_per_token(3) * 8 == 10 * 16
 
 
+def test_4bit_format_is_eight_bits_per_two_dims():
+    """The 4-bit width: 256 entries of 2 dims, 8 bits per 2 elements, 64 codes
+    and 64 bytes per token."""
+    E, dsub = oracle.FORMATS[4]
+    assert (E, dsub) == (256, 2)
+    assert math.log2(E) / dsub == 4.0 and oracle.code_bytes_per_token(4) * 8 == 8 * 64
+
+
+def test_pack_4bit_positions():
+    """Hand-computed byte positions of the 4-bit layouts (2^8 x 2, byte codes):
+    keys token-major, 64 bytes per token, byte j = sub-vector j; values in
+    64-token blocks of 4096 bytes, (t, j) with w = j // 2, u = t % 64 -> chunk
+    16*((w%16)//4) + 4*(u%4) + w%4, byte 4*(u//4) + 2*(w//16) + j%2 of that
+    64-byte chunk."""
+    T = 130
+    c = synth.random_codes(6, (T, 64), 256)
+    kb = oracle.pack_k(4, c, 192)
+    vb = oracle.pack_v(4, c, 192)
+    assert kb.size == vb.size == 192 * 64
+    for t, j in [(0, 0), (0, 63), (1, 0), (33, 7), (129, 63)]:
+        assert kb[t * 64 + j] == c[t, j]
+    assert vb[0] == c[0, 0] and vb[1] == c[0, 1]     # chunk 0, bytes 0 and 1
+    assert vb[64 * 23] == c[1, 14]                   # w = 7: chunk 16 + 4 + 3, byte 0
+    assert vb[64 * 23 + 33] == c[33, 15]             # same chunk, byte 4 * 8 + 0 + 1
+    assert vb[64 * 3 + 2] == c[0, 38]                # w = 19: chunk 3, byte 2 * 1
+    assert vb[4096 + 64 * 63 + 31] == c[95, 63]      # block 1, u = 31, w = 31: chunk 48 + 12 + 3, byte 28 + 2 + 1
+    assert vb[4096 + 64 * 24 + 2] == c[66, 40]       # block 1, u = 2, w = 20: chunk 16 + 8 + 0, byte 2
+    assert vb[2 * 4096 + 64 * 4 + 1] == c[129, 1]    # block 2, u = 1: chunk 4, byte 1
+    assert np.array_equal(oracle.unpack_k(4, kb, T), c)
+    assert np.array_equal(oracle.unpack_v(4, vb, T), c)
+
+
+def test_pack_4bit_round_trip_and_every_byte_once():
+    """Every (token, sub-vector) of a block lands on its own byte: packing the
+    code value 1 at one position at a time sets exactly one byte each time,
+    all 4096 of them distinct; random codes survive pack/unpack."""
+    seen = set()
+    for t in range(64):
+        for j in range(64):
+            c = np.zeros((64, 64), dtype=np.uint16)
+            c[t, j] = 1
+            nz = np.flatnonzero(oracle.pack_v(4, c, 64))
+            assert nz.size == 1
+            seen.add(int(nz[0]))
+    assert len(seen) == 4096
+    c = synth.random_codes(7, (300, 64), 256)
+    assert np.array_equal(oracle.unpack_v(4, oracle.pack_v(4, c, 320), 300), c)
+    assert np.array_equal(oracle.unpack_k(4, oracle.pack_k(4, c, 320), 300), c)
+
+
 # ------------------------------------------------------------------------ K-Means
 
 def _blobs(seed, E, dsub, per):
@@ -660,7 +710,7 @@ def _blobs(seed, E, dsub, per):
     return pts, init
 
 
-@pytest.mark.parametrize("dsub,E", [(4, 16), (8, 12)])
+@pytest.mark.parametrize("dsub,E", [(2, 20), (4, 16), (8, 12)])
 def test_kmeans_matches_sklearn_lloyd(dsub, E):
     from sklearn.cluster import KMeans
     pts, init = _blobs(dsub, E, dsub, 40)
