@@ -104,7 +104,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_b32_t196k")
     ap.add_argument("--also", default="llama8b_b1_t196k,llama8b_b1_t32k,qwen14b_b8_t128k_1p5,llama8b_b8_t196k_3bit,"
-                                      "qwen14b_b8_t128k_1p25",
+                                      "qwen14b_b8_t128k_1p25,llama8b_b8_t196k_4bit",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")

@@ -42,7 +42,8 @@
  *   b2 = c1 >> 4.  3-bit: the same 12-bit pairs for sub-vectors 2i and 2i+1
  *   (dims 4*2i..), 48 bytes per token.  1.25-bit: 10-bit codes as
  *   little-endian bit fields (the same convention), sub-vector j in bits
- *   [10j, 10j + 10) of the token's 20 bytes.
+ *   [10j, 10j + 10) of the token's 20 bytes.  4-bit: byte j holds the code of
+ *   sub-vector j (dims 2j, 2j+1), 64 bytes per token.
  * - Value codes, blocked by tokens and arranged so that every lane of the
  *   decode kernel reads its codes for a block with one wide load.  2-bit:
  *   blocks of 64 tokens, 2048 bytes each, cut into 64 chunks of 32 bytes;
@@ -59,6 +60,10 @@
  *   bytes in the 1.5-bit stream order (stream 8*(j/2) + 2*(u%4) + j%2 for the
  *   pair (j, j + 8), j < 8), the pair of token group u/4 in bits
  *   [20*(u/4), 20*(u/4) + 20) of the stream, sub-vector j in its low 10 bits.
+ *   4-bit: blocks of 64 tokens, 4096 bytes each, cut into 64 chunks of 64
+ *   bytes; sub-vectors 2w and 2w + 1 (4 dims) take the place of the 2-bit
+ *   layout's sub-vector w: the code of token t and sub-vector j (w = j/2) sits
+ *   in chunk 16*((w%16)/4) + 4*(u%4) + w%4, at byte 4*(u/4) + 2*(w/16) + j%2.
  * - Codebooks: fp16 [Hkv][E][dsub], one for keys and one for values per KV
  *   head, shared by every sub-vector position.  Key codebooks live in the
  *   rotated space.
@@ -92,7 +97,10 @@ typedef enum {
     /* The low end of that range: 1024 entries x 8 dims, 10-bit codes, 1.25 bits
      * per element, 20 B per token. */
     VQKV_FMT_1P25BIT = 3,
-    /* Flag OR'ed into either format: the value-transform variant.  The pages'
+    /* The high end: 256 entries x 2 dims, uint8 codes, 4 bits per element,
+     * 64 B per token. */
+    VQKV_FMT_4BIT = 4,
+    /* Flag OR'ed into any format: the value-transform variant.  The pages'
      * technical-framework paragraph quantizes the "preprocessed KV cache"; read
      * that way, values get their own per-channel scales s_v and the keys'
      * rotation, v' = H (v / s_v), are coded as v', and the attention output is
@@ -118,8 +126,8 @@ typedef struct {
 /* ------------------------------------------------------------- size queries */
 
 /* Bytes per token per KV head for one of K or V: 32 (2-bit), 24 (1.5-bit),
- * 48 (3-bit) or 20 (1.25-bit), with or without VQKV_FMT_VALUE_TRANSFORM; 0 for
- * an unknown format.  VecInfer card, "Key points" (codebook size). */
+ * 48 (3-bit), 20 (1.25-bit) or 64 (4-bit), with or without
+ * VQKV_FMT_VALUE_TRANSFORM; 0 for an unknown format.  VecInfer card, "Key points" (codebook size). */
 size_t vqkv_code_bytes_per_token(int32_t fmt);
 
 /* Bytes of one code cache (keys or values): B * Hkv * max_tokens * W.

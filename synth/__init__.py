@@ -33,8 +33,10 @@ FMT_2BIT = 0      # 2^8 entries x 4 dims  -> 2 bits per element
 FMT_1P5BIT = 1    # 2^12 entries x 8 dims -> 1.5 bits per element
 FMT_3BIT = 2      # 2^12 entries x 4 dims -> 3 bits per element
 FMT_1P25BIT = 3   # 2^10 entries x 8 dims -> 1.25 bits per element
+FMT_4BIT = 4      # 2^8 entries x 2 dims  -> 4 bits per element
 FORMATS = {FMT_2BIT: dict(entries=256, dsub=4), FMT_1P5BIT: dict(entries=4096, dsub=8),
-           FMT_3BIT: dict(entries=4096, dsub=4), FMT_1P25BIT: dict(entries=1024, dsub=8)}
+           FMT_3BIT: dict(entries=4096, dsub=4), FMT_1P25BIT: dict(entries=1024, dsub=8),
+           FMT_4BIT: dict(entries=256, dsub=2)}
 
 N_OUTLIER = 4
 OUTLIER_SCALE = 15.0
@@ -68,7 +70,7 @@ class Workload:
         return HEAD_DIM // self.dsub
 
 
-# The five workloads: a tiny CPU-fast case, the Llama-3.1-8B attention shape at
+# The workloads: a tiny CPU-fast case, the Llama-3.1-8B attention shape at
 # 32k and 196k context (batch 1 and batch 32), and a Qwen2.5-14B shape at 1.5 bits.
 WORKLOADS = {
     "tiny_g4_t2048": Workload("tiny_g4_t2048", 1, 4, 1, 2048, FMT_2BIT, "fp32"),
@@ -80,6 +82,8 @@ WORKLOADS = {
     "llama8b_b8_t196k_3bit": Workload("llama8b_b8_t196k_3bit", 8, 32, 8, 196608, FMT_3BIT, "bf16"),
     # The 1.25-bit width (2^10 x 8) on the Qwen2.5-14B attention shape of the 1.5-bit workload.
     "qwen14b_b8_t128k_1p25": Workload("qwen14b_b8_t128k_1p25", 8, 40, 8, 131072, FMT_1P25BIT, "bf16"),
+    # The 4-bit width (2^8 x 2) on the Llama-3.1-8B attention shape of the 3-bit workload.
+    "llama8b_b8_t196k_4bit": Workload("llama8b_b8_t196k_4bit", 8, 32, 8, 196608, FMT_4BIT, "bf16"),
 }
 
 

@@ -22,7 +22,7 @@ int main() {
     const int32_t* Fi = static_cast<const int32_t*>(F);
     vqkv_shape good{32, 32, 8, 128, 196608, VQKV_FMT_2BIT};
     for (int fmt : {(int)VQKV_FMT_2BIT, (int)VQKV_FMT_1P5BIT, (int)VQKV_FMT_3BIT, (int)VQKV_FMT_1P25BIT,
-                    (int)VQKV_FMT_3BIT | (int)VQKV_FMT_VALUE_TRANSFORM}) {
+                    (int)VQKV_FMT_4BIT, (int)VQKV_FMT_3BIT | (int)VQKV_FMT_VALUE_TRANSFORM}) {
         vqkv_shape s = good;
         s.fmt = fmt;
         CHECK(vqkv_cache_bytes(&s) > 0);
@@ -51,7 +51,7 @@ int main() {
     CHECK(vqkv_decode_attention(&bad, Ff, Fb, Fb, Fc, Fc, 100, 0.088f, 1, F, nullptr) == VQKV_ERR_UNSUPPORTED);
     bad = good; bad.num_q_heads = 30;
     CHECK(vqkv_transform_query(&bad, F, 0, Ff, Ff, nullptr) == VQKV_ERR_INVALID_ARG);
-    bad = good; bad.fmt = 4;
+    bad = good; bad.fmt = 5;
     CHECK(vqkv_cache_bytes(&bad) == 0);
     bad = good; bad.fmt = 0x200;
     CHECK(vqkv_quantize_append(&bad, F, F, 0, 1, 0, Ff, Fb, Fb, Fc, Fc, nullptr) == VQKV_ERR_INVALID_ARG);

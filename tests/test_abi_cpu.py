@@ -47,7 +47,9 @@ def test_size_queries():
     assert vq.code_bytes_per_token(vq.FMT_3BIT) == 48
     assert vq.code_bytes_per_token(vq.FMT_1P25BIT) == 20
     assert vq.code_bytes_per_token(vq.FMT_1P25BIT | vq.FMT_VALUE_TRANSFORM) == 20
-    assert vq.code_bytes_per_token(4) == 0
+    assert vq.code_bytes_per_token(vq.FMT_4BIT) == 64
+    assert vq.code_bytes_per_token(vq.FMT_4BIT | vq.FMT_VALUE_TRANSFORM) == 64
+    assert vq.code_bytes_per_token(5) == 0
     assert vq.code_bytes_per_token(7) == 0
     s = vq.make_shape(32, 32, 8, 196608, vq.FMT_2BIT)
     assert vq.cache_bytes(s) == 32 * 8 * 196608 * 32
@@ -227,7 +229,8 @@ def test_transform_combine_and_calibration_checks():
     assert L.vqkv_smooth_scales(1, 0, FAKE, 0, FAKE, None) == INVALID
     assert vq.train_workspace_bytes(0, 4096) > 4096 * 128 * 8
     assert vq.train_workspace_bytes(3, 4096) > 0            # 1.25-bit
-    assert vq.train_workspace_bytes(4, 4096) == 0
+    assert vq.train_workspace_bytes(4, 4096) > 4096 * 128 * 8  # 4-bit: 64 two-dim points per row
+    assert vq.train_workspace_bytes(5, 4096) == 0
     # 1.5-bit needs at least 4096 points: 255 rows x 16 sub-vectors is too few.
     assert L.vqkv_train_codebook(1, 255, FAKE, 0, 0, None, FAKE, 20, FAKE, None, FAKE, None) == INVALID
     assert L.vqkv_train_codebook(0, 64, FAKE, 0, 1, None, FAKE, 20, FAKE, None, FAKE, None) == INVALID  # key needs smooth

@@ -123,7 +123,7 @@ def test_smooth_scales_bit_exact(dtype):
         assert np.array_equal(got[h], oracle.smooth_scales(case.k_cal[h]))
 
 
-@pytest.mark.parametrize("fmt,n_cal,iters", [(0, 1024, 20), (1, 512, 4), (2, 256, 4), (3, 256, 6)])
+@pytest.mark.parametrize("fmt,n_cal,iters", [(0, 1024, 20), (1, 512, 4), (2, 256, 4), (3, 256, 6), (4, 512, 8)])
 @pytest.mark.parametrize("is_key", [True, False])
 def test_train_codebook_bit_exact(fmt, n_cal, iters, is_key):
     say(f"train_codebook fmt{fmt} n_cal{n_cal} iters{iters} key{is_key}")
@@ -169,7 +169,7 @@ def _oracle_codes(fmt, case, s, kb, vb):
     return kc, vc
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_quantize_append_bit_exact_with_ragged_appends(fmt, dtype):
     """A prefill of 37 tokens at 0, then appends of 1, 2, 1, 17 and 64 tokens at
@@ -207,7 +207,7 @@ def test_quantize_append_bit_exact_with_ragged_appends(fmt, dtype):
 VT = vq.FMT_VALUE_TRANSFORM
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_value_transform_append_bit_exact(fmt):
     """Value-transform variant: bulk appends (2-bit exact scan, 1.5-bit screen)
     and one-token appends code the values as H (v / s_v), bit-exact against the
@@ -243,7 +243,7 @@ def test_value_transform_append_bit_exact(fmt):
             assert np.array_equal(oracle.unpack_v(fmt, gv[b, h], n), vc_ref[b, h])
 
 
-@pytest.mark.parametrize("fmt,S", [(0, 1), (0, 7), (1, 3), (2, 4), (3, 2)])
+@pytest.mark.parametrize("fmt,S", [(0, 1), (0, 7), (1, 3), (2, 4), (3, 2), (4, 3)])
 def test_value_transform_attention_matches_oracle(fmt, S):
     """Value-transform variant: transform_query + decode_attention + combine +
     value_output_transform against the oracle's attention with the output map."""
@@ -270,7 +270,7 @@ def test_value_transform_attention_matches_oracle(fmt, S):
 
 @pytest.mark.parametrize("fmt,S,paged", [(0, 1, False), (0, 6, False), (1, 1, False), (1, 4, False),
                                          (0, 5, True), (1, 3, True), (2, 3, False), (0, 1, True),
-                                         (3, 1, False), (3, 4, True)])
+                                         (3, 1, False), (3, 4, True), (4, 1, False), (4, 3, True)])
 def test_value_transform_step_equals_the_calls(fmt, S, paged):
     """Value-transform variant: decode_step (uniform) or decode_step_paged
     (ragged positions) against append + transform_query + decode + combine +
@@ -341,7 +341,7 @@ def test_value_transform_step_equals_the_calls(fmt, S, paged):
         assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_quantize_ties_go_to_lowest_index(fmt):
     """Duplicate codebook entries and values exactly halfway between two entries."""
     say(f"quantize ties fmt{fmt}")
@@ -386,7 +386,7 @@ def test_quantize_ties_go_to_lowest_index(fmt):
     assert np.array_equal(oracle.unpack_v(fmt, vcodes1[0, 0].cpu().numpy(), 9), vc_ref[:9])
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_quantize_near_ties_below_fp32_resolution(fmt):
     """Keys whose rotated sub-vectors sit at the midpoint of two codebook
     entries one fp16 ulp apart (up to the fp32 rounding of k): the two
@@ -443,7 +443,7 @@ def test_quantize_near_ties_below_fp32_resolution(fmt):
         assert np.array_equal(oracle.unpack_v(fmt, vcodes[0, 0].cpu().numpy(), n), vc_ref), mode
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_quantize_fallbacks_match_oracle(fmt):
     """Points the distance screen cannot take (coordinates beyond the fp16 range,
     NaN) go through the exact scan: codes still equal the oracle's, in the bulk
@@ -482,7 +482,7 @@ def test_quantize_fallbacks_match_oracle(fmt):
         assert np.array_equal(oracle.unpack_v(fmt, vcodes[0, 0].cpu().numpy(), n), vc_ref), mode
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_quantize_degenerate_scales_match_oracle(fmt):
     """Smoothing scales are device data the library does not inspect (that would
     need a synchronizing copy).  A negative and an infinite scale (that channel
@@ -592,6 +592,12 @@ ATTN_CASES = [
     (3, 1, 2, 2, 3001, 7, None),           # G = 1
     (3, 2, 12, 4, 4099, 9, None),          # G = 3, ragged tail
     (3, 2, 32, 8, 1, 1, None),
+    (4, 1, 4, 1, 2048, 1, None),           # 4-bit
+    (4, 2, 32, 8, 4099, 9, None),          # ragged tail
+    (4, 1, 8, 8, 777, 5, None),            # G = 1
+    (4, 1, 16, 2, 333, 2, None),           # G = 8
+    (4, 1, 10, 2, 129, 3, None),           # G = 5
+    (4, 2, 32, 8, 1, 1, None),
 ]
 
 
@@ -606,7 +612,7 @@ def test_decode_matches_oracle(fmt, B, Hq, Hkv, T, S, path):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt,Hq,Hkv", [(0, 8, 2), (1, 10, 2), (2, 8, 2), (3, 10, 2)])
+@pytest.mark.parametrize("fmt,Hq,Hkv", [(0, 8, 2), (1, 10, 2), (2, 8, 2), (3, 10, 2), (4, 8, 2)])
 @pytest.mark.parametrize("S", [1, 5, 64])
 def test_decode_varlen_matches_oracle(fmt, Hq, Hkv, S):
     """Ragged batch: each sequence its own length (1, a ragged tail, the longest,
@@ -636,7 +642,7 @@ def test_decode_varlen_matches_oracle(fmt, Hq, Hkv, S):
         assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_quantize_append_varlen_bit_exact(fmt):
     """One token per sequence at its own position (odd, even, block edges);
     a position outside the cache leaves that sequence untouched; every other
@@ -690,7 +696,7 @@ def _paged_pool(kbytes, vbytes, W, seed, spare=3):
     return kpool, vpool, perm
 
 
-@pytest.mark.parametrize("fmt,Hq,Hkv", [(0, 8, 2), (1, 10, 2), (2, 8, 2), (3, 10, 2)])
+@pytest.mark.parametrize("fmt,Hq,Hkv", [(0, 8, 2), (1, 10, 2), (2, 8, 2), (3, 10, 2), (4, 8, 2)])
 @pytest.mark.parametrize("S", [1, 7])
 @pytest.mark.parametrize("lens", [(1000, 700), (20000, 13001)])
 def test_decode_paged_equals_contiguous(fmt, Hq, Hkv, S, lens):
@@ -725,7 +731,7 @@ def test_decode_paged_equals_contiguous(fmt, Hq, Hkv, S, lens):
     assert rel_err(outs[1][1:2], ref) <= TOL
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_quantize_append_paged_bit_exact(fmt):
     """One token per sequence into a paged cache lands in the pool block its table
     names, byte for byte as in the contiguous cache; other pool bytes untouched."""
@@ -766,6 +772,8 @@ STEP_CASES = [
     (3, 1, 40, 8, 1000, 4, "bf16"),       # 1.25-bit, G = 5
     (3, 2, 12, 4, 4098, 9, "fp32"),       # G = 3
     (3, 1, 8, 8, 700, 1, "bf16"),         # one split
+    (4, 1, 40, 8, 1000, 4, "bf16"),       # 4-bit, G = 5
+    (4, 2, 12, 4, 4098, 9, "fp32"),       # G = 3
     # 2-bit, one split: the append runs inside the attention kernel (one launch).
     (0, 1, 16, 2, 700, 1, "fp32"),        # G = 8
     (0, 3, 8, 8, 2000, 1, "fp32"),        # G = 1
@@ -984,7 +992,8 @@ def test_step_captured_in_a_graph_replays_exactly(fmt):
 @pytest.mark.parametrize("fmt,Hq,Hkv,S,paged", [(0, 8, 2, 1, False), (0, 8, 2, 7, False), (1, 10, 2, 5, False),
                                                 (0, 8, 2, 7, True), (1, 10, 2, 3, True), (0, 32, 8, 64, True),
                                                 (2, 8, 2, 5, True), (0, 40, 8, 1, True), (0, 8, 8, 1, True),
-                                                (3, 10, 2, 5, False), (3, 40, 8, 3, True)])
+                                                (3, 10, 2, 5, False), (3, 40, 8, 3, True), (4, 8, 2, 4, False),
+                                                (4, 40, 8, 3, True)])
 def test_decode_step_ragged_equals_the_four_calls(fmt, Hq, Hkv, S, paged):
     """decode_step_varlen / decode_step_paged against append (varlen / paged) +
     transform_query + decode (varlen / paged, lengths positions + 1) + combine:
@@ -1060,7 +1069,7 @@ def test_decode_step_ragged_equals_the_four_calls(fmt, Hq, Hkv, S, paged):
         assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt,S", [(0, 1), (0, 3), (1, 3), (3, 2)])
+@pytest.mark.parametrize("fmt,S", [(0, 1), (0, 3), (1, 3), (3, 2), (4, 2)])
 def test_decode_step_varlen_appends_past_max_seq_len(fmt, S):
     """A ragged step whose max_seq_len is below positions[b] + 1: the token is
     still appended (by the last split's work-group in the one-launch 2-bit
@@ -1099,7 +1108,7 @@ def test_decode_step_varlen_appends_past_max_seq_len(fmt, S):
     _assert_cache_codes(fmt, got_k.cpu().numpy(), got_v.cpu().numpy(), kc, vc, [p + 1 for p in pos])
 
 
-@pytest.mark.parametrize("fmt,S", [(0, 3), (1, 4), (0, 1), (2, 2), (3, 3)])
+@pytest.mark.parametrize("fmt,S", [(0, 3), (1, 4), (0, 1), (2, 2), (3, 3), (4, 1), (4, 4)])
 def test_decode_step_captured_in_a_graph(fmt, S):
     """decode_step captured in a HIP graph: the prologue clears the arrival
     counters with ordinary stores (no memset node), so every replay, with eager
@@ -1158,7 +1167,7 @@ def test_decode_single_token_returns_its_value():
         assert np.abs(got[0, g] - v0).max() <= 1e-6 * np.abs(v0).max()
 
 
-@pytest.mark.parametrize("fmt,Hq,Hkv,S", [(0, 8, 2, 3), (1, 10, 2, 3), (2, 8, 2, 1), (3, 10, 2, 4)])
+@pytest.mark.parametrize("fmt,Hq,Hkv,S", [(0, 8, 2, 3), (1, 10, 2, 3), (2, 8, 2, 1), (3, 10, 2, 4), (4, 8, 2, 3)])
 def test_decode_query_beyond_fp16_range(fmt, Hq, Hkv, S):
     """Queries whose elements times sm_scale * log2(e) pass the fp16 maximum
     (65504): the matrix-core path scales such a head's query operand by a
@@ -1181,7 +1190,7 @@ def test_decode_query_beyond_fp16_range(fmt, Hq, Hkv, S):
 
 
 @pytest.mark.parametrize("fmt,path", [(0, "table"), (0, "gather"), (0, "mfma"), (1, "mfma"), (1, "gather"), (2, "mfma"),
-                                      (3, "mfma")])
+                                      (3, "mfma"), (4, "mfma")])
 def test_decode_split_invariance_and_determinism(fmt, path):
     """1 split vs 64 splits, and a rerun.  Every path rounds each weight to fp16
     (round to nearest, relative error <= 2^-11) against a running maximum that
@@ -1267,7 +1276,7 @@ def test_end_to_end_tiny_workload():
 # ---------------------------------------------------------- full sizes, sampled
 
 FULL = ["llama8b_b1_t32k", "llama8b_b1_t196k", "llama8b_b32_t196k", "qwen14b_b8_t128k_1p5", "llama8b_b8_t196k_3bit",
-        "qwen14b_b8_t128k_1p25"]
+        "qwen14b_b8_t128k_1p25", "llama8b_b8_t196k_4bit"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -69,7 +69,7 @@ def last_token_value_bits(fmt, E, J):
 
 # (workload, number of sampled (b, KV head) slices)
 PRODUCT = [("llama8b_b32_t196k", 4), ("llama8b_b1_t196k", 8), ("llama8b_b1_t32k", 8),
-           ("qwen14b_b8_t128k_1p5", 2), ("qwen14b_b8_t128k_1p25", 2)]
+           ("qwen14b_b8_t128k_1p5", 2), ("qwen14b_b8_t128k_1p25", 2), ("llama8b_b8_t196k_4bit", 2)]
 
 
 @pytest.mark.parametrize("name,nsamp", PRODUCT)

@@ -25,12 +25,13 @@ FMT_2BIT = 0
 FMT_1P5BIT = 1
 FMT_3BIT = 2                      # 4096 x 4: a third width inside the pages' 1.25-4 bit range
 FMT_1P25BIT = 3                   # 1024 x 8: the low end of that range
+FMT_4BIT = 4                      # 256 x 2: the high end
 FMT_VALUE_TRANSFORM = 0x100      # OR'ed into a format: values smoothed and rotated too
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 HEAD_DIM = 128
-ENTRIES = {FMT_2BIT: 256, FMT_1P5BIT: 4096, FMT_3BIT: 4096, FMT_1P25BIT: 1024}
-DSUB = {FMT_2BIT: 4, FMT_1P5BIT: 8, FMT_3BIT: 4, FMT_1P25BIT: 8}
+ENTRIES = {FMT_2BIT: 256, FMT_1P5BIT: 4096, FMT_3BIT: 4096, FMT_1P25BIT: 1024, FMT_4BIT: 256}
+DSUB = {FMT_2BIT: 4, FMT_1P5BIT: 8, FMT_3BIT: 4, FMT_1P25BIT: 8, FMT_4BIT: 2}
 # Kernels selectable for measurement (measure_decode_attention).
 DECODE_PATHS = {"default": 0, "table": 1, "gather": 2, "mfma": 3}
 

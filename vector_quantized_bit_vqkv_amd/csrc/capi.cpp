@@ -42,10 +42,15 @@ const float* value_scales(const vqkv_shape* s, const float* smooth) {
     return (s->fmt & VQKV_FMT_VALUE_TRANSFORM) ? smooth + (int64_t)s->num_kv_heads * 128 : nullptr;
 }
 
-int entries_of(int fmt) { return fmt == VQKV_FMT_2BIT ? 256 : (fmt == VQKV_FMT_1P25BIT ? 1024 : 4096); }
-int dsub_of(int fmt) { return (fmt == VQKV_FMT_1P5BIT || fmt == VQKV_FMT_1P25BIT) ? 8 : 4; }
+int entries_of(int fmt) {
+    return (fmt == VQKV_FMT_2BIT || fmt == VQKV_FMT_4BIT) ? 256 : (fmt == VQKV_FMT_1P25BIT ? 1024 : 4096);
+}
+int dsub_of(int fmt) {
+    return (fmt == VQKV_FMT_1P5BIT || fmt == VQKV_FMT_1P25BIT) ? 8 : (fmt == VQKV_FMT_4BIT ? 2 : 4);
+}
 bool known_fmt(int fmt) {
-    return fmt == VQKV_FMT_2BIT || fmt == VQKV_FMT_1P5BIT || fmt == VQKV_FMT_3BIT || fmt == VQKV_FMT_1P25BIT;
+    return fmt == VQKV_FMT_2BIT || fmt == VQKV_FMT_1P5BIT || fmt == VQKV_FMT_3BIT || fmt == VQKV_FMT_1P25BIT ||
+           fmt == VQKV_FMT_4BIT;
 }
 
 // Checks shared by every call that takes a shape.  `need_cache` adds the
@@ -119,6 +124,7 @@ size_t vqkv_code_bytes_per_token(int32_t fmt) {
     if (base_fmt(fmt) == VQKV_FMT_1P5BIT) return 24;
     if (base_fmt(fmt) == VQKV_FMT_3BIT) return 48;
     if (base_fmt(fmt) == VQKV_FMT_1P25BIT) return 20;
+    if (base_fmt(fmt) == VQKV_FMT_4BIT) return 64;
     return 0;
 }
 
@@ -271,7 +277,7 @@ vqkv_status decode_attention_impl(const vqkv_shape* s, const float* q_prime, con
     if (path < 0 || path > 3) return fail(VQKV_ERR_INVALID_ARG, "unknown decode path %d", path);
     if (path == 1 && !(base_fmt(s->fmt) == VQKV_FMT_2BIT && G <= 4))
         return fail(VQKV_ERR_UNSUPPORTED, "score-table path needs the 2-bit format and Hq/Hkv <= 4");
-    if (path == 2 && (base_fmt(s->fmt) == VQKV_FMT_3BIT || base_fmt(s->fmt) == VQKV_FMT_1P25BIT))
+    if (path == 2 && base_fmt(s->fmt) != VQKV_FMT_2BIT && base_fmt(s->fmt) != VQKV_FMT_1P5BIT)
         return fail(VQKV_ERR_UNSUPPORTED, "the gather path takes the 2-bit and 1.5-bit formats");
     vqkv::DecodeArgs a{q_prime, k_book, v_book, k_codes, v_codes, part_o, part_ml,
                        s->batch, s->num_q_heads, s->num_kv_heads, s->max_tokens, base_fmt(s->fmt),

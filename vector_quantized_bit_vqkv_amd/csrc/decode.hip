@@ -565,13 +565,17 @@ template <int FMT, int G, int NW, bool PAGED, bool APPEND = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int HB = (G + 3) / 4;
     constexpr int PT_BYTES = NW * HB * 512;
+    // 4-bit: two 512-byte rows per wave where the value lookups are assembled
+    // into 4-dim rows for the transposing read.
+    constexpr int SV_BYTES = FMT == 4 ? NW * 1024 : 0;
     constexpr int MERGE_BYTES = NW * G * (kHeadDim + 2) * 4;
-    constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES;
+    constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES + SV_BYTES;
     constexpr int SMEM = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
-    constexpr int W = FMT == 0 ? 32 : (FMT == 1 ? 24 : (FMT == 2 ? 48 : 20));
+    constexpr int W = FMT == 0 ? 32 : (FMT == 1 ? 24 : (FMT == 2 ? 48 : (FMT == 3 ? 20 : 64)));
     static_assert(FMT != 1 || 4096 * 16 == kBookBytes, "a 1.5-bit book fills one book region");
     static_assert(FMT != 3 || 1024 * 16 * 4 == kBookBytes, "four copies of a 1.25-bit book fill one region");
     static_assert(FMT != 2 || 4096 * 8 <= kBookBytes, "a 3-bit book fits one book region");
+    static_assert(FMT != 4 || 256 * 64 * 4 == kBookBytes, "64 copies of a 4-bit book fill one region");
     __shared__ __align__(16) unsigned char smem[SMEM];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -593,9 +597,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // decode over 32k tokens 11.3 -> 9.8 us).  The 12-bit formats stage their
     // books directly: held in registers across the code loads, their 128 bytes
     // per lane spill.
-    static_assert(FMT != 0 || NW == 16, "2-bit: 16 waves stage 16 entries each");
+    static_assert((FMT != 0 && FMT != 4) || NW == 16, "2-bit, 4-bit: 16 waves stage 16 entries each");
     static_assert(FMT != 3 || NW * 64 == 1024, "1.25-bit: one thread per book entry");
-    uint32_t kd[FMT == 0 ? 32 : 1], vd[FMT == 0 ? 32 : 1];  // 2-bit: the wave's 16 entries (SGPRs)
+    constexpr int ND = FMT == 0 ? 32 : (FMT == 4 ? 16 : 1);
+    uint32_t kd[ND], vd[ND];                                // 2-bit, 4-bit: the wave's 16 entries (SGPRs)
     uint4 kq3, vq3;                                         // 1.25-bit: entry threadIdx.x of each book
     if constexpr (FMT == 3) {
         kq3 = ((const uint4*)(a.k_book + (int64_t)h * 1024 * 8))[threadIdx.x];
@@ -606,6 +611,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         const const_u32_ptr vbs = (const_u32_ptr)(a.v_book + (int64_t)h * 256 * 4) + wave * 32;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
+            kd[i] = kbs[i];
+            vd[i] = vbs[i];
+        }
+    } else if constexpr (FMT == 4) {
+        // 4-bit: wave w reads entries [16 w, 16 w + 16) of each book (one
+        // 4-byte entry per dword) through the scalar path, as the 2-bit books.
+        typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+        const const_u32_ptr kbs = (const_u32_ptr)(a.k_book + (int64_t)h * 256 * 2) + wave * 16;
+        const const_u32_ptr vbs = (const_u32_ptr)(a.v_book + (int64_t)h * 256 * 2) + wave * 16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
             kd[i] = kbs[i];
             vd[i] = vbs[i];
         }
@@ -644,6 +660,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 ((uint4*)smem)[threadIdx.x * 4 + c] = kq3;
                 ((uint4*)(smem + kBookBytes))[threadIdx.x * 4 + c] = vq3;
             }
+        } else if constexpr (FMT == 4) {
+            // Slot 64 e + c holds copy c of entry e (4 bytes; 256 bytes per
+            // entry): wave w writes its 16 entries, lane = copy.
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                ((uint32_t*)smem)[(16 * wave + k) * 64 + lane] = kd[k];
+                ((uint32_t*)(smem + kBookBytes))[(16 * wave + k) * 64 + lane] = vd[k];
+            }
         }
     };
     float m[G];
@@ -680,8 +704,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // 2-bit: 32 copies, lane l reads copy l % 32; the value book starts at 64 KB.
     // 1.5-bit: value lookups read half e = lane % 2 of the entry.
     // 1.25-bit: score lookups copy lane % 4, value lookups copy (lane / 2) % 4, half lane % 2.
-    const uint32_t kofs = FMT == 0 ? (uint32_t)(lane & 31) * 8 : (FMT == 3 ? (uint32_t)(lane & 3) * 16 : 0u);
-    const uint32_t vofs = FMT == 0   ? (kofs | (1u << 16))
+    // 4-bit: 64 copies, lane l reads copy l (4-byte entries).
+    const uint32_t kofs = FMT == 0   ? (uint32_t)(lane & 31) * 8
+                          : FMT == 3 ? (uint32_t)(lane & 3) * 16
+                          : FMT == 4 ? (uint32_t)lane * 4
+                                     : 0u;
+    const uint32_t vofs = (FMT == 0 || FMT == 4) ? (kofs | (1u << 16))
                           : FMT == 3 ? (((uint32_t)(lane >> 1) & 3u) * 16 | ((uint32_t)(lane & 1) << 3) | (1u << 16))
                           : FMT == 1 ? (((uint32_t)(lane & 1) << 3) | (1u << 16))
                                      : (1u << 16);
@@ -712,12 +740,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // lane pair's value stream (the 1.5-bit stream index).
     const uint8_t* kl3 = kbase + lane * 20;
     const uint8_t* vl3 = vbase + vstream * 40;
+    // 4-bit: 64 bytes per lane per tile for keys (the lane's token) and values
+    // (chunk = lane of the block).
+    const uint8_t* kl4 = kbase + lane * 64;
+    const uint8_t* vl4 = vbase + lane * 64;
     uint4 ck0, ck1, cv0, cv1;                               // 2-bit
     uint2 dk[3];                                            // 1.5-bit
     uint4 dv[3];
     uint4 ek[3], ev[3];                                     // 3-bit
     uint32_t fk[5];                                         // 1.25-bit
     uint2 fv[5];
+    uint4 gk[4], gv[4];                                     // 4-bit
     auto load_k = [&](int tl) {
         if constexpr (FMT == 0) {
             const int64_t o = toff(tl);
@@ -729,6 +762,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         } else if constexpr (FMT == 3) {
 #pragma unroll
             for (int i = 0; i < 5; ++i) fk[i] = *(const uint32_t*)(kl3 + toff(tl) + 4 * i);
+        } else if constexpr (FMT == 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gk[i] = *(const uint4*)(kl4 + toff(tl) + 16 * i);
         } else {
 #pragma unroll
             for (int i = 0; i < 3; ++i) dk[i] = *(const uint2*)(kl1 + toff(tl) + 8 * i);
@@ -745,6 +781,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         } else if constexpr (FMT == 3) {
 #pragma unroll
             for (int i = 0; i < 5; ++i) fv[i] = *(const uint2*)(vl3 + toff(tl) + 8 * i);
+        } else if constexpr (FMT == 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gv[i] = *(const uint4*)(vl4 + toff(tl) + 16 * i);
         } else {
 #pragma unroll
             for (int i = 0; i < 3; ++i) dv[i] = *(const uint4*)(vl1 + toff(tl) + 16 * i);
@@ -795,7 +834,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         // 2-bit: the query, then the first tiles' codes, then the books into
         // LDS; the waits for the books and the query leave the codes in flight.
         fetch_q(a.q_prime + ((int64_t)b * a.hq + h * G) * kHeadDim);
-        if constexpr (FMT == 0 || FMT == 3) {
+        if constexpr (FMT == 0 || FMT == 3 || FMT == 4) {
             __builtin_amdgcn_sched_barrier(0);
             load_first();
             loaded = true;
@@ -889,6 +928,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 if (half == 0) ck0 = *(const uint4*)(kl0 + toff(nxt));
                 else ck1 = *(const uint4*)(kl0 + toff(nxt) + 16);
             }
+        } else if constexpr (FMT == 4) {
+            // Scores: 32 groups of 4 dims; group w is sub-vectors 2w and 2w + 1,
+            // bytes 2w and 2w + 1 of the lane's 64 bytes: two 4-byte lookups
+            // make the B operand of the 2-bit path's sub-vector w.
+            const uint32_t kw[16] = {gk[0].x, gk[0].y, gk[0].z, gk[0].w, gk[1].x, gk[1].y, gk[1].z, gk[1].w,
+                                     gk[2].x, gk[2].y, gk[2].z, gk[2].w, gk[3].x, gk[3].y, gk[3].z, gk[3].w};
+            static_for<0, 32>([&](auto wc) {
+                constexpr int w = decltype(wc)::value;
+                const uint32_t a0 = __builtin_amdgcn_perm(kw[w >> 1], kofs, lookup_sel<2 * (w & 1)>());
+                const uint32_t a1 = __builtin_amdgcn_perm(kw[w >> 1], kofs, lookup_sel<2 * (w & 1) + 1>());
+                const half4_t kv =
+                    __builtin_bit_cast(half4_t, make_uint2(*(const uint32_t*)(smem + a0), *(const uint32_t*)(smem + a1)));
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) sacc[hb] = mfma_bcast<w & 15>(qa[hb][w >> 4], kv, sacc[hb]);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(nxt);
         } else if constexpr (FMT == 2) {
             // Scores: 32 sub-vectors; the 12-bit code of sub-vector j sits at
             // bit 12 j of the lane's 48 bytes.
@@ -990,6 +1046,34 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 if (hv == 0) cv0 = *(const uint4*)(vl0 + toff(nxt));
                 else cv1 = *(const uint4*)(vl0 + toff(nxt) + 16);
             }
+        } else if constexpr (FMT == 4) {
+            // Values: lane 16r + 4k + q takes, at step st, dword st of its
+            // chunk: the codes of token 4 st + k, sub-vectors 2w and 2w + 1 with
+            // w = 16 hh + 4r + q, for dims half hh = 0 (bytes 0, 1) and hh = 1
+            // (bytes 2, 3).  Its two 4-byte entries are written as the lane's
+            // 8-byte row (dims 4w..4w+3 of the token) and read back through the
+            // transposing read, which hands block 4r + q the same (token x dim)
+            // operand the 2-bit path's direct lookup does.
+            const uint32_t vw[16] = {gv[0].x, gv[0].y, gv[0].z, gv[0].w, gv[1].x, gv[1].y, gv[1].z, gv[1].w,
+                                     gv[2].x, gv[2].y, gv[2].z, gv[2].w, gv[3].x, gv[3].y, gv[3].z, gv[3].w};
+            unsigned char* rows = smem + 2 * kBookBytes + PT_BYTES + wave * 1024 + lane * 8;
+            static_for<0, 16>([&](auto sc16) {
+                constexpr int st = decltype(sc16)::value;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t a0 = __builtin_amdgcn_perm(vw[st], vofs, hh == 0 ? lookup_sel<0>() : lookup_sel<2>());
+                    const uint32_t a1 = __builtin_amdgcn_perm(vw[st], vofs, hh == 0 ? lookup_sel<1>() : lookup_sel<3>());
+                    *(uint2*)(rows + hh * 512) = make_uint2(*(const uint32_t*)(smem + a0), *(const uint32_t*)(smem + a1));
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const half4_t vv = lds_read_tr16((const lds_char*)(rows + hh * 512));
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_bcast<st>(pt_op[hb], vv, o[hb][hh]);
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            load_v(nxt);
         } else if constexpr (FMT == 2) {
             // Values: step st takes the pair (sub-vector j, j + 16) of token
             // group st, bytes 3 st.. of the lane's chunk (j % 16 fixed by the lane).
@@ -1345,9 +1429,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                 VQKV_G(2, 1) VQKV_G(2, 2) VQKV_G(2, 3) VQKV_G(2, 4) VQKV_G(2, 5) VQKV_G(2, 6) VQKV_G(2, 7) VQKV_G(2, 8)
                 default: return hipErrorInvalidValue;
             }
-        } else {
+        } else if (a.fmt == 3) {
             switch (G) {
                 VQKV_G(3, 1) VQKV_G(3, 2) VQKV_G(3, 3) VQKV_G(3, 4) VQKV_G(3, 5) VQKV_G(3, 6) VQKV_G(3, 7) VQKV_G(3, 8)
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (G) {
+                VQKV_G(4, 1) VQKV_G(4, 2) VQKV_G(4, 3) VQKV_G(4, 4) VQKV_G(4, 5) VQKV_G(4, 6) VQKV_G(4, 7) VQKV_G(4, 8)
                 default: return hipErrorInvalidValue;
             }
         }

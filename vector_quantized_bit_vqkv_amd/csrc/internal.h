@@ -18,6 +18,18 @@ __host__ __device__ __forceinline__ int64_t v_code_offset_2bit(int64_t t, int j)
     return (t >> 6) * 2048 + 32 * chunk + 2 * (u >> 2) + (j >> 4);
 }
 
+// Byte offset of the value code of (token t, sub-vector j), j < 64, in a 4-bit
+// stream: blocks of 64 tokens x 64 sub-vectors = 4096 bytes, cut into 64
+// chunks of 64 bytes; sub-vectors 2w and 2w + 1 sit where the 2-bit layout
+// puts sub-vector w: chunk 16 ((w % 16) / 4) + 4 (u % 4) + w % 4 (u = t % 64),
+// byte 4 (u / 4) + 2 (w / 16) + j % 2, i.e. the lane of a decode tile reads
+// the codes of step s at dword s of its chunk.
+__host__ __device__ __forceinline__ int64_t v_code_offset_4bit(int64_t t, int j) {
+    const int u = (int)(t & 63), w = j >> 1;
+    const int chunk = 16 * ((w & 15) >> 2) + 4 * (u & 3) + (w & 3);
+    return (t >> 6) * 4096 + 64 * chunk + 4 * (u >> 2) + 2 * (w >> 4) + (j & 1);
+}
+
 // Byte offset of the 3-byte pair holding the value codes of sub-vectors
 // (j, j + 8), j < 8, of token t in a 1.5-bit stream.  Blocks of 64 tokens x 16
 // sub-vectors = 1536 bytes, cut into 32 streams of 48 bytes, stream
@@ -101,7 +113,7 @@ struct DecodeArgs {
     int batch, hq, hkv, cap, fmt;
     int seq_len, splits, chunk;
     float qscale;           // sm_scale * log2(e)
-    int path;               // 0 auto, 1 score table (2-bit), 2 gather, 3 matrix cores (2-bit)
+    int path;               // 0 auto, 1 score table (2-bit), 2 gather (2-bit, 1.5-bit), 3 matrix cores
     const int32_t* seq_lens;   // device [B] or null (then seq_len for every sequence)
     const int32_t* block_table;  // device [B][Hkv][cap / 64] or null: k_codes / v_codes are block pools
     int num_blocks;

@@ -34,6 +34,7 @@ template <> struct Fmt<0> { static constexpr int E = 256, DS = 4, J = 32, W = 32
 template <> struct Fmt<1> { static constexpr int E = 4096, DS = 8, J = 16, W = 24; };
 template <> struct Fmt<2> { static constexpr int E = 4096, DS = 4, J = 32, W = 48; };
 template <> struct Fmt<3> { static constexpr int E = 1024, DS = 8, J = 16, W = 20; };
+template <> struct Fmt<4> { static constexpr int E = 256, DS = 2, J = 64, W = 64; };
 
 // Writes the `width`-bit field v (width <= 56) at bit `bit` of the little-endian
 // byte string p, keeping every bit outside the field (1.25-bit codes: 10-bit
@@ -265,7 +266,7 @@ __device__ __forceinline__ double screen_operands(const double* x, int np, half4
 
 // Tiles are TT-aligned; 1.25-bit value pairs of tokens u, u + 4 (u % 8 < 4) share
 // bytes, so its tiles must hold whole 8-token groups (TT a multiple of 8).
-template <int FMT> struct AppendTile { static constexpr int TT = FMT == 0 ? 32 : 16; };   // 12- and 10-bit: 16
+template <int FMT> struct AppendTile { static constexpr int TT = (FMT == 0 || FMT == 4) ? 32 : 16; };   // 12-, 10-bit: 16
 
 // The screen's bound for a point of norm xn against a book with
 // (max |c|^2, max |c|_1) = cb.
@@ -421,12 +422,12 @@ __global__ __launch_bounds__(1024) void quantize_screen_kernel(AppendArgs a) {
     // Write the codes of positions [lo, hi) in the cache layout.
     uint8_t* kc = a.k_codes + stream * (int64_t)a.cap * W;
     uint8_t* vc = a.v_codes + stream * (int64_t)a.cap * W;
-    if (FMT == 0) {
+    if (FMT == 0 || FMT == 4) {
         for (int idx = threadIdx.x; idx < nt * J; idx += blockDim.x) {
             const int r = off + idx / J, j = idx % J;
             const int64_t t = tile_base + r;
             kc[t * W + j] = (uint8_t)codes[0][r * J + j];
-            vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[1][r * J + j];
+            vc[FMT == 0 ? v_code_offset_2bit(t, j) : v_code_offset_4bit(t, j)] = (uint8_t)codes[1][r * J + j];
         }
     } else if (FMT == 3) {
         write_tile_1p25<TT>(kc, vc, tile_base, off, nt, codes[0], codes[1]);
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(1024) void quantize_screen_kernel(AppendArgs a) {
 
 // Bulk quantization by the exact scan (fp64 distances to every entry, over
 // slices of the codebook): block of 256 threads per tile of TT positions.
-// Used for the 2-bit format, where 256 entries make the scan cheaper than
+// Used for the 256-entry books (2-bit, 4-bit), where the scan is cheaper than
 // the screen's per-point reductions.
 template <int FMT>
 __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
@@ -542,12 +543,12 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
     // Write the codes of positions [lo, hi) in the cache layout.
     uint8_t* kc = a.k_codes + stream * (int64_t)a.cap * W;
     uint8_t* vc = a.v_codes + stream * (int64_t)a.cap * W;
-    if (FMT == 0) {
+    if (FMT == 0 || FMT == 4) {
         for (int idx = threadIdx.x; idx < nt * J; idx += blockDim.x) {
             const int r = off + idx / J, j = idx % J;
             const int64_t t = tile_base + r;
             kc[t * W + j] = (uint8_t)codes[0][r * J + j];
-            vc[v_code_offset_2bit(t, j)] = (uint8_t)codes[1][r * J + j];
+            vc[FMT == 0 ? v_code_offset_2bit(t, j) : v_code_offset_4bit(t, j)] = (uint8_t)codes[1][r * J + j];
         }
     } else if (FMT == 3) {
         write_tile_1p25<TT>(kc, vc, tile_base, off, nt, codes[0], codes[1]);
@@ -605,7 +606,9 @@ __device__ __forceinline__ void screen_dot(const uint16_t* c, const half2_t (&xh
 
 // Blocks per key (and per value) of the one-token append: a 4096-entry search
 // is split over 4 blocks of 4 sub-vectors each, so the grid fills the GPU.
-template <int FMT> struct TokenSplit { static constexpr int P = FMT == 0 ? 1 : (FMT == 3 ? 2 : 4); };   // 1024: 2, 4096: 4
+template <int FMT> struct TokenSplit {                  // 256 entries: 1 block, 1024: 2, 4096: 4
+    static constexpr int P = (FMT == 0 || FMT == 4) ? 1 : (FMT == 3 ? 2 : 4);
+};
 
 // The per-step append (one new token per sequence), latency-bound: grid
 // (2P, Hkv, B), block x / P = 0 codes the key, 1 the value, x % P = part p
@@ -659,7 +662,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     // Sub-vector j of the block's jj-th.
     // 12-bit values: the block's JB / 2 low sub-vectors and their partners J / 2 further.
     auto sub_of = [&](int jj) -> int {
-        if (FMT != 0 && ph == 1) return (JB / 2) * part + jj % (JB / 2) + (J / 2) * (jj / (JB / 2));
+        if (FMT != 0 && FMT != 4 && ph == 1) return (JB / 2) * part + jj % (JB / 2) + (J / 2) * (jj / (JB / 2));
         return part * JB + jj;
     };
     {
@@ -687,8 +690,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         // lanes read consecutive entries (no LDS bank conflicts).
         double best = __builtin_inf();
         int idx = sl;
-        bool exact = FMT == 0;
-        if constexpr (FMT != 0) {
+        bool exact = FMT == 0 || FMT == 4;
+        if constexpr (FMT != 0 && FMT != 4) {
             // 4096 entries: a screen on the dot units, then the pinned fp64
             // distance for the candidates only.  Up to the common |x|^2, the
             // distance is s = |c|^2 - 2 x.c; the screen takes x rounded to
@@ -799,11 +802,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         vblk = a.v_codes + stream * (int64_t)a.cap * W + (t >> 6) * (64 * W);
     }
     const int u = (int)(t & 63);
-    if (FMT == 0) {
+    if (FMT == 0 || FMT == 4) {
         if (threadIdx.x < JB) {
             const int j = sub_of(threadIdx.x);
             if (ph == 0) kblk[u * W + j] = (uint8_t)codes[threadIdx.x];
-            else vblk[v_code_offset_2bit(u, j)] = (uint8_t)codes[threadIdx.x];
+            else vblk[FMT == 0 ? v_code_offset_2bit(u, j) : v_code_offset_4bit(u, j)] = (uint8_t)codes[threadIdx.x];
         }
     } else if (FMT == 3) {
         // Keys: the block's JB consecutive sub-vectors, whole 5-byte groups of
@@ -989,24 +992,28 @@ hipError_t train_codebook(const TrainArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t stream) {
-    const int TT = a.fmt == 0 ? AppendTile<0>::TT
-                 : (a.fmt == 1 ? AppendTile<1>::TT : (a.fmt == 2 ? AppendTile<2>::TT : AppendTile<3>::TT));
+    static_assert(AppendTile<0>::TT == AppendTile<4>::TT && AppendTile<1>::TT == AppendTile<2>::TT &&
+                  AppendTile<1>::TT == AppendTile<3>::TT, "tile sizes by book size");
+    const int TT = (a.fmt == 0 || a.fmt == 4) ? AppendTile<0>::TT : AppendTile<1>::TT;
     const int first = a.start_pos / TT, last = (a.start_pos + a.n_new - 1) / TT;
     const dim3 grid(last - first + 1, a.hkv, a.batch);
     if (a.n_new == 1 || a.positions) {
         const int P = a.fmt == 0 ? TokenSplit<0>::P
-                    : (a.fmt == 1 ? TokenSplit<1>::P : (a.fmt == 2 ? TokenSplit<2>::P : TokenSplit<3>::P));
+                    : (a.fmt == 1 ? TokenSplit<1>::P
+                                  : (a.fmt == 2 ? TokenSplit<2>::P : (a.fmt == 3 ? TokenSplit<3>::P : TokenSplit<4>::P)));
         const dim3 g1(2 * P, a.hkv, a.batch);
         if (a.fmt == 0) hipLaunchKernelGGL(quantize_token_kernel<0>, g1, dim3(1024), 0, stream, a);
         else if (a.fmt == 1) hipLaunchKernelGGL(quantize_token_kernel<1>, g1, dim3(1024), 0, stream, a);
         else if (a.fmt == 2) hipLaunchKernelGGL(quantize_token_kernel<2>, g1, dim3(1024), 0, stream, a);
-        else hipLaunchKernelGGL(quantize_token_kernel<3>, g1, dim3(1024), 0, stream, a);
+        else if (a.fmt == 3) hipLaunchKernelGGL(quantize_token_kernel<3>, g1, dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL(quantize_token_kernel<4>, g1, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     if (a.fmt == 0) hipLaunchKernelGGL(quantize_exact_kernel<0>, grid, dim3(256), 0, stream, a);
     else if (a.fmt == 1) hipLaunchKernelGGL(quantize_screen_kernel<1>, grid, dim3(1024), 0, stream, a);
     else if (a.fmt == 2) hipLaunchKernelGGL(quantize_screen_kernel<2>, grid, dim3(1024), 0, stream, a);
-    else hipLaunchKernelGGL(quantize_screen_kernel<3>, grid, dim3(1024), 0, stream, a);
+    else if (a.fmt == 3) hipLaunchKernelGGL(quantize_screen_kernel<3>, grid, dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL(quantize_exact_kernel<4>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1018,6 +1025,7 @@ hipError_t launch_smooth_scales(int hkv, int n_cal, const void* k_cal, int dtype
 hipError_t launch_train_codebook(const TrainArgs& a, hipStream_t stream) {
     if (a.fmt == 0) return train_codebook<0>(a, stream);
     if (a.fmt == 3) return train_codebook<3>(a, stream);
+    if (a.fmt == 4) return train_codebook<4>(a, stream);
     return a.fmt == 1 ? train_codebook<1>(a, stream) : train_codebook<2>(a, stream);
 }
 
