@@ -565,8 +565,9 @@ template <int FMT, int G, int NW, bool PAGED, bool APPEND = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int HB = (G + 3) / 4;
     constexpr int PT_BYTES = NW * HB * 512;
-    // 4-bit: two 512-byte rows per wave where the value lookups are assembled
-    // into 4-dim rows for the transposing read.
+    // 4-bit: 1 KB per wave where the value lookups are assembled into 4-dim
+    // rows for the transposing read (16 bytes per lane: its rows for both
+    // dims halves).
     constexpr int SV_BYTES = FMT == 4 ? NW * 1024 : 0;
     constexpr int MERGE_BYTES = NW * G * (kHeadDim + 2) * 4;
     constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES + SV_BYTES;
@@ -1056,18 +1057,20 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             // operand the 2-bit path's direct lookup does.
             const uint32_t vw[16] = {gv[0].x, gv[0].y, gv[0].z, gv[0].w, gv[1].x, gv[1].y, gv[1].z, gv[1].w,
                                      gv[2].x, gv[2].y, gv[2].z, gv[2].w, gv[3].x, gv[3].y, gv[3].z, gv[3].w};
-            unsigned char* rows = smem + 2 * kBookBytes + PT_BYTES + wave * 1024 + lane * 8;
+            // The lane's two rows (hh = 0, 1) are adjacent: one 16-byte write.
+            unsigned char* rows = smem + 2 * kBookBytes + PT_BYTES + wave * 1024 + lane * 16;
             static_for<0, 16>([&](auto sc16) {
                 constexpr int st = decltype(sc16)::value;
+                uint32_t e[4];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const uint32_t a0 = __builtin_amdgcn_perm(vw[st], vofs, hh == 0 ? lookup_sel<0>() : lookup_sel<2>());
-                    const uint32_t a1 = __builtin_amdgcn_perm(vw[st], vofs, hh == 0 ? lookup_sel<1>() : lookup_sel<3>());
-                    *(uint2*)(rows + hh * 512) = make_uint2(*(const uint32_t*)(smem + a0), *(const uint32_t*)(smem + a1));
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t sel = i == 0 ? lookup_sel<0>() : (i == 1 ? lookup_sel<1>() : (i == 2 ? lookup_sel<2>() : lookup_sel<3>()));
+                    e[i] = *(const uint32_t*)(smem + __builtin_amdgcn_perm(vw[st], vofs, sel));
                 }
+                *(uint4*)rows = make_uint4(e[0], e[1], e[2], e[3]);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const half4_t vv = lds_read_tr16((const lds_char*)(rows + hh * 512));
+                    const half4_t vv = lds_read_tr16((const lds_char*)(rows + hh * 8));
 #pragma unroll
                     for (int hb = 0; hb < HB; ++hb) o[hb][hh] = mfma_bcast<st>(pt_op[hb], vv, o[hb][hh]);
                 }
