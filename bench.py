@@ -222,21 +222,7 @@ class Workload:
         """The same step through decode_step: the combine fused into the decode, and with one
         2-bit split the append too (one launch; else the append is a launch of its own).
         Returns the mean ms per step of each of `runs` timed runs of exactly `steps` steps."""
-        import torch
-        for i in range(warmup):
-            self.fused_step(i)
-        torch.cuda.synchronize()
-        per_run = []
-        for r in range(runs):
-            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            head_start(self.q.device)
-            start.record()
-            for i in range(steps):
-                self.fused_step(warmup + r * steps + i)
-            end.record()
-            torch.cuda.synchronize()
-            per_run.append(start.elapsed_time(end) / steps)
-        return per_run
+        return self._time_runs(self.fused_step, steps, warmup, runs)
 
     def _time_runs(self, fn, steps, warmup, runs):
         """Mean ms per call of `steps` back-to-back calls fn(i), for each of `runs`
