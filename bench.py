@@ -261,6 +261,23 @@ class Workload:
             self.decode(kc, vc)
         return self._time_runs(once, steps, warmup, runs)
 
+    def time_parts(self, steps, warmup):
+        """The step's two small calls on their own, back to back: the one-token
+        append (vqkv_quantize_append, all sequences and KV heads) and the query
+        transform; median ms per call of each."""
+        import vector_quantized_bit_vqkv_amd as vq
+        T = self.wl.seq_len
+
+        def append(i):
+            kc, vc = self.caches[i % len(self.caches)]
+            vq.quantize_append(self.shape, self.k_new, self.v_new, T - 1, self.smooth, self.k_book, self.v_book,
+                               kc, vc)
+
+        def transform(i):
+            vq.transform_query(self.shape, self.q, self.smooth, self.q_prime)
+        return (pct(self._time_runs(append, steps, warmup, RUNS), 0.5),
+                pct(self._time_runs(transform, steps, warmup, RUNS), 0.5))
+
     def time_attention_only(self, steps, warmup):
         """decode + combine only (what the bf16 comparison times)."""
         import torch
@@ -402,6 +419,7 @@ def measure(name, args, dev, with_bf16, with_cpu):
     dec = wk.time_decode(args.steps, args.warmup)
     dec_ms = sum(dec) / len(dec)                  # every run has the same number of launches
     attn_ms = wk.time_attention_only(args.steps, args.warmup)
+    append_ms, transform_ms = wk.time_parts(args.steps, args.warmup)
     res = {
         "workload": name,
         "us_per_step": round(step_ms * 1e3, 2),
@@ -419,6 +437,8 @@ def measure(name, args, dev, with_bf16, with_cpu):
         "decode_launches": len(dec) * args.steps,
         "decode_GBps": round(wk.decode_bytes / (dec_ms * 1e-3) / 1e9, 1),
         "attention_us": round(attn_ms * 1e3, 2),
+        "append_us": round(append_ms * 1e3, 2),
+        "transform_query_us": round(transform_ms * 1e3, 2),
         "num_splits": wk.S,
         "cache_copies": len(wk.caches),
         "step_bytes": wk.step_bytes,
@@ -461,6 +481,8 @@ def main():
     stream_gbps = read_stream_peak(dev)
 
     achieved = head["decode_GBps"]
+    for r in [head] + also:                      # against this box's own read stream
+        r["decode_pct_read_stream"] = round(100 * r["decode_GBps"] / stream_gbps, 1)
     line = {
         "metric": METRIC,
         "value": head["GBps"],
