@@ -723,6 +723,46 @@ def test_kmeans_matches_sklearn_lloyd(dsub, E):
     assert np.array_equal(assign, km.labels_)
 
 
+@pytest.mark.parametrize("fmt,n_cal", [(0, 64), (1, 512), (4, 32)])
+def test_train_codebooks_recovers_planted_books(fmt, n_cal):
+    """The composition train_codebooks = transform the keys, cut rows into
+    sub-vectors, K-Means, round to fp16: calibration rows built exactly from
+    planted fp16 centroids (keys as s * H(concat C_K[codes]) with scipy's H,
+    values as concat C_V[codes]), every entry used, and Forgy indices pointing
+    at one point of each entry, give back the planted books bit for bit (a
+    transposed reshape, a missing transform or a wrong index would mix the
+    clusters)."""
+    E, dsub = oracle.FORMATS[fmt]
+    J = D // dsub
+    rng = np.random.default_rng(300 + fmt)
+
+    def planted(seed):
+        book = synth.random_fp16_book(seed, (E, dsub))
+        while len({r.tobytes() for r in book}) < E:           # distinct rows
+            book = synth.random_fp16_book(seed := seed + 1, (E, dsub))
+        return book
+
+    kb, vb = planted(310 + fmt), planted(320 + fmt)
+    codes = []
+    for _ in range(2):
+        c = rng.integers(0, E, size=n_cal * J)
+        c[:E] = rng.permutation(E)                            # every entry used
+        codes.append(c.reshape(n_cal, J))
+    kc, vc = codes
+    s = rng.uniform(0.7, 6.0, D).astype(np.float32)
+    H = scipy.linalg.hadamard(D) / math.sqrt(D)
+    kf = kb.view(np.float16).astype(np.float64)
+    vf = vb.view(np.float16).astype(np.float64)
+    k = (kf[kc].reshape(n_cal, D) @ H) * s.astype(np.float64)
+    v = vf[vc].reshape(n_cal, D)
+    # Point p = t * J + j of the sub-vector array; entry e starts from a point of entry e.
+    init_k = np.array([np.flatnonzero(kc.ravel() == e)[0] for e in range(E)])
+    init_v = np.array([np.flatnonzero(vc.ravel() == e)[0] for e in range(E)])
+    gk, gv = oracle.train_codebooks(fmt, k, v, s, init_k, init_v, iters=3)
+    assert np.array_equal(gk, kb)
+    assert np.array_equal(gv, vb)
+
+
 def test_kmeans_objective_never_increases():
     rng = np.random.default_rng(3)
     pts = rng.standard_normal((3000, 4))
