@@ -19,8 +19,8 @@
 // Kernels (the matrix-core one chosen by measurement; the others stay
 // selectable for measurement):
 //   * decode_mfma_kernel (default, every format: 2-bit 2^8 x 4, 1.5-bit
-//     2^12 x 8, 3-bit 2^12 x 4, 1.25-bit 2^10 x 8): scores and values both on
-//     the matrix cores,
+//     2^12 x 8, 3-bit 2^12 x 4, 1.25-bit 2^10 x 8, 4-bit 2^8 x 2): scores
+//     and values both on the matrix cores,
 //     v_mfma_f32_4x4x4f16, with the centroids gathered from LDS codebooks
 //     (details at the kernel).  For the fused decode step it also finishes
 //     the output: with one split the work-group writes it directly, with more
@@ -561,6 +561,12 @@ __device__ __forceinline__ uint32_t code12_addr(const uint32_t (&w)[N], uint32_t
 // four copies), value lookups copy (lane / 2) % 4 (a lane pair reads the two
 // halves of one copy), which about halves the bank conflicts of random
 // lookups into a single copy.
+// 4-bit (2^8 x 2): the 2-bit products with each 4-dim operand made of the two
+// 2-dim entries of sub-vectors 2w and 2w + 1.  A 1 KB book fills its 64 KB
+// region as 64 copies, copy c of entry e at 256 e + 4 c, and lane l reads copy
+// l (the 64 lanes of a 4-byte read hit 64 distinct banks).  Key codes are 64
+// bytes per token; a value lookup's two entries are written as the lane's
+// 8-byte row into a per-wave area and read back through the transposing read.
 template <int FMT, int G, int NW, bool PAGED, bool APPEND = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int HB = (G + 3) / 4;
