@@ -445,6 +445,8 @@ def measure(name, args, dev, with_bf16, with_cpu):
         "decode_bytes": wk.decode_bytes,
         "setup_s": {"generate": round(wk.gen_s, 2), "calibrate": round(wk.calib_s, 2),
                     "prefill_quantize": round(wk.prefill_s, 2)},
+        # Bulk append of the whole context (one call, wall clock, first launch included).
+        "prefill_Mtoken_heads_per_s": round(wk.wl.batch * wk.wl.num_kv_heads * wk.wl.seq_len / wk.prefill_s / 1e6, 1),
     }
     if with_bf16:
         bf_ms, bf_gbps, bf_S = wk.time_bf16(max(5, args.steps // 5), 2)
