@@ -932,7 +932,7 @@ def test_fused_step_append_hard_cases_match_oracle(S):
             assert np.array_equal(oracle.unpack_k(fmt, kcodes[0, h].cpu().numpy(), p0), kc0[0, h, :p0])
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_step_captured_in_a_graph_replays_exactly(fmt):
     """One decode step (append of one token per sequence, query transform,
     decode, combine) captured in a HIP graph: every replay, with eager work and
