@@ -598,6 +598,11 @@ ATTN_CASES = [
     (4, 1, 16, 2, 333, 2, None),           # G = 8
     (4, 1, 10, 2, 129, 3, None),           # G = 5
     (4, 2, 32, 8, 1, 1, None),
+    (0, 1, 12, 2, 300, 2, None),           # G = 6
+    (1, 1, 14, 2, 300, 3, None),           # G = 7
+    (2, 1, 12, 2, 300, 1, None),           # G = 6
+    (3, 1, 14, 2, 300, 2, None),           # G = 7
+    (4, 1, 14, 2, 300, 3, None),           # G = 7
 ]
 
 
