@@ -777,6 +777,8 @@ STEP_CASES = [
     (3, 1, 40, 8, 1000, 4, "bf16"),       # 1.25-bit, G = 5
     (3, 2, 12, 4, 4098, 9, "fp32"),       # G = 3
     (3, 1, 8, 8, 700, 1, "bf16"),         # one split
+    (0, 1, 12, 2, 2000, 3, "bf16"),       # G = 6
+    (0, 1, 14, 2, 2000, 1, "fp32"),       # G = 7, one split
     (4, 1, 40, 8, 1000, 4, "bf16"),       # 4-bit, G = 5
     (4, 2, 12, 4, 4098, 9, "fp32"),       # G = 3
     # 2-bit, one split: the append runs inside the attention kernel (one launch).
