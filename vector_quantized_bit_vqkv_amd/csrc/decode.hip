@@ -799,19 +799,29 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // 2-bit: a second code set, so each tile's codes arrive two tiles ahead
     // (which matters when a wave has few tiles: six per wave at batch 1).
     uint4 bk0, bk1, bv0, bv1;
-    // Issued on every path: a wave without tiles reads tile 0, which every
-    // stream has (capacity >= 64 tokens; paged, table entries are clamped).
-    // With a path that skips them, the waits the compiler places for the
-    // query loads above would also cover these, and the first tiles' codes
-    // would have to arrive before the loop starts.
-    // The loads go out in the loop's own order (keys, values; set A, set B),
-    // so the waits inside the loop are the same on the first pass.
+    // The first tile's codes, issued on every path: a wave without tiles
+    // reads tile 0, which every stream has (capacity >= 64 tokens; paged,
+    // table entries are clamped).  With a path that skips them, the waits the
+    // compiler places for the query loads above would also cover these, and
+    // the first tile's codes would have to arrive before the loop starts.
+    // The loads go out in the loop's own order (keys, values; set A, then set
+    // B in load_second), so the waits inside the loop are the same on the
+    // first pass.
     auto load_first = [&]() {
         const int f = first < t_end ? first : 0;
         load_k(f);
         __builtin_amdgcn_sched_barrier(0);
         load_v(f);
+    };
+    // 2-bit: the second tile's codes (set B), issued after the prologue's
+    // barrier.  With both tiles requested at kernel start (32 MB at batch 1)
+    // the books, the query and the fused append's own loads queued behind
+    // them; half as much ahead of the prologue made the batch-1 196k decode
+    // 27.4 -> 26.5 us and its step 33.8 -> 32.1 us (interleaved A/B, one box;
+    // batch 32 unchanged).
+    auto load_second = [&]() {
         if constexpr (FMT == 0) {
+            const int f = first < t_end ? first : 0;
             const int second = first + kStride < t_end ? first + kStride : f;
             const int64_t o = toff(second);
             __builtin_amdgcn_sched_barrier(0);
@@ -854,16 +864,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         static_assert(2 * kHeadDim * 8 + G * kHeadDim * 4 <= PT_BYTES, "rows and q' fit the probability tiles");
         double* xr = (double*)(smem + 2 * kBookBytes);
         float* qr = (float*)(smem + 2 * kBookBytes + 2 * kHeadDim * 8);
-        // The append's own loads, then the wave's first two tiles, then the
-        // books into LDS: the append's waits leave the code loads in flight.
-        // If one of the two tiles holds the new token its codes are requested
-        // again after the append (the first loads read the old bytes).
+        // The append's own loads, then the wave's first tile, then the books
+        // into LDS: the append's waits leave the code loads in flight.  If the
+        // first tile holds the new token its codes are requested again after
+        // the append (the first loads read the old bytes); the second tile is
+        // requested after the append in any case (load_second).
         const AppendFetch af = fused_append_fetch<G, NW>(a, b, h);
         bool stale = false;
         if (af.app && first < t_end) {
-            const int second = first + kStride < t_end ? first + kStride : first;
             const int64_t nb = toff((int)(af.t & ~(int64_t)63));
-            stale = toff(first) == nb || toff(second) == nb;
+            stale = toff(first) == nb;
         }
         __builtin_amdgcn_sched_barrier(0);
         load_first();
@@ -910,6 +920,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
     __syncthreads();
     if (!loaded) load_first();
+    load_second();
 
     // One tile; the 2-bit code registers are parameters so that two sets can
     // alternate (codes loaded two tiles ahead).
