@@ -297,17 +297,21 @@ vqkv_status vqkv_combine(const vqkv_shape* shape, int32_t num_splits, const void
  *   vqkv_quantize_append(n_new = 1, start_pos = position), vqkv_transform_query,
  *   vqkv_decode_attention(seq_len = position + 1), vqkv_combine
  * on the same arguments (the same kernels' arithmetic).  Runs on the
- * matrix-core kernel, in one or two launches:
+ * matrix-core kernel, in one to three launches:
  *   - 2-bit without VQKV_FMT_VALUE_TRANSFORM: the attention kernel appends
  *     the token (in the work-group whose split holds `position`) and
  *     transforms its queries itself; with one split it writes `out` directly
  *     (one launch), with more it writes the splits' partials to the
  *     workspace and vqkv_combine's kernel merges them (two launches);
  *   - the other formats: an append launch that also transforms the query,
- *     then the attention, where the last split of each (b, KV head) to finish
- *     combines that head's splits (a per-head arrival counter in the
- *     workspace, cleared by the append launch of every step, so the
- *     workspace needs no initialization; one split needs no counter).
+ *     then the attention: with one split it writes `out` directly (two
+ *     launches), with more it writes the splits' partials and vqkv_combine's
+ *     kernel merges them (three launches);
+ *   - with VQKV_FMT_VALUE_TRANSFORM and more than one split: the append
+ *     launch, then the attention, where the last split of each (b, KV head)
+ *     to finish combines that head's splits and maps the output back (a
+ *     per-head arrival counter in the workspace, cleared by the append launch
+ *     of every step, so the workspace needs no initialization).
  *   q                 device, [B][Hq][128], dtype (the same dtype as k_new)
  *   k_new, v_new      device, [B][Hkv][1][128], dtype
  *   position          host, 0 <= position < max_tokens

@@ -42,7 +42,10 @@ int main() {
         CHECK(vqkv_decode_step_static(&s, F, F, F, 0, 4098, Ff, Fb, Fb, Fc, Fc, 0.088f, 1, Ff, nullptr) == VQKV_OK);
         const int vt = (fmt & VQKV_FMT_VALUE_TRANSFORM) != 0;
         CHECK(vqkv_value_output_transform(&s, Ff, Ff, nullptr) == (vt ? VQKV_OK : VQKV_ERR_INVALID_ARG));
-        CHECK(g_launches - before == 8 + 2 * 3 + (fmt == VQKV_FMT_2BIT ? 1 : 2) + vt);
+        // Steps at 9 splits: 2-bit, fused append + combine (2); the value transform, append + attention
+        // with the fused combine (2); the other formats, append + attention + combine (3).
+        const int step_launches = (fmt == VQKV_FMT_2BIT || vt) ? 2 : 3;
+        CHECK(g_launches - before == 8 + 3 * step_launches + (fmt == VQKV_FMT_2BIT ? 1 : 2) + vt);
     }
     // Rejections: no launch may happen.
     const int before = g_launches;

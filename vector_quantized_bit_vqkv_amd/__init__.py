@@ -262,8 +262,9 @@ def combine(shape: Shape, num_splits: int, workspace, out) -> None:
 def decode_step(shape: Shape, q, k_new, v_new, position: int, smooth, k_book, v_book, k_codes, v_codes,
                 num_splits: int, workspace, out, sm_scale: float | None = None) -> None:
     """Append one token per sequence at `position`, then attention over [0, position] into out
-    (two launches, one for 2-bit with one split; bit-identical to quantize_append + transform_query +
-    decode_attention + combine)."""
+    (one to three launches: the 2-bit attention appends the token itself, and with several splits a
+    combine launch follows; bit-identical to quantize_append + transform_query + decode_attention +
+    combine)."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype or q.dtype != k_new.dtype:
@@ -410,7 +411,7 @@ class VQCache:
         return out
 
     def step(self, q, k_new, v_new, position: int, num_splits: int | None = None, out=None, workspace=None):
-        """One decode step (decode_step's one or two launches): append k_new, v_new [B][Hkv][1][128] at `position`,
+        """One decode step (decode_step's one to three launches): append k_new, v_new [B][Hkv][1][128] at `position`,
         then attend with q over tokens [0, position] (decode_step)."""
         import torch
         if num_splits is None:

@@ -460,6 +460,18 @@ vqkv_status decode_step_impl(const vqkv_shape* s, const void* q, const void* k_n
     }
     snprintf(what, sizeof(what), "%s append launch", name);
     VQKV_CHECK(hip_status(vqkv::launch_quantize_append(ap, (hipStream_t)stream), what));
+    if (num_splits > 1 && ap.v_smooth == nullptr) {
+        // Three launches: the attention writes the splits' partials and the
+        // combine kernel merges them (2-2.5 us shorter per step than the last
+        // split of each head combining after a release/acquire pair, for the
+        // 1.5-, 1.25-, 3- and 4-bit batch-8 steps).
+        d.out = nullptr;
+        snprintf(what, sizeof(what), "%s decode launch", name);
+        VQKV_CHECK(hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what));
+        vqkv::CombineArgs c{part_o, part_ml, out, s->batch, s->num_q_heads, num_splits};
+        snprintf(what, sizeof(what), "%s combine launch", name);
+        return hip_status(vqkv::launch_combine(c, (hipStream_t)stream), what);
+    }
     snprintf(what, sizeof(what), "%s decode launch", name);
     return hip_status(vqkv::launch_decode(d, (hipStream_t)stream), what);
 }
