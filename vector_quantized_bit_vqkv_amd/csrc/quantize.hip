@@ -122,7 +122,8 @@ __device__ __forceinline__ void argmin_range(const double* x, const float* book,
 //
 // Nearest centroid by a screen and an exact refinement, a set of points at a time:
 // s~_e = |c_e|^2 - 2 x.c_e on v_mfma_f32_4x4x4f16, with x split into fp16
-// hi + lo parts (products exact, fp32 sums) and broadcast to all 16 blocks
+// hi + lo parts (each rounded through fp32: two hardware conversions instead
+// of a software double-to-half rounding; products exact, fp32 sums) and broadcast to all 16 blocks
 // (CBSZ = 4, ABID = group of 4 points), each lane holding one centroid of a
 // 64-centroid group.  |s~_e - s_e| <= tau, with s_e = |c_e|^2 - 2 x.c_e exact
 // and tau = 2^-18 (|x| + max|c|)^2 + 2^-22 max|c|_1 (twice the worst case of
@@ -130,12 +131,19 @@ __device__ __forceinline__ void argmin_range(const double* x, const float* book,
 // Every centroid with s~ <= min s~ + 3 tau is a candidate; candidates get the
 // exact fp64 distance in the pinned order and the lowest index among the
 // smallest wins, so the code equals the brute-force one.  Each lane keeps its
-// best and second-best screened value: when a lane's second value is also a
+// best and second-best screened value (updated with selects, not branches:
+// the screen is bound by VALU issue): when a lane's second value is also a
 // candidate, or a coordinate is outside the fp16 range (|x| >= 2^15, NaN),
 // the point falls back to the exact scan of the whole book.
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// x = hi + lo + err, both parts rounded through fp32 with the hardware
+// conversions: |x - hi| <= 2^-11 (1 + 2^-12) |x|, |err| <= 2^-22 (1 + 2^-10) |x|
+// + 2^-25 (lo subnormal), inside the bound's margin for the x split.
+__device__ __forceinline__ _Float16 split_hi(double v) { return (_Float16)(float)v; }
+__device__ __forceinline__ _Float16 split_lo(double v, _Float16 hi) { return (_Float16)(float)(v - (double)hi); }
 
 template <int V> struct IntC { static constexpr int value = V; };
 template <int I, int N, class Fn>
@@ -231,8 +239,10 @@ __device__ __forceinline__ void screen_set(const half4_t (&ahi)[DS / 4], const h
             for (int i = 0; i < 4; ++i) {
                 const int pt = 4 * g + i;
                 const float v = __builtin_fmaf(-2.0f, d[i], c2);
-                if (v < m1[pt]) { m2[pt] = m1[pt]; m1[pt] = v; a1[pt] = e; }
-                else if (v < m2[pt]) m2[pt] = v;
+                const bool lt1 = v < m1[pt], lt2 = v < m2[pt];
+                m2[pt] = lt1 ? m1[pt] : (lt2 ? v : m2[pt]);
+                a1[pt] = lt1 ? e : a1[pt];
+                m1[pt] = lt1 ? v : m1[pt];
             }
         });
     }
@@ -254,9 +264,8 @@ __device__ __forceinline__ double screen_operands(const double* x, int np, half4
             const double v = p < np ? x[p * DS + 4 * q + i] : 0.0;
             n2 = n2 + v * v;
             if (!(__builtin_fabs(v) < 32768.0)) out_of_range = true;
-            const _Float16 h = (_Float16)v;
-            ahi[q][i] = h;
-            alo[q][i] = (_Float16)(v - (double)h);
+            ahi[q][i] = split_hi(v);
+            alo[q][i] = split_lo(v, ahi[q][i]);
         }
     }
     return __builtin_sqrt(n2);
