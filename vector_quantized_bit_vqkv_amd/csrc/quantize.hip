@@ -83,18 +83,6 @@ __device__ void block_fwht(double* x, int ntok) {
 
 // Squared L2 distance, fixed left-to-right order.
 template <int DS>
-__device__ __forceinline__ double dist(const double* x, const float* c) {
-    double t = x[0] - (double)c[0];
-    double d = t * t;
-#pragma unroll
-    for (int i = 1; i < DS; ++i) {
-        t = x[i] - (double)c[i];
-        d = d + t * t;
-    }
-    return d;
-}
-
-template <int DS>
 __device__ __forceinline__ double dist_d(const double* x, const double* c) {
     double t = x[0] - c[0];
     double d = t * t;
@@ -106,14 +94,16 @@ __device__ __forceinline__ double dist_d(const double* x, const double* c) {
     return d;
 }
 
-// Nearest entry among [e0, e1) of an fp32 book in LDS; strict "<" keeps the lowest index.
+// Nearest entry among [e0, e1) of a book in LDS, widened to fp64 once when
+// staged (the conversions were a fifth of the scan's instructions); strict
+// "<" keeps the lowest index.
 template <int DS>
-__device__ __forceinline__ void argmin_range(const double* x, const float* book, int e0, int e1,
+__device__ __forceinline__ void argmin_range(const double* x, const double* book, int e0, int e1,
                                              double& best, int& idx) {
     best = __builtin_inf();
     idx = e0;
     for (int e = e0; e < e1; ++e) {
-        const double d = dist<DS>(x, book + e * DS);
+        const double d = dist_d<DS>(x, book + e * DS);
         if (d < best) { best = d; idx = e; }
     }
 }
@@ -473,7 +463,7 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
     using F = Fmt<FMT>;
     constexpr int E = F::E, DS = F::DS, J = F::J, W = F::W;
     constexpr int TT = AppendTile<FMT>::TT;
-    __shared__ float book[E * DS];              // one codebook at a time (K, then V)
+    __shared__ double book[E * DS];             // one codebook at a time (K, then V), widened once
     __shared__ double xk[TT * kHeadDim];        // transformed keys of the tile
     __shared__ uint16_t codes[2][TT * J];
     __shared__ double red_d[256];
@@ -512,7 +502,7 @@ __global__ __launch_bounds__(256) void quantize_exact_kernel(AppendArgs a) {
             block_fwht(xk + off * kHeadDim, nt);
         }
         const uint16_t* src = (phase == 0 ? a.k_book : a.v_book) + (int64_t)h * E * DS;
-        for (int i = threadIdx.x; i < E * DS; i += blockDim.x) book[i] = half_bits_to_float(src[i]);
+        for (int i = threadIdx.x; i < E * DS; i += blockDim.x) book[i] = (double)half_bits_to_float(src[i]);
         __syncthreads();
         const int items = P * ES;
         for (int it = threadIdx.x; it < items; it += blockDim.x) {
