@@ -441,7 +441,8 @@ __device__ __forceinline__ AppendFetch fused_append_fetch(const DecodeArgs& a, i
 
 template <int G, int NW>
 __device__ __forceinline__ void fused_append_2bit(const DecodeArgs& a, int b, int h, const AppendFetch& f,
-                                                  double* xr, float* qr, const unsigned char* books) {
+                                                  double* xr, float* qr, const unsigned char* books,
+                                                  double* wide) {
     static_assert(NW == 16 && 4 + G <= NW, "64 sub-vectors x 16 slices fill the 1024 threads");
     const AppendArgs& ap = a.app;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -457,6 +458,18 @@ __device__ __forceinline__ void fused_append_2bit(const DecodeArgs& a, int b, in
     }
     __syncthreads();
     if (app && (wave == 0 || (wave == 1 && a.v_smooth != nullptr))) rotate_row_wave(xr + wave * kHeadDim, lane);
+    if (app) {
+        // Both books (copy 0 of the staged copies), widened to fp64 once: the
+        // search then converts nothing (the conversions were two of every
+        // five of its instructions).  Two elements per thread.
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = threadIdx.x + NW * 64 * r;        // element of [2][256][4]
+            const int isv = i >> 10, e = (i >> 2) & 255, c = i & 3;
+            wide[i] = (double)half_bits_to_float(
+                ((const uint16_t*)(books + isv * kBookBytes + e * kBookStride))[c]);
+        }
+    }
     __syncthreads();
     if (app) {
         // Sub-vector sv = thread / 16: key j = sv for sv < 32, value j = sv - 32;
@@ -466,13 +479,13 @@ __device__ __forceinline__ void fused_append_2bit(const DecodeArgs& a, int b, in
         double xs[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) xs[i] = xr[isv * kHeadDim + 4 * j + i];
-        const unsigned char* book = books + isv * kBookBytes + (lane & 31) * 8;
+        const double* book = wide + isv * 1024;
         double best = __builtin_inf();
         int idx = sl;
 #pragma unroll 4
         for (int k = 0; k < 16; ++k) {
             const int e = sl + 16 * k;
-            const double d = dist_h<4>(xs, (const uint16_t*)(book + e * kBookStride));
+            const double d = dist_f64<4>(xs, book + 4 * e);
             if (d < best) { best = d; idx = e; }
         }
         group_argmin<16>(best, idx);
@@ -576,7 +589,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     // dims halves).
     constexpr int SV_BYTES = FMT == 4 ? NW * 1024 : 0;
     constexpr int MERGE_BYTES = NW * G * (kHeadDim + 2) * 4;
-    constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES + SV_BYTES;
+    // Fused append: both books widened to fp64 for its exact search (16 KB).
+    constexpr int WIDE_BYTES = APPEND ? 2 * 256 * 4 * 8 : 0;
+    constexpr int MAIN_BYTES = 2 * kBookBytes + PT_BYTES + SV_BYTES + WIDE_BYTES;
     constexpr int SMEM = MAIN_BYTES > MERGE_BYTES ? MAIN_BYTES : MERGE_BYTES;
     constexpr int W = FMT == 0 ? 32 : (FMT == 1 ? 24 : (FMT == 2 ? 48 : (FMT == 3 ? 20 : 64)));
     static_assert(FMT != 1 || 4096 * 16 == kBookBytes, "a 1.5-bit book fills one book region");
@@ -880,7 +895,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         loaded = !stale;
         __builtin_amdgcn_sched_barrier(0);
         write_books();
-        fused_append_2bit<G, NW>(a, b, h, af, xr, qr, smem);
+        fused_append_2bit<G, NW>(a, b, h, af, xr, qr, smem,
+                                 (double*)(smem + 2 * kBookBytes + PT_BYTES + SV_BYTES));
         fetch_q(qr);
     }
     // The query operand in fp16 range: head g's q' * qscale is scaled by

@@ -81,19 +81,6 @@ __device__ void block_fwht(double* x, int ntok) {
     __syncthreads();
 }
 
-// Squared L2 distance, fixed left-to-right order.
-template <int DS>
-__device__ __forceinline__ double dist_d(const double* x, const double* c) {
-    double t = x[0] - c[0];
-    double d = t * t;
-#pragma unroll
-    for (int i = 1; i < DS; ++i) {
-        t = x[i] - c[i];
-        d = d + t * t;
-    }
-    return d;
-}
-
 // Nearest entry among [e0, e1) of a book in LDS, widened to fp64 once when
 // staged (the conversions were a fifth of the scan's instructions); strict
 // "<" keeps the lowest index.
@@ -103,7 +90,7 @@ __device__ __forceinline__ void argmin_range(const double* x, const double* book
     best = __builtin_inf();
     idx = e0;
     for (int e = e0; e < e1; ++e) {
-        const double d = dist_d<DS>(x, book + e * DS);
+        const double d = dist_f64<DS>(x, book + e * DS);
         if (d < best) { best = d; idx = e; }
     }
 }
@@ -909,7 +896,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(const double* pts, i
         __syncthreads();
         if (p < n) {
             for (int e = 0; e < ne; ++e) {
-                const double d = dist_d<DS>(x, c + e * DS);
+                const double d = dist_f64<DS>(x, c + e * DS);
                 if (d < best) { best = d; idx = e0 + e; }
             }
         }

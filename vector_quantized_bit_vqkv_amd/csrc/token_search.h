@@ -25,6 +25,21 @@ __device__ __forceinline__ double load_elem_d(const void* base, int64_t i, int d
     return (double)load_elem(base, i, dtype);
 }
 
+// Exact distance to a book entry already widened to fp64 (the same values
+// as dist_h's conversions, so the same result), pinned order.
+template <int DS>
+__device__ __forceinline__ double dist_f64(const double* x, const double* c) {
+#pragma clang fp contract(off)
+    double t = x[0] - c[0];
+    double d = t * t;
+#pragma unroll
+    for (int i = 1; i < DS; ++i) {
+        t = x[i] - c[i];
+        d = d + t * t;
+    }
+    return d;
+}
+
 // Exact distance to an fp16 book entry, pinned order.
 template <int DS>
 __device__ __forceinline__ double dist_h(const double* x, const uint16_t* c) {
