@@ -100,9 +100,10 @@ __device__ __forceinline__ void argmin_range(const double* x, const double* book
 // Nearest centroid by a screen and an exact refinement, a set of points at a time:
 // s~_e = |c_e|^2 - 2 x.c_e on v_mfma_f32_4x4x4f16, with x split into fp16
 // hi + lo parts (each rounded through fp32: two hardware conversions instead
-// of a software double-to-half rounding; products exact, fp32 sums) and broadcast to all 16 blocks
-// (CBSZ = 4, ABID = group of 4 points), each lane holding one centroid of a
-// 64-centroid group.  |s~_e - s_e| <= tau, with s_e = |c_e|^2 - 2 x.c_e exact
+// of a software double-to-half rounding; products exact, fp32 sums) and
+// broadcast to all 16 blocks (CBSZ = 4, ABID = group of 4 points), each lane
+// holding one centroid of a 64-centroid group.  |s~_e - s_e| <= tau, with
+// s_e = |c_e|^2 - 2 x.c_e exact
 // and tau = 2^-18 (|x| + max|c|)^2 + 2^-22 max|c|_1 (twice the worst case of
 // the x split, 18 fp32 accumulations, the fp32 |c|^2 and the final rounding).
 // Every centroid with s~ <= min s~ + 3 tau is a candidate; candidates get the
